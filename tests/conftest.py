@@ -1,0 +1,27 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def _ensure_built():
+    # Build only what is missing: the GPU runs use the in-tree libraries as built.
+    from oracle import build as oracle_build
+    if not os.path.exists(oracle_build.LIB):
+        oracle_build.build()
+
+
+_ensure_built()
+
+
+@pytest.fixture(scope="session")
+def repo_root():
+    return ROOT
