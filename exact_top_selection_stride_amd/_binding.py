@@ -1,0 +1,169 @@
+"""ctypes binding of libtopk_exact.so (include/topk_exact.h).
+
+Argument marshalling only: shapes, dtypes and devices are checked, the raw device
+pointers and the current HIP stream are handed to the C ABI, and every step of
+the selection runs in the library's kernels. There is no CPU fallback: if the
+library is missing the call raises.
+"""
+import contextlib
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtopk_exact.so")
+
+TOPK_OK = 0
+TOPK_ERR_NULL_POINTER = 1
+TOPK_ERR_BAD_SHAPE = 2
+TOPK_ERR_BAD_K = 3
+TOPK_ERR_BAD_SENTINEL = 4
+TOPK_ERR_WORKSPACE = 5
+TOPK_ERR_HIP = 6
+TOPK_ERR_BAD_ARG = 7
+TOPK_K_MAX = 2048
+
+PATH_AUTO = 0
+PATH_SAMPLED = 1
+PATH_ROWSPLIT = 2
+PATH_DIRECT = 3
+PATH_RECOVERY = 4
+
+STAT_NAMES = (
+    "rows", "sentinel", "direct", "sampled", "tau0", "tau1", "recover_under", "recover_over",
+    "rowsplit", "forced_recovery", "long_exact", "frontier_wide", "queued",
+)
+STAT_COUNT = 16
+
+EXPORTED = (
+    "topk_exact", "topk_exact_reserve", "topk_exact_get_stats", "topk_exact_reset_stats",
+    "topk_exact_set_path_override", "topk_exact_last_error", "topk_stream_read_probe",
+)
+
+
+class TopKError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what} failed with status {code}: {last_error()}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads the in-tree HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m exact_top_selection_stride_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        L.topk_exact.restype = ctypes.c_int
+        L.topk_exact.argtypes = [vp, vp, i64, i64, i32, vp, i32, vp]
+        L.topk_exact_reserve.restype = ctypes.c_int
+        L.topk_exact_reserve.argtypes = [i64, i64, i32]
+        L.topk_exact_get_stats.restype = ctypes.c_int
+        L.topk_exact_get_stats.argtypes = [vp, ctypes.c_int, vp]
+        L.topk_exact_reset_stats.restype = ctypes.c_int
+        L.topk_exact_reset_stats.argtypes = [vp]
+        L.topk_exact_set_path_override.restype = ctypes.c_int
+        L.topk_exact_set_path_override.argtypes = [ctypes.c_int]
+        L.topk_exact_last_error.restype = ctypes.c_char_p
+        L.topk_exact_last_error.argtypes = []
+        L.topk_stream_read_probe.restype = ctypes.c_int
+        L.topk_stream_read_probe.argtypes = [vp, i64, vp, vp]
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    if _lib is None:
+        return ""
+    return (_lib.topk_exact_last_error() or b"").decode(errors="replace")
+
+
+def _check(code: int, what: str):
+    if code != TOPK_OK:
+        raise TopKError(code, what)
+
+
+def _stream_handle(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def topk_exact(scores: torch.Tensor, row_len: torch.Tensor, K: int = 2048, sentinel: int = -1,
+               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Exact top-K indices of each ragged row; returns int32 [M, K] on the scores' device.
+
+    scores: float32 [M, N_alloc] on a GPU, unit column stride and row stride N_alloc.
+    row_len: int32 [M] on the same GPU. out (optional): int32 [M, K], contiguous.
+    Enqueued on `stream` (default: the current stream); nothing synchronizes.
+    """
+    if scores.dim() != 2 or scores.dtype != torch.float32 or not scores.is_cuda:
+        raise ValueError("scores must be a 2-D float32 GPU tensor")
+    M, N = scores.shape
+    if scores.stride(1) != 1 or (M > 1 and scores.stride(0) != N):
+        raise ValueError("scores must be row-major with row stride N_alloc")
+    if row_len.dtype != torch.int32 or row_len.device != scores.device or tuple(row_len.shape) != (M,):
+        raise ValueError("row_len must be an int32 [M] tensor on the scores' device")
+    if not row_len.is_contiguous():
+        raise ValueError("row_len must be contiguous")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.int32, device=scores.device)
+    elif (out.dtype != torch.int32 or out.device != scores.device or tuple(out.shape) != (M, K)
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous int32 [M, K] tensor on the scores' device")
+    with torch.cuda.device(scores.device):
+        code = lib().topk_exact(scores.data_ptr(), row_len.data_ptr(), M, N, K, out.data_ptr(),
+                                sentinel, _stream_handle(scores.device, stream))
+    _check(code, "topk_exact")
+    return out
+
+
+def reserve(M_max: int, N_alloc_max: int, K: int = 2048, device=None):
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        _check(lib().topk_exact_reserve(M_max, N_alloc_max, K), "topk_exact_reserve")
+
+
+def get_stats(device=None, stream=None) -> dict:
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    buf = (ctypes.c_uint64 * STAT_COUNT)()
+    with torch.cuda.device(dev):
+        _check(lib().topk_exact_get_stats(ctypes.addressof(buf), STAT_COUNT, _stream_handle(dev, stream)),
+               "topk_exact_get_stats")
+    return {name: int(buf[i]) for i, name in enumerate(STAT_NAMES)}
+
+
+def reset_stats(device=None, stream=None):
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(dev):
+        _check(lib().topk_exact_reset_stats(_stream_handle(dev, stream)), "topk_exact_reset_stats")
+
+
+def set_path_override(mode: int):
+    _check(lib().topk_exact_set_path_override(int(mode)), "topk_exact_set_path_override")
+
+
+@contextlib.contextmanager
+def path_override(mode: int):
+    set_path_override(mode)
+    try:
+        yield
+    finally:
+        set_path_override(PATH_AUTO)
+
+
+def stream_read_probe(x: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Reads every element of x (a float32 GPU tensor) once; measurement only."""
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 GPU tensor")
+    if sink.dtype != torch.float32 or sink.device != x.device or sink.numel() < 4096:
+        raise ValueError("sink must be a float32 tensor of >= 4096 elements on x's device")
+    with torch.cuda.device(x.device):
+        _check(lib().topk_stream_read_probe(x.data_ptr(), x.numel(), sink.data_ptr(),
+                                            _stream_handle(x.device, stream)), "topk_stream_read_probe")

@@ -1,0 +1,947 @@
+// topk_exact.hip -- gfx950 (CDNA4, wave64) kernels and host dispatch for the
+// sample-guided exact Top-K selector declared in include/topk_exact.h.
+//
+// Pages cited (by title):
+//   [Cx] "几何平均快 1.55 倍，但短行采样会输：腾讯怎么测精确 Top-K"
+//   [PD] "腾讯|长上下文稀疏注意力前K精确选择:20种配置平均加速1.55倍"
+//   [AX] "Sample-Guided Exact Top-K Selection for Long-Context Sparse Attention"
+//        (arxivdaily abstract page)
+//
+// Per row of the score matrix (one 512-thread workgroup per row at a time,
+// workgroups pull rows from a device ticket: persistent execution, [AX]):
+//   1. Rows with L <= K write 0..L-1 and the sentinel; no score is read
+//      ([Cx] section "什么叫精确，时间怎么量").
+//   2. Short rows (direct-exact, [Cx] section "采样不是处处都该开": exact
+//      proposals win on short rows) are staged in LDS as order keys and
+//      selected exactly there: one HBM read.
+//   3. Longer rows take the sampled path ([PD] question 2, Fig. 4):
+//      a. the fixed-stride view x[j*128] proposes tau0 (target 1.5K
+//         candidates) and the nested, wider tau1 (target 1.75K) as ranks of
+//         the sample ([Cx] section "采样不是处处都该开"; [PD] question 2);
+//      b. one mandatory full-row pass reads the row with 128-bit loads,
+//         admits keys >= tau1 into an LDS candidate buffer by wave ballot and
+//         prefix count, counts C(tau0) and C(tau1), and builds the first
+//         radix histogram of the admitted keys ([PD] question 2, Fig. 4 stage
+//         2; [AX]);
+//      c. certification: C(tau0) >= K, else C(tau1) >= K (the nested set is
+//         already in LDS, so this fallback rereads nothing), else exact
+//         full-row recovery; a candidate overflow also goes to recovery.
+//         Nothing is written before this decision ([PD] question 2; [AX]);
+//      d. refinement on the unresolved boundary only: bins above the bin that
+//         holds rank K are committed at once, that bin's candidates move to a
+//         small frontier buffer and radix digits narrow it until the K-th key
+//         is exact ([PD] question 2, Fig. 4 stage 3).
+//   4. Exact full-row recovery is a two-pass radix select from HBM: a
+//      histogram pass, then a pass that commits every key above the boundary
+//      bin and collects that bin into LDS for the final exact step.
+//
+// Keys: a float's 32-bit pattern u maps to key(u) = u ^ (sign ? 0xFFFFFFFF :
+// 0x80000000), whose unsigned order is IEEE totalOrder. The hot loop never
+// builds keys: admission key(u) >= key(tau1) is a single signed compare of u
+// (tau1 >= +0) or unsigned compare (tau1 <= -0). No floating-point arithmetic
+// happens anywhere on the path.
+
+#include "topk_exact.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+namespace {
+
+constexpr int BLOCK = 512;            // threads per workgroup (8 waves of 64)
+constexpr int WAVE = 64;
+constexpr int NWAVES = BLOCK / WAVE;
+constexpr int NB_BITS = 11;
+constexpr int NB = 1 << NB_BITS;      // radix histogram bins
+constexpr int CAP = 8192;             // candidate (index, key) pairs in LDS
+constexpr int KEYS_CAP = 2 * CAP;     // keys-only capacity of the same region
+constexpr int FL_CAP = 512;           // frontier (index, key) pairs
+constexpr uint32_t STRIDE = 128;      // sample stride s
+constexpr int UNROLL = 4;             // 128-bit loads per thread per batch
+constexpr uint32_t DIRECT_MAX_DEFAULT = 16384;
+constexpr uint32_t KEY_MAX = 0xFFFFFFFFu;
+
+static_assert(NB % BLOCK == 0, "bins per thread must be integral");
+static_assert(TOPK_K_MAX * 7 / 4 + 1 <= CAP, "candidate buffer must hold the tau1 target");
+
+struct Control {
+  uint32_t row_ticket;
+  uint32_t done_ticket;
+  uint32_t pad[30];
+  unsigned long long stats[TOPK_STAT_COUNT];
+};
+
+struct Params {
+  const float* scores;
+  const int32_t* row_len;
+  int32_t* out;
+  Control* ctl;
+  uint32_t M;
+  uint32_t N;
+  uint32_t K;
+  int32_t sentinel;
+  uint32_t T0;          // primary candidate target, ceil(1.5 K)
+  uint32_t T1;          // secondary candidate target, ceil(1.75 K)
+  uint32_t direct_max;  // auto mode: rows up to this length take the direct path
+  int32_t mode;
+};
+
+struct Smem {
+  uint32_t buf[2 * CAP];       // candidates: idx in [0,CAP), key in [CAP,2CAP); or keys only
+  uint32_t hist[NB];
+  uint32_t fl_idx[FL_CAP];
+  uint32_t fl_key[FL_CAP];
+  uint32_t wtmp[NWAVES];
+  uint32_t cnt;                // admitted / collected count
+  uint32_t cnt0;               // admitted keys >= tau0
+  uint32_t fl_cnt;
+  uint32_t out_gt;             // output slots taken by keys above the threshold
+  uint32_t out_tie;            // output slots taken by keys equal to the threshold
+  uint32_t mn, mx;
+  uint32_t sel_bin, sel_above;
+  int32_t row;
+};
+
+// ---------------------------------------------------------------- primitives
+
+__device__ __forceinline__ uint32_t key_of_bits(uint32_t u) {
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint32_t mbcnt64(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Reserves consecutive slots of an LDS counter for the lanes whose pred is set, one
+// atomic per wave. Every active lane of the wave must reach it.
+__device__ __forceinline__ uint32_t wave_reserve(bool pred, uint32_t* counter) {
+  const uint64_t m = __ballot(pred);
+  uint32_t base = 0;
+  if (m != 0) {
+    const int leader = __builtin_ctzll(m);
+    uint32_t b = 0;
+    if ((int)lane_id() == leader) b = atomicAdd(counter, (uint32_t)__popcll(m));
+    base = __shfl(b, leader);
+  }
+  return base + mbcnt64(m);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  for (int o = WAVE / 2; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  for (int o = WAVE / 2; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const uint32_t l = lane_id();
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const uint32_t n = __shfl_up(v, o);
+    if (l >= (uint32_t)o) v += n;
+  }
+  return v;
+}
+
+// Smallest shift such that span >> shift fits in NB bins (at most 21).
+__device__ __forceinline__ uint32_t shift_for(uint32_t span) {
+  if (span < (uint32_t)NB) return 0;
+  return (32u - (uint32_t)__clz(span)) - NB_BITS;
+}
+
+// Folds per-thread min/max into s.mn / s.mx (initialised by the caller before a
+// barrier). Ends with a barrier.
+__device__ __forceinline__ void block_minmax(Smem& s, uint32_t mn, uint32_t mx) {
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if (lane_id() == 0) {
+    atomicMin(&s.mn, mn);
+    atomicMax(&s.mx, mx);
+  }
+  __syncthreads();
+}
+
+// Finds the bin b holding rank r (1-based, counted from the top) of s.hist and the
+// count of entries in bins above it. Requires 1 <= r <= sum(hist). Result in
+// s.sel_bin / s.sel_above; starts and ends with a barrier-protected section.
+__device__ void block_find_bin(Smem& s, uint32_t r) {
+  constexpr int PER = NB / BLOCK;
+  const uint32_t t = threadIdx.x;
+  uint32_t h[PER];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    h[j] = s.hist[t * PER + j];
+    sum += h[j];
+  }
+  uint32_t incl = wave_incl_scan(sum);
+  const uint32_t w = t / WAVE;
+  if (lane_id() == WAVE - 1) s.wtmp[w] = incl;
+  if (t == 0) {
+    s.sel_bin = 0;
+    s.sel_above = 0;
+  }
+  __syncthreads();
+  uint32_t before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVES; ++i) {
+    const uint32_t v = s.wtmp[i];
+    before += ((uint32_t)i < w) ? v : 0u;
+    total += v;
+  }
+  incl += before;
+  const uint32_t above = total - incl;  // entries in bins owned by higher threads
+  if (above < r && r <= above + sum) {
+    uint32_t cum = above;
+#pragma unroll
+    for (int j = PER - 1; j >= 0; --j) {
+      if (cum + h[j] >= r) {
+        s.sel_bin = t * PER + j;
+        s.sel_above = cum;
+        break;
+      }
+      cum += h[j];
+    }
+  }
+  __syncthreads();
+}
+
+// Exact rank selection by radix narrowing. `for_keys(f)` calls f(key) for every key
+// of the set, block-cooperatively. Among the keys in [lo, hi], finds T = the r-th
+// largest (1 <= r <= count in range) and gt = the number of them above T. Each
+// round bins the range into NB buckets, keeps only the bucket holding rank r, and
+// shrinks the range by 2^11, so at most three rounds run.
+template <class ForKeys>
+__device__ void select_rank(Smem& s, ForKeys&& for_keys, uint32_t r, uint32_t lo, uint32_t hi,
+                            uint32_t& T, uint32_t& gt) {
+  const uint32_t t = threadIdx.x;
+  gt = 0;
+  for (;;) {
+    const uint32_t sh = shift_for(hi - lo);
+    for (uint32_t i = t; i < (uint32_t)NB; i += BLOCK) s.hist[i] = 0;
+    __syncthreads();
+    const uint32_t lo_ = lo, hi_ = hi;
+    for_keys([&](uint32_t k) {
+      if (k >= lo_ && k <= hi_) atomicAdd(&s.hist[(k - lo_) >> sh], 1u);
+    });
+    __syncthreads();
+    block_find_bin(s, r);
+    const uint32_t b = s.sel_bin, above = s.sel_above;
+    r -= above;
+    gt += above;
+    const uint32_t blo = lo + (b << sh);
+    if (sh == 0) {
+      T = blo;
+      break;
+    }
+    const uint32_t wdt = (1u << sh) - 1u;
+    const uint32_t d = hi - blo;
+    lo = blo;
+    hi = blo + (d < wdt ? d : wdt);
+  }
+  __syncthreads();
+}
+
+template <class F>
+__device__ __forceinline__ void quad(const uint4& v, uint32_t e, F&& f) {
+  f(v.x, e);
+  f(v.y, e + 1);
+  f(v.z, e + 2);
+  f(v.w, e + 3);
+}
+
+// Calls f(bits, index) for every element of x[0, L), block-cooperatively, with
+// 128-bit loads for the aligned body. Lanes of a wave call f in lockstep (with
+// trailing lanes masked off), so f may use wave-wide ballots.
+template <class F>
+__device__ void for_each_element(const float* __restrict__ x, uint32_t L, F&& f) {
+  const uint32_t t = threadIdx.x;
+  const uint32_t* xu = reinterpret_cast<const uint32_t*>(x);
+  uint32_t head = (uint32_t)((4u - ((uint32_t)(reinterpret_cast<uintptr_t>(x) >> 2) & 3u)) & 3u);
+  if (head > L) head = L;
+  if (t < head) f(xu[t], t);
+  const uint32_t nv = (L - head) >> 2;
+  const uint4* p4 = reinterpret_cast<const uint4*>(xu + head);
+  const uint32_t per = BLOCK * UNROLL;
+  uint32_t q0 = 0;
+  for (; q0 + per <= nv; q0 += per) {
+    uint4 v[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) v[u] = p4[q0 + u * BLOCK + t];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) quad(v[u], head + 4u * (q0 + u * BLOCK + t), f);
+  }
+  for (uint32_t q = q0 + t; q < nv; q += BLOCK) quad(p4[q], head + 4u * q, f);
+  const uint32_t tail0 = head + 4u * nv;
+  if (t < L - tail0) f(xu[tail0 + t], tail0 + t);
+}
+
+__device__ __forceinline__ void stat_add(Control* ctl, int slot) {
+  atomicAdd(&ctl->stats[slot], 1ull);
+}
+
+// Zeroes the per-row counters and the histogram; ends with a barrier.
+__device__ __forceinline__ void reset_row_state(Smem& s) {
+  const uint32_t t = threadIdx.x;
+  for (uint32_t i = t; i < (uint32_t)NB; i += BLOCK) s.hist[i] = 0;
+  if (t == 0) {
+    s.cnt = 0;
+    s.cnt0 = 0;
+    s.fl_cnt = 0;
+    s.out_gt = 0;
+    s.out_tie = 0;
+    s.mn = KEY_MAX;
+    s.mx = 0;
+  }
+  __syncthreads();
+}
+
+// Commits keys > T (slots continue from s.out_gt) and `ties` keys == T (slots
+// gt_total + 0..) from a (key, index) list in LDS.
+__device__ __forceinline__ void commit_list(Smem& s, const uint32_t* keys, const uint32_t* idx,
+                                            uint32_t n, uint32_t T, uint32_t gt_total, uint32_t K,
+                                            int32_t* __restrict__ out) {
+  const uint32_t ties = K - gt_total;
+  for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
+    const uint32_t k = keys[i];
+    const uint32_t id = idx ? idx[i] : i;
+    const bool g = k > T;
+    const uint32_t p = wave_reserve(g, &s.out_gt);
+    if (g && p < K) out[p] = (int32_t)id;
+    const bool e = k == T;
+    const uint32_t q = wave_reserve(e, &s.out_tie);
+    if (e && q < ties && gt_total + q < K) out[gt_total + q] = (int32_t)id;
+  }
+}
+
+// ------------------------------------------------------ exact full-row select
+
+// Exact selection of K of x[0, L) read from global memory (L > K). [lo, hi] is a key
+// range expected to hold the K-th key; bins clamp outside it, so any range is
+// correct and a good one makes the boundary bin small. Pass 1 builds the
+// histogram; pass 2 commits every key above the boundary bin and collects the bin
+// into LDS; the bin is then resolved exactly. If the bin exceeds the LDS buffer,
+// the bin is narrowed by further passes over the row instead.
+__device__ void exact_full_row(Smem& s, const float* __restrict__ x, uint32_t L, uint32_t K,
+                               uint32_t lo, uint32_t hi, int32_t* __restrict__ out, Control* ctl) {
+  reset_row_state(s);
+  const uint32_t sh = shift_for(hi - lo);
+  for_each_element(x, L, [&](uint32_t u, uint32_t) {
+    const uint32_t k = key_of_bits(u);
+    const uint32_t d = k < lo ? 0u : (k - lo) >> sh;
+    atomicAdd(&s.hist[d < (uint32_t)(NB - 1) ? d : (uint32_t)(NB - 1)], 1u);
+  });
+  __syncthreads();
+  block_find_bin(s, K);
+  const uint32_t b = s.sel_bin, above = s.sel_above;
+  const uint32_t cb = s.hist[b];
+  const uint32_t need = K - above;
+  const uint32_t braw = lo + (b << sh);
+  const uint32_t blo = (b == 0) ? 0u : braw;
+  const uint32_t wdt = (1u << sh) - 1u;
+  const uint32_t bhi = (b == (uint32_t)(NB - 1)) ? KEY_MAX
+                                                 : braw + ((KEY_MAX - braw) < wdt ? (KEY_MAX - braw) : wdt);
+  const bool fits = cb <= (uint32_t)CAP;
+  __syncthreads();
+  for_each_element(x, L, [&](uint32_t u, uint32_t e) {
+    const uint32_t k = key_of_bits(u);
+    const bool g = k > bhi;
+    const uint32_t p = wave_reserve(g, &s.out_gt);
+    if (g && p < K) out[p] = (int32_t)e;
+    if (fits) {
+      const bool in = k >= blo && k <= bhi;
+      const uint32_t f = wave_reserve(in, &s.cnt);
+      if (in && f < (uint32_t)CAP) {
+        s.buf[f] = e;
+        s.buf[CAP + f] = k;
+      }
+    }
+  });
+  __syncthreads();
+  uint32_t T, gt2;
+  if (fits) {
+    const uint32_t* keys = &s.buf[CAP];
+    select_rank(s, [&](auto&& f) {
+      for (uint32_t i = threadIdx.x; i < cb; i += BLOCK) f(keys[i]);
+    }, need, blo, bhi, T, gt2);
+    commit_list(s, keys, s.buf, cb, T, above + gt2, K, out);
+  } else {
+    if (threadIdx.x == 0) stat_add(ctl, TOPK_STAT_FRONTIER_WIDE);
+    select_rank(s, [&](auto&& f) {
+      for_each_element(x, L, [&](uint32_t u, uint32_t) { f(key_of_bits(u)); });
+    }, need, blo, bhi, T, gt2);
+    const uint32_t gt_total = above + gt2;
+    const uint32_t ties = K - gt_total;
+    for_each_element(x, L, [&](uint32_t u, uint32_t e) {
+      const uint32_t k = key_of_bits(u);
+      const bool g = k > T && k <= bhi;
+      const uint32_t p = wave_reserve(g, &s.out_gt);
+      if (g && p < K) out[p] = (int32_t)e;
+      const bool q_ = k == T;
+      const uint32_t q = wave_reserve(q_, &s.out_tie);
+      if (q_ && q < ties && gt_total + q < K) out[gt_total + q] = (int32_t)e;
+    });
+  }
+}
+
+// ---------------------------------------------------------- direct (in LDS)
+
+__device__ void direct_exact(Smem& s, const float* __restrict__ x, uint32_t L, uint32_t K,
+                             int32_t* __restrict__ out) {
+  uint32_t mn = KEY_MAX, mx = 0;
+  for_each_element(x, L, [&](uint32_t u, uint32_t e) {
+    const uint32_t k = key_of_bits(u);
+    s.buf[e] = k;
+    mn = min(mn, k);
+    mx = max(mx, k);
+  });
+  block_minmax(s, mn, mx);
+  uint32_t T, gt;
+  select_rank(s, [&](auto&& f) {
+    for (uint32_t i = threadIdx.x; i < L; i += BLOCK) f(s.buf[i]);
+  }, K, s.mn, s.mx, T, gt);
+  commit_list(s, s.buf, nullptr, L, T, gt, K, out);
+}
+
+// ---------------------------------------------------------------- sampled path
+
+struct PassCtx {
+  uint32_t thr;    // raw-bit admission threshold (see admits)
+  uint32_t t1key;  // key(tau1): admitted keys are >= it
+  uint32_t t0key;  // key(tau0)
+  uint32_t sh;     // first-histogram shift
+};
+
+// key(u) >= key(tau1), evaluated on raw bits: for tau1 >= +0 it is a signed compare
+// against tau1's bits, for tau1 <= -0 an unsigned <= against tau1's bits.
+template <bool POS>
+__device__ __forceinline__ bool admits(uint32_t u, uint32_t thr) {
+  return POS ? ((int32_t)u >= (int32_t)thr) : (u <= thr);
+}
+
+template <bool POS>
+__device__ __forceinline__ bool quad_admits(const uint4& v, uint32_t thr) {
+  if (POS) {
+    const int32_t m = max(max((int32_t)v.x, (int32_t)v.y), max((int32_t)v.z, (int32_t)v.w));
+    return m >= (int32_t)thr;
+  } else {
+    const uint32_t m = min(min(v.x, v.y), min(v.z, v.w));
+    return m <= thr;
+  }
+}
+
+template <bool POS>
+__device__ __forceinline__ bool batch_admits(const uint4 (&v)[UNROLL], uint32_t thr) {
+  if (POS) {
+    int32_t m = (int32_t)v[0].x;
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+      m = max(max(m, max((int32_t)v[u].x, (int32_t)v[u].y)), max((int32_t)v[u].z, (int32_t)v[u].w));
+    return m >= (int32_t)thr;
+  } else {
+    uint32_t m = v[0].x;
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) m = min(min(m, min(v[u].x, v[u].y)), min(v[u].z, v[u].w));
+    return m <= thr;
+  }
+}
+
+// Candidate formation for one element slot across the wave: ballot, one LDS atomic
+// per wave for the base slot, prefix count for each lane's slot, histogram update
+// and the tau0 count. Every active lane of the wave must reach it.
+template <bool POS>
+__device__ __forceinline__ void admit_one(Smem& s, uint32_t u, uint32_t e, const PassCtx& c,
+                                          uint32_t& c0w) {
+  const bool pred = admits<POS>(u, c.thr);
+  const uint64_t m = __ballot(pred);
+  if (m == 0) return;
+  const int leader = __builtin_ctzll(m);
+  uint32_t b = 0;
+  if ((int)lane_id() == leader) b = atomicAdd(&s.cnt, (uint32_t)__popcll(m));
+  const uint32_t pos = __shfl(b, leader) + mbcnt64(m);
+  const uint32_t k = key_of_bits(u);
+  if (pred) {
+    if (pos < (uint32_t)CAP) {
+      s.buf[pos] = e;
+      s.buf[CAP + pos] = k;
+    }
+    const uint32_t d = (k - c.t1key) >> c.sh;
+    atomicAdd(&s.hist[d < (uint32_t)(NB - 1) ? d : (uint32_t)(NB - 1)], 1u);
+  }
+  c0w += (uint32_t)__popcll(__ballot(pred && k >= c.t0key));
+}
+
+template <bool POS>
+__device__ __forceinline__ void admit_quad(Smem& s, const uint4& v, uint32_t e, const PassCtx& c,
+                                           uint32_t& c0w) {
+  if (__ballot(quad_admits<POS>(v, c.thr)) == 0) return;
+  admit_one<POS>(s, v.x, e, c, c0w);
+  admit_one<POS>(s, v.y, e + 1, c, c0w);
+  admit_one<POS>(s, v.z, e + 2, c, c0w);
+  admit_one<POS>(s, v.w, e + 3, c, c0w);
+}
+
+// The mandatory full-row pass: certification counts, candidate compaction and the
+// first histogram, fused. The next batch of loads is issued before the current one
+// is examined so that each thread keeps 2 x UNROLL 128-bit loads in flight.
+template <bool POS>
+__device__ void fused_pass(Smem& s, const float* __restrict__ x, uint32_t L, const PassCtx& c) {
+  const uint32_t t = threadIdx.x;
+  uint32_t c0w = 0;
+  const uint32_t* xu = reinterpret_cast<const uint32_t*>(x);
+  uint32_t head = (uint32_t)((4u - ((uint32_t)(reinterpret_cast<uintptr_t>(x) >> 2) & 3u)) & 3u);
+  if (head > L) head = L;
+  if (t < head) admit_one<POS>(s, xu[t], t, c, c0w);
+  const uint32_t nv = (L - head) >> 2;
+  const uint4* __restrict__ p4 = reinterpret_cast<const uint4*>(xu + head);
+  const uint32_t per = BLOCK * UNROLL;
+  const uint32_t nfull = nv / per;
+  auto examine = [&](const uint4 (&v)[UNROLL], uint32_t it) {
+    if (__ballot(batch_admits<POS>(v, c.thr)) != 0) {
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u)
+        admit_quad<POS>(s, v[u], head + 4u * (it * per + u * BLOCK + t), c, c0w);
+    }
+  };
+  if (nfull > 0) {
+    // The prefetch is unconditional inside the loop (the last batch is peeled) so
+    // the compiler waits only for the batch being examined, not for the next one.
+    uint4 a[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) a[u] = p4[u * BLOCK + t];
+    uint32_t it = 0;
+    for (; it + 1 < nfull; ++it) {
+      uint4 nx[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) nx[u] = p4[(it + 1) * per + u * BLOCK + t];
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the examination
+      examine(a, it);
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) a[u] = nx[u];
+    }
+    examine(a, it);
+  }
+  for (uint32_t q = nfull * per + t; q < nv; q += BLOCK) admit_quad<POS>(s, p4[q], head + 4u * q, c, c0w);
+  const uint32_t tail0 = head + 4u * nv;
+  if (t < L - tail0) admit_one<POS>(s, xu[tail0 + t], tail0 + t, c, c0w);
+  if (lane_id() == 0 && c0w != 0) atomicAdd(&s.cnt0, c0w);
+}
+
+// Boundary refinement and commit after a certified pass: n = C(tau1) <= CAP
+// candidates are in LDS with the first histogram over (key - key(tau1)) >> sh.
+__device__ void refine_commit(Smem& s, uint32_t n, uint32_t K, const PassCtx& c,
+                              int32_t* __restrict__ out, Control* ctl) {
+  block_find_bin(s, K);
+  const uint32_t b = s.sel_bin, above = s.sel_above;
+  const uint32_t cb = s.hist[b];
+  const uint32_t need = K - above;
+  const uint32_t blo = c.t1key + (b << c.sh);
+  const uint32_t wdt = (1u << c.sh) - 1u;
+  const uint32_t bhi = (b == (uint32_t)(NB - 1)) ? KEY_MAX
+                                                 : blo + ((KEY_MAX - blo) < wdt ? (KEY_MAX - blo) : wdt);
+  const bool fits = cb <= (uint32_t)FL_CAP;
+  // Commit the resolved bins above b; move bin b to the frontier buffer.
+  for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
+    const uint32_t k = s.buf[CAP + i];
+    const uint32_t id = s.buf[i];
+    const bool g = k > bhi;
+    const uint32_t p = wave_reserve(g, &s.out_gt);
+    if (g && p < K) out[p] = (int32_t)id;
+    if (fits) {
+      const bool in = k >= blo && k <= bhi;
+      const uint32_t f = wave_reserve(in, &s.fl_cnt);
+      if (in && f < (uint32_t)FL_CAP) {
+        s.fl_idx[f] = id;
+        s.fl_key[f] = k;
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t T, gt2;
+  if (fits) {
+    select_rank(s, [&](auto&& f) {
+      for (uint32_t i = threadIdx.x; i < cb; i += BLOCK) f(s.fl_key[i]);
+    }, need, blo, bhi, T, gt2);
+    commit_list(s, s.fl_key, s.fl_idx, cb, T, above + gt2, K, out);
+  } else {
+    if (threadIdx.x == 0) stat_add(ctl, TOPK_STAT_FRONTIER_WIDE);
+    const uint32_t* keys = &s.buf[CAP];
+    select_rank(s, [&](auto&& f) {
+      for (uint32_t i = threadIdx.x; i < n; i += BLOCK) f(keys[i]);
+    }, need, blo, bhi, T, gt2);
+    const uint32_t gt_total = above + gt2;
+    const uint32_t ties = K - gt_total;
+    for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
+      const uint32_t k = keys[i];
+      const uint32_t id = s.buf[i];
+      const bool g = k > T && k <= bhi;
+      const uint32_t p = wave_reserve(g, &s.out_gt);
+      if (g && p < K) out[p] = (int32_t)id;
+      const bool e = k == T;
+      const uint32_t q = wave_reserve(e, &s.out_tie);
+      if (e && q < ties && gt_total + q < K) out[gt_total + q] = (int32_t)id;
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t sample_rank(uint32_t target, uint32_t n_s, uint32_t L) {
+  uint64_t r = ((uint64_t)target * n_s + L - 1) / L;
+  if (r < 1) r = 1;
+  if (r > n_s) r = n_s;
+  return (uint32_t)r;
+}
+
+__device__ void sampled_row(Smem& s, const Params& p, const float* __restrict__ x, uint32_t L,
+                            int32_t* __restrict__ out) {
+  const uint32_t t = threadIdx.x;
+  const uint32_t n_s = (L + STRIDE - 1) / STRIDE;
+  if (n_s > (uint32_t)KEYS_CAP) {
+    if (t == 0) stat_add(p.ctl, TOPK_STAT_LONG_EXACT);
+    exact_full_row(s, x, L, p.K, 0u, KEY_MAX, out, p.ctl);
+    return;
+  }
+  if (t == 0) stat_add(p.ctl, TOPK_STAT_SAMPLED);
+  // Fixed-stride row-local view: x[j * 128], j < ceil(L / 128).
+  const uint32_t* xu = reinterpret_cast<const uint32_t*>(x);
+  uint32_t mn = KEY_MAX, mx = 0;
+#pragma unroll 8
+  for (uint32_t j = t; j < n_s; j += BLOCK) {
+    const uint32_t k = key_of_bits(xu[(size_t)j * STRIDE]);
+    s.buf[j] = k;
+    mn = min(mn, k);
+    mx = max(mx, k);
+  }
+  block_minmax(s, mn, mx);
+  const uint32_t smin = s.mn, smax = s.mx;
+  const uint32_t r1 = sample_rank(p.T1, n_s, L);
+  const uint32_t r0 = sample_rank(p.T0, n_s, L);
+  uint32_t t1key, t0key, unused;
+  select_rank(s, [&](auto&& f) {
+    for (uint32_t i = t; i < n_s; i += BLOCK) f(s.buf[i]);
+  }, r1, smin, smax, t1key, unused);
+  select_rank(s, [&](auto&& f) {
+    for (uint32_t i = t; i < n_s; i += BLOCK) f(s.buf[i]);
+  }, r0, t1key, smax, t0key, unused);
+
+  PassCtx c;
+  c.t1key = t1key;
+  c.t0key = t0key;
+  c.sh = shift_for(smax - t1key);
+  const bool pos = t1key >= 0x80000000u;
+  c.thr = pos ? (t1key ^ 0x80000000u) : ~t1key;
+  reset_row_state(s);
+  if (pos) fused_pass<true>(s, x, L, c);
+  else fused_pass<false>(s, x, L, c);
+  __syncthreads();
+  const uint32_t c1 = s.cnt, c0 = s.cnt0;
+  if (c1 > (uint32_t)CAP) {
+    // Too many admitted to hold: the K-th key is >= tau1, recover exactly.
+    if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_OVER);
+    exact_full_row(s, x, L, p.K, t1key, smax, out, p.ctl);
+  } else if (c1 < p.K) {
+    // Even the nested threshold underfills: the K-th key is < tau1.
+    if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_UNDER);
+    exact_full_row(s, x, L, p.K, smin, t1key, out, p.ctl);
+  } else {
+    if (t == 0) stat_add(p.ctl, c0 >= p.K ? TOPK_STAT_TAU0 : TOPK_STAT_TAU1);
+    refine_commit(s, c1, p.K, c, out, p.ctl);
+  }
+}
+
+__device__ void process_row(Smem& s, const Params& p, uint32_t row) {
+  const uint32_t t = threadIdx.x;
+  int32_t len = p.row_len[row];
+  uint32_t L = len < 0 ? 0u : (uint32_t)len;
+  if (L > p.N) L = p.N;
+  const float* __restrict__ x = p.scores + (size_t)row * p.N;
+  int32_t* __restrict__ out = p.out + (size_t)row * p.K;
+  if (t == 0) stat_add(p.ctl, TOPK_STAT_ROWS);
+  if (L <= p.K) {
+    for (uint32_t j = t; j < p.K; j += BLOCK) out[j] = j < L ? (int32_t)j : p.sentinel;
+    if (t == 0) stat_add(p.ctl, TOPK_STAT_SENTINEL);
+    return;
+  }
+  reset_row_state(s);
+  const bool direct = (p.mode == TOPK_PATH_DIRECT) || (p.mode == TOPK_PATH_AUTO && L <= p.direct_max);
+  if (direct) {
+    if (t == 0) stat_add(p.ctl, TOPK_STAT_DIRECT);
+    if (L <= (uint32_t)KEYS_CAP) direct_exact(s, x, L, p.K, out);
+    else exact_full_row(s, x, L, p.K, 0u, KEY_MAX, out, p.ctl);
+  } else if (p.mode == TOPK_PATH_RECOVERY) {
+    if (t == 0) stat_add(p.ctl, TOPK_STAT_FORCED_RECOVERY);
+    exact_full_row(s, x, L, p.K, 0u, KEY_MAX, out, p.ctl);
+  } else {
+    sampled_row(s, p, x, L, out);
+  }
+}
+
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
+void topk_rows_kernel(Params p) {
+  __shared__ Smem s;
+  const uint32_t t = threadIdx.x;
+  for (;;) {
+    if (t == 0) s.row = (int32_t)atomicAdd(&p.ctl->row_ticket, 1u);
+    __syncthreads();
+    const uint32_t row = (uint32_t)s.row;
+    if (row >= p.M) break;
+    process_row(s, p, row);
+    __syncthreads();
+  }
+  // The last workgroup to leave rewinds the row ticket for the next call. Every
+  // workgroup increments done_ticket only after its final ticket draw, so no draw
+  // can follow the rewind.
+  if (t == 0) {
+    __threadfence();
+    const uint32_t d = atomicAdd(&p.ctl->done_ticket, 1u);
+    if (d == gridDim.x - 1) {
+      atomicExch(&p.ctl->row_ticket, 0u);
+      atomicExch(&p.ctl->done_ticket, 0u);
+    }
+  }
+}
+
+__global__ void zero_stats_kernel(Control* ctl) {
+  const uint32_t t = threadIdx.x;
+  if (t < (uint32_t)TOPK_STAT_COUNT) ctl->stats[t] = 0ull;
+}
+
+__global__ __launch_bounds__(BLOCK) void stream_read_probe_kernel(const float* __restrict__ x, uint64_t n,
+                                                                  float* __restrict__ sink) {
+  const uint4* p4 = reinterpret_cast<const uint4*>(x);
+  const uint64_t nv = n >> 2;
+  uint32_t acc = 0;
+  const uint64_t stride = (uint64_t)gridDim.x * BLOCK;
+  uint64_t q = (uint64_t)blockIdx.x * BLOCK + threadIdx.x;
+  for (; q + 3 * stride < nv; q += 4 * stride) {
+    const uint4 a = p4[q], b = p4[q + stride], c = p4[q + 2 * stride], d = p4[q + 3 * stride];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; q < nv; q += stride) {
+    const uint4 a = p4[q];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (blockIdx.x == 0) {
+    const uint32_t* xu = reinterpret_cast<const uint32_t*>(x);
+    for (uint64_t i = 4 * nv + threadIdx.x; i < n; i += BLOCK) acc ^= xu[i];
+  }
+  acc = wave_max_u32(acc);  // any combine that depends on every lane keeps the loads live
+  __shared__ uint32_t w[NWAVES];
+  if (lane_id() == 0) w[threadIdx.x / WAVE] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t v = 0;
+    for (int i = 0; i < NWAVES; ++i) v ^= w[i];
+    sink[blockIdx.x] = __uint_as_float(v);
+  }
+}
+
+// ------------------------------------------------------------------- host side
+
+struct DevState {
+  bool ready = false;
+  int n_cu = 0;
+  int occ = 0;
+  Control* ctl = nullptr;
+};
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_mu;
+DevState g_dev[MAX_DEVICES];
+std::atomic<int> g_mode{TOPK_PATH_AUTO};
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(TOPK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Returns the current device's state, creating it when allowed.
+int get_state(bool capturing, DevState** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(TOPK_ERR_HIP, "device index %d unsupported", dev);
+  std::lock_guard<std::mutex> lock(g_mu);
+  DevState& st = g_dev[dev];
+  if (!st.ready) {
+    if (capturing)
+      return fail(TOPK_ERR_WORKSPACE,
+                  "workspace not created on device %d; call topk_exact_reserve before capturing", dev);
+    int n_cu = 0, occ = 0;
+    e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(topk_rows_kernel),
+                                                     BLOCK, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    if (occ < 1) return fail(TOPK_ERR_HIP, "selector kernel cannot be resident (occupancy %d)", occ);
+    Control* ctl = nullptr;
+    e = hipMalloc(reinterpret_cast<void**>(&ctl), sizeof(Control));
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
+    e = hipMemset(ctl, 0, sizeof(Control));
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      (void)hipFree(ctl);
+      return hip_fail(e, "workspace initialisation");
+    }
+    st.n_cu = n_cu;
+    st.occ = occ;
+    st.ctl = ctl;
+    st.ready = true;
+  }
+  *out = &st;
+  return TOPK_OK;
+}
+
+int stream_capturing(hipStream_t stream, bool* capturing) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  *capturing = cs != hipStreamCaptureStatusNone;
+  return TOPK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc, int32_t K,
+               int32_t* out_idx, int32_t sentinel, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (M < 0) return fail(TOPK_ERR_BAD_SHAPE, "M = %lld is negative", (long long)M);
+  if (N_alloc < 1 || N_alloc > INT32_MAX)
+    return fail(TOPK_ERR_BAD_SHAPE, "N_alloc = %lld outside [1, INT32_MAX]", (long long)N_alloc);
+  if (K < 1 || K > TOPK_K_MAX) return fail(TOPK_ERR_BAD_K, "K = %d outside [1, %d]", K, TOPK_K_MAX);
+  if (M > INT32_MAX) return fail(TOPK_ERR_BAD_SHAPE, "M = %lld exceeds INT32_MAX", (long long)M);
+  if (M > 0 && (N_alloc > INT64_MAX / M || (int64_t)K > INT64_MAX / M))
+    return fail(TOPK_ERR_BAD_SHAPE, "M*N_alloc or M*K overflows");
+  if (sentinel >= 0 && (int64_t)sentinel < N_alloc)
+    return fail(TOPK_ERR_BAD_SENTINEL, "sentinel %d lies inside [0, N_alloc = %lld)", sentinel,
+                (long long)N_alloc);
+  if (M == 0) return TOPK_OK;
+  if (!scores || !row_len || !out_idx) return fail(TOPK_ERR_NULL_POINTER, "null scores/row_len/out_idx");
+  if ((reinterpret_cast<uintptr_t>(scores) & 3u) != 0)
+    return fail(TOPK_ERR_BAD_ARG, "scores is not 4-byte aligned");
+
+  bool capturing = false;
+  int rc = stream_capturing(stream, &capturing);
+  if (rc != TOPK_OK) return rc;
+  DevState* st = nullptr;
+  rc = get_state(capturing, &st);
+  if (rc != TOPK_OK) return rc;
+
+  Params p;
+  p.scores = scores;
+  p.row_len = row_len;
+  p.out = out_idx;
+  p.ctl = st->ctl;
+  p.M = (uint32_t)M;
+  p.N = (uint32_t)N_alloc;
+  p.K = (uint32_t)K;
+  p.sentinel = sentinel;
+  p.T0 = (uint32_t)((3 * K + 1) / 2);
+  p.T1 = (uint32_t)((7 * K + 3) / 4);
+  p.direct_max = DIRECT_MAX_DEFAULT;
+  p.mode = g_mode.load();
+  const int64_t resident = (int64_t)st->occ * st->n_cu;
+  const unsigned grid = (unsigned)(M < resident ? M : resident);
+  hipLaunchKernelGGL(topk_rows_kernel, dim3(grid), dim3(BLOCK), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "launch topk_rows_kernel");
+  return TOPK_OK;
+}
+
+int topk_exact_reserve(int64_t M_max, int64_t N_alloc_max, int32_t K) {
+  g_err[0] = '\0';
+  if (M_max < 0 || N_alloc_max < 1 || N_alloc_max > INT32_MAX)
+    return fail(TOPK_ERR_BAD_SHAPE, "bad reserve shape");
+  if (K < 1 || K > TOPK_K_MAX) return fail(TOPK_ERR_BAD_K, "K = %d outside [1, %d]", K, TOPK_K_MAX);
+  DevState* st = nullptr;
+  return get_state(false, &st);
+}
+
+int topk_exact_get_stats(uint64_t* host_counts, int n, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (!host_counts) return fail(TOPK_ERR_NULL_POINTER, "host_counts is null");
+  if (n < 0 || n > TOPK_STAT_COUNT) return fail(TOPK_ERR_BAD_ARG, "n = %d outside [0, %d]", n, TOPK_STAT_COUNT);
+  bool capturing = false;
+  int rc = stream_capturing(stream, &capturing);
+  if (rc != TOPK_OK) return rc;
+  if (capturing) return fail(TOPK_ERR_BAD_ARG, "topk_exact_get_stats cannot run under capture");
+  DevState* st = nullptr;
+  rc = get_state(false, &st);
+  if (rc != TOPK_OK) return rc;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  unsigned long long tmp[TOPK_STAT_COUNT];
+  e = hipMemcpy(tmp, st->ctl->stats, sizeof(tmp), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy(stats)");
+  for (int i = 0; i < n; ++i) host_counts[i] = tmp[i];
+  return TOPK_OK;
+}
+
+int topk_exact_reset_stats(hipStream_t stream) {
+  g_err[0] = '\0';
+  bool capturing = false;
+  int rc = stream_capturing(stream, &capturing);
+  if (rc != TOPK_OK) return rc;
+  DevState* st = nullptr;
+  rc = get_state(capturing, &st);
+  if (rc != TOPK_OK) return rc;
+  hipLaunchKernelGGL(zero_stats_kernel, dim3(1), dim3(64), 0, stream, st->ctl);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "launch zero_stats_kernel");
+  return TOPK_OK;
+}
+
+int topk_exact_set_path_override(int mode) {
+  g_err[0] = '\0';
+  if (mode < TOPK_PATH_AUTO || mode > TOPK_PATH_RECOVERY)
+    return fail(TOPK_ERR_BAD_ARG, "path mode %d unknown", mode);
+  g_mode.store(mode);
+  return TOPK_OK;
+}
+
+const char* topk_exact_last_error(void) { return g_err; }
+
+int topk_stream_read_probe(const float* x, int64_t n, float* sink, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (n < 0) return fail(TOPK_ERR_BAD_SHAPE, "n = %lld is negative", (long long)n);
+  if (n == 0) return TOPK_OK;
+  if (!x || !sink) return fail(TOPK_ERR_NULL_POINTER, "null x/sink");
+  if ((reinterpret_cast<uintptr_t>(x) & 15u) != 0) return fail(TOPK_ERR_BAD_ARG, "x must be 16-byte aligned");
+  bool capturing = false;
+  int rc = stream_capturing(stream, &capturing);
+  if (rc != TOPK_OK) return rc;
+  DevState* st = nullptr;
+  rc = get_state(capturing, &st);
+  if (rc != TOPK_OK) return rc;
+  int64_t want = (n / 4 + BLOCK * 16 - 1) / (BLOCK * 16);
+  int64_t cap = (int64_t)st->n_cu * 8;
+  if (cap > 4096) cap = 4096;
+  const unsigned grid = (unsigned)(want < 1 ? 1 : (want < cap ? want : cap));
+  hipLaunchKernelGGL(stream_read_probe_kernel, dim3(grid), dim3(BLOCK), 0, stream, x, (uint64_t)n, sink);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "launch stream_read_probe_kernel");
+  return TOPK_OK;
+}
+
+}  // extern "C"

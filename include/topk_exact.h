@@ -1,0 +1,134 @@
+/* topk_exact.h -- C ABI of the MI355X (gfx950) sample-guided exact Top-K selector.
+ *
+ * Pages cited (by title):
+ *   [Cx] "几何平均快 1.55 倍，但短行采样会输：腾讯怎么测精确 Top-K" (codexqa.cn
+ *        write-up of the HPC-Ops Top-K paper)
+ *   [PD] "腾讯|长上下文稀疏注意力前K精确选择:20种配置平均加速1.55倍" (PaperDaily
+ *        explainer of the same paper)
+ *   [AX] "Sample-Guided Exact Top-K Selection for Long-Context Sparse Attention"
+ *        (arxivdaily abstract page)
+ *
+ * The operation ([Cx] section "什么叫精确，时间怎么量"; [AX] abstract): for every
+ * row r of an M x N_alloc FP32 score matrix whose valid prefix has length
+ * L_r = row_len[r], return the indices of the K largest scores of that prefix.
+ * Indices are distinct and lie in [0, L_r). When L_r > K exactly K indices are
+ * returned and min(selected) >= max(unselected); boundary ties may go either way
+ * and the order is unspecified. When L_r <= K all L_r valid indices are returned
+ * and the remaining slots hold the caller's sentinel. There is no float
+ * tolerance: scores are compared as IEEE-754 totalOrder on their 32-bit
+ * patterns (so -0 < +0), which is this library's reading of "exact" on the
+ * original FP32 values ([PD] question 2, Fig. 4 stage-3 caption).
+ *
+ * How ([PD] question 2, Fig. 4; [AX] abstract): a fixed-stride sample of the
+ * row (stride 128) proposes a primary threshold tau0 aimed at about 1.5K
+ * candidates and a nested, wider tau1 aimed at about 1.75K ([Cx] section
+ * "采样不是处处都该开"); one mandatory full-row pass certifies the candidate
+ * count, compacts the admitted candidates into LDS and builds the first radix
+ * histogram; exact radix refinement then runs only on the unresolved boundary
+ * bin. Underfilled or overflowing proposals fall back to exact full-row
+ * recovery before anything is written. Short rows take a direct exact path.
+ * All work is enqueued on the caller's stream and is graph-capturable.
+ *
+ * Threading and streams: the library keeps one small workspace per device
+ * (control counters and statistics). Calls that overlap in time on one device
+ * (for example on two streams without ordering between them) share it and race;
+ * order such calls on one stream. Every pointer argument named "device" must be
+ * memory of the current HIP device.
+ */
+#ifndef TOPK_EXACT_H
+#define TOPK_EXACT_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TOPK_OK = 0,
+  TOPK_ERR_NULL_POINTER = 1, /* scores, row_len or out_idx is NULL while M > 0 */
+  TOPK_ERR_BAD_SHAPE = 2,    /* M < 0, N_alloc < 1, N_alloc > INT32_MAX, or M*N_alloc, M*K overflow */
+  TOPK_ERR_BAD_K = 3,        /* K < 1 or K > TOPK_K_MAX */
+  TOPK_ERR_BAD_SENTINEL = 4, /* 0 <= sentinel < N_alloc: it would look like a valid index */
+  TOPK_ERR_WORKSPACE = 5,    /* workspace missing or too small while the stream is capturing */
+  TOPK_ERR_HIP = 6,          /* a HIP call or launch failed; see topk_exact_last_error() */
+  TOPK_ERR_BAD_ARG = 7       /* another argument is out of range (stats/override calls) */
+} topk_status_t;
+
+#define TOPK_K_MAX 2048
+
+/* Path override modes (test and benchmark use; default TOPK_PATH_AUTO). */
+#define TOPK_PATH_AUTO 0      /* per-row choice: sentinel, direct-exact or sampled */
+#define TOPK_PATH_SAMPLED 1   /* every row with L > K takes the sampled path */
+#define TOPK_PATH_ROWSPLIT 2  /* every row with L > K takes the row-split sampled path */
+#define TOPK_PATH_DIRECT 3    /* every row with L > K takes the direct exact path */
+#define TOPK_PATH_RECOVERY 4  /* every row with L > K takes exact full-row recovery */
+
+/* Statistics slots returned by topk_exact_get_stats (row counts since the last reset). */
+enum {
+  TOPK_STAT_ROWS = 0,            /* rows processed */
+  TOPK_STAT_SENTINEL = 1,        /* rows with L <= K */
+  TOPK_STAT_DIRECT = 2,          /* rows finished by the direct exact path */
+  TOPK_STAT_SAMPLED = 3,         /* rows that took the sampled proposal */
+  TOPK_STAT_TAU0 = 4,            /* sampled rows certified at tau0: C(tau0) >= K */
+  TOPK_STAT_TAU1 = 5,            /* sampled rows with C(tau0) < K <= C(tau1) (nested fallback) */
+  TOPK_STAT_RECOVER_UNDER = 6,   /* sampled rows with C(tau1) < K: exact full-row recovery */
+  TOPK_STAT_RECOVER_OVER = 7,    /* sampled rows whose candidates overflowed: exact recovery */
+  TOPK_STAT_ROWSPLIT = 8,        /* rows scanned by several workgroups (row-split) */
+  TOPK_STAT_FORCED_RECOVERY = 9, /* rows sent to exact recovery by TOPK_PATH_RECOVERY */
+  TOPK_STAT_LONG_EXACT = 10,     /* rows too long for the LDS sample: exact full-row path */
+  TOPK_STAT_FRONTIER_WIDE = 11,  /* refinements whose boundary bin exceeded the frontier buffer */
+  TOPK_STAT_QUEUED = 12,         /* recovery rows handed to the cooperative recovery kernels */
+  TOPK_STAT_COUNT = 16
+};
+
+/* Selects the top-K indices of every row.
+ *   scores   device, row-major [M][N_alloc] float32, row stride N_alloc; read-only. Only
+ *            the first clamp(row_len[r], 0, N_alloc) entries of row r are ever read.
+ *   row_len  device, [M] int32, valid prefix length per row. Values outside [0, N_alloc]
+ *            violate the precondition; they are clamped into it so that no access goes
+ *            out of bounds, and the result for that row is then only guaranteed in-bounds.
+ *   M, N_alloc, K  sizes: M >= 0, 1 <= N_alloc <= INT32_MAX, 1 <= K <= TOPK_K_MAX.
+ *   out_idx  device, row-major [M][K] int32; every slot is written. For L > K: K distinct
+ *            indices in [0, L), any order. For L <= K: slots [0, L) hold 0..L-1 in some
+ *            order and slots [L, K) hold `sentinel`.
+ *   sentinel value for empty slots; must lie outside [0, N_alloc) (e.g. -1).
+ *   stream   every launch is enqueued here; the call never synchronizes, allocates or
+ *            reads device memory from the host once the workspace exists, so it may be
+ *            captured into a HIP graph (call topk_exact_reserve first in that case).
+ * Returns TOPK_OK, or an error code before anything is enqueued. M == 0 is a no-op.
+ * Asynchronous device faults surface on the stream like any kernel's. */
+int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc,
+               int32_t K, int32_t* out_idx, int32_t sentinel, hipStream_t stream);
+
+/* Creates the current device's workspace sized for calls up to (M_max, N_alloc_max, K)
+ * and resolves launch parameters. Synchronous; call it outside stream capture before
+ * capturing topk_exact. Calls with larger sizes grow the workspace when not capturing. */
+int topk_exact_reserve(int64_t M_max, int64_t N_alloc_max, int32_t K);
+
+/* Copies up to n (<= TOPK_STAT_COUNT) statistics counters of the current device into
+ * host_counts (host memory). Synchronizes `stream` first. Not capturable. */
+int topk_exact_get_stats(uint64_t* host_counts, int n, hipStream_t stream);
+
+/* Zeroes the current device's statistics counters (enqueued on `stream`). */
+int topk_exact_reset_stats(hipStream_t stream);
+
+/* Forces one execution path for later calls (TOPK_PATH_*); a captured graph keeps the
+ * mode that was set when it was captured. Process-wide. */
+int topk_exact_set_path_override(int mode);
+
+/* Text of the last error raised on this host thread ("" if none). */
+const char* topk_exact_last_error(void);
+
+/* Bandwidth probe (measurement only, not part of the selection): reads n floats from
+ * `x` (device) with the same 128-bit load pattern as the selector's full-row pass and
+ * writes one float per workgroup into `sink` (device, >= 4096 floats) so the reads
+ * cannot be elided. Used to report a measured HBM read ceiling next to the peak. */
+int topk_stream_read_probe(const float* x, int64_t n, float* sink, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOPK_EXACT_H */

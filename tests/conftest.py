@@ -25,3 +25,12 @@ _ensure_built()
 @pytest.fixture(scope="session")
 def repo_root():
     return ROOT
+
+
+def _ensure_hip_built():
+    from exact_top_selection_stride_amd import build as hip_build
+    if not os.path.exists(hip_build.LIB):
+        hip_build.build()
+
+
+_ensure_hip_built()
