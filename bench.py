@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle leg")
     ap.add_argument("--check-rows", type=int, default=32, help="rows per group checked before timing")
     ap.add_argument("--probe", action="store_true", help="also time the stream-read probe")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy first (known bytes, for counter calibration)")
     return ap.parse_args()
 
 
@@ -84,28 +86,25 @@ def gate_rows(scores, lengths, out, K, sentinel, rows):
     return bad
 
 
-def cpu_baseline(scores, lengths, K, sentinel, target_s):
-    """Times the CPU oracle on a bounded leading block of the group's rows."""
+def cpu_baseline(scores, lengths, K, sentinel, target_s, max_rows=1024):
+    """Times the CPU oracle on a bounded leading block of the group's rows, repeating
+    the block until about target_s seconds of selection work have been timed."""
     import numpy as np
     import oracle
     threads = oracle.default_threads()
-    n = min(int(lengths.shape[0]), max(threads, 16))
-    done_rows, spent = 0, 0.0
-    while True:
-        blk_s = scores[done_rows:done_rows + n].cpu().numpy()
-        blk_l = lengths[done_rows:done_rows + n].cpu().numpy().astype(np.int32)
+    n = min(int(lengths.shape[0]), max_rows)
+    blk_s = scores[:n].cpu().numpy()
+    blk_l = lengths[:n].cpu().numpy().astype(np.int32)
+    done_rows, spent, reps = 0, 0.0, 0
+    while spent < target_s and reps < 50:
         t0 = time.perf_counter()
         oracle.topk(blk_s, blk_l, K, sentinel, n_threads=threads)
         spent += time.perf_counter() - t0
         done_rows += n
-        if spent >= target_s or done_rows >= int(lengths.shape[0]):
-            break
-        per_row = spent / done_rows
-        n = int(min(lengths.shape[0] - done_rows, max(threads, (target_s - spent) / per_row)))
-        n = max(1, min(n, 1024))
+        reps += 1
     return {"value": done_rows / spent, "unit": "rows/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {done_rows} rows of the timed group (same lengths and values), "
-                      f"{spent:.1f} s of selection on host copies"}
+            "sample": f"first {n} rows of the timed group (same lengths and values) selected "
+                      f"{reps} times on host copies, {spent:.1f} s of selection"}
 
 
 def main():
@@ -123,6 +122,14 @@ def main():
     w = W.get(args.workload)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        # A plain copy of exactly 2^28 floats (1 GiB read + 1 GiB written) per launch.
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     t_gen = time.perf_counter()
     window, lengths = W.make_window(w, dev)
     torch.cuda.synchronize()

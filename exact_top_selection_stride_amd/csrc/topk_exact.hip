@@ -40,6 +40,11 @@
 // builds keys: admission key(u) >= key(tau1) is a single signed compare of u
 // (tau1 >= +0) or unsigned compare (tau1 <= -0). No floating-point arithmetic
 // happens anywhere on the path.
+//
+// Code conventions: the workgroup's LDS state is one file-scope __shared__
+// object, and score/output rows are handled through address-space-1 (global)
+// pointers, so the per-row function can stay out of line (register allocation
+// per phase) while every access still compiles to ds_* / global_* instructions.
 
 #include "topk_exact.h"
 
@@ -52,7 +57,13 @@
 #include <cstring>
 #include <mutex>
 
+#define GLB __attribute__((address_space(1)))
+
 namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef const GLB uint32_t* grow_t;   // a row of score bit patterns
+typedef GLB int32_t* gout_t;          // a row of output indices
 
 constexpr int BLOCK = 512;            // threads per workgroup (8 waves of 64)
 constexpr int WAVE = 64;
@@ -108,6 +119,8 @@ struct Smem {
   int32_t row;
 };
 
+__shared__ Smem g_s;  // the selector workgroup's LDS state
+
 // ---------------------------------------------------------------- primitives
 
 __device__ __forceinline__ uint32_t key_of_bits(uint32_t u) {
@@ -120,6 +133,10 @@ __device__ __forceinline__ uint32_t mbcnt64(uint64_t m) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
+
+__device__ __forceinline__ u32x4 load4(grow_t p) { return *reinterpret_cast<const GLB u32x4*>(p); }
+
+__device__ __forceinline__ u32x4 splat4(uint32_t v) { return u32x4{v, v, v, v}; }
 
 // Reserves consecutive slots of an LDS counter for the lanes whose pred is set, one
 // atomic per wave. Every active lane of the wave must reach it.
@@ -160,9 +177,14 @@ __device__ __forceinline__ uint32_t shift_for(uint32_t span) {
   return (32u - (uint32_t)__clz(span)) - NB_BITS;
 }
 
+__device__ __forceinline__ void stat_add(Control* ctl, int slot) {
+  atomicAdd(&ctl->stats[slot], 1ull);
+}
+
 // Folds per-thread min/max into s.mn / s.mx (initialised by the caller before a
 // barrier). Ends with a barrier.
-__device__ __forceinline__ void block_minmax(Smem& s, uint32_t mn, uint32_t mx) {
+__device__ __forceinline__ void block_minmax(uint32_t mn, uint32_t mx) {
+  Smem& s = g_s;
   mn = wave_min_u32(mn);
   mx = wave_max_u32(mx);
   if (lane_id() == 0) {
@@ -175,7 +197,8 @@ __device__ __forceinline__ void block_minmax(Smem& s, uint32_t mn, uint32_t mx) 
 // Finds the bin b holding rank r (1-based, counted from the top) of s.hist and the
 // count of entries in bins above it. Requires 1 <= r <= sum(hist). Result in
 // s.sel_bin / s.sel_above; starts and ends with a barrier-protected section.
-__device__ void block_find_bin(Smem& s, uint32_t r) {
+__device__ void block_find_bin(uint32_t r) {
+  Smem& s = g_s;
   constexpr int PER = NB / BLOCK;
   const uint32_t t = threadIdx.x;
   uint32_t h[PER];
@@ -223,8 +246,9 @@ __device__ void block_find_bin(Smem& s, uint32_t r) {
 // round bins the range into NB buckets, keeps only the bucket holding rank r, and
 // shrinks the range by 2^11, so at most three rounds run.
 template <class ForKeys>
-__device__ void select_rank(Smem& s, ForKeys&& for_keys, uint32_t r, uint32_t lo, uint32_t hi,
-                            uint32_t& T, uint32_t& gt) {
+__device__ void select_rank(ForKeys&& for_keys, uint32_t r, uint32_t lo, uint32_t hi, uint32_t& T,
+                            uint32_t& gt) {
+  Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   gt = 0;
   for (;;) {
@@ -236,7 +260,7 @@ __device__ void select_rank(Smem& s, ForKeys&& for_keys, uint32_t r, uint32_t lo
       if (k >= lo_ && k <= hi_) atomicAdd(&s.hist[(k - lo_) >> sh], 1u);
     });
     __syncthreads();
-    block_find_bin(s, r);
+    block_find_bin(r);
     const uint32_t b = s.sel_bin, above = s.sel_above;
     r -= above;
     gt += above;
@@ -254,7 +278,7 @@ __device__ void select_rank(Smem& s, ForKeys&& for_keys, uint32_t r, uint32_t lo
 }
 
 template <class F>
-__device__ __forceinline__ void quad(const uint4& v, uint32_t e, F&& f) {
+__device__ __forceinline__ void quad(const u32x4& v, uint32_t e, F&& f) {
   f(v.x, e);
   f(v.y, e + 1);
   f(v.z, e + 2);
@@ -265,34 +289,30 @@ __device__ __forceinline__ void quad(const uint4& v, uint32_t e, F&& f) {
 // 128-bit loads for the aligned body. Lanes of a wave call f in lockstep (with
 // trailing lanes masked off), so f may use wave-wide ballots.
 template <class F>
-__device__ void for_each_element(const float* __restrict__ x, uint32_t L, F&& f) {
+__device__ void for_each_element(grow_t x, uint32_t L, F&& f) {
   const uint32_t t = threadIdx.x;
-  const uint32_t* xu = reinterpret_cast<const uint32_t*>(x);
-  uint32_t head = (uint32_t)((4u - ((uint32_t)(reinterpret_cast<uintptr_t>(x) >> 2) & 3u)) & 3u);
+  uint32_t head = (uint32_t)((4u - ((uint32_t)((uintptr_t)x >> 2) & 3u)) & 3u);
   if (head > L) head = L;
-  if (t < head) f(xu[t], t);
+  if (t < head) f(x[t], t);
   const uint32_t nv = (L - head) >> 2;
-  const uint4* p4 = reinterpret_cast<const uint4*>(xu + head);
+  grow_t body = x + head;
   const uint32_t per = BLOCK * UNROLL;
   uint32_t q0 = 0;
   for (; q0 + per <= nv; q0 += per) {
-    uint4 v[UNROLL];
+    u32x4 v[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) v[u] = p4[q0 + u * BLOCK + t];
+    for (int u = 0; u < UNROLL; ++u) v[u] = load4(body + 4u * (q0 + u * BLOCK + t));
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) quad(v[u], head + 4u * (q0 + u * BLOCK + t), f);
   }
-  for (uint32_t q = q0 + t; q < nv; q += BLOCK) quad(p4[q], head + 4u * q, f);
+  for (uint32_t q = q0 + t; q < nv; q += BLOCK) quad(load4(body + 4u * q), head + 4u * q, f);
   const uint32_t tail0 = head + 4u * nv;
-  if (t < L - tail0) f(xu[tail0 + t], tail0 + t);
-}
-
-__device__ __forceinline__ void stat_add(Control* ctl, int slot) {
-  atomicAdd(&ctl->stats[slot], 1ull);
+  if (t < L - tail0) f(x[tail0 + t], tail0 + t);
 }
 
 // Zeroes the per-row counters and the histogram; ends with a barrier.
-__device__ __forceinline__ void reset_row_state(Smem& s) {
+__device__ __forceinline__ void reset_row_state() {
+  Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   for (uint32_t i = t; i < (uint32_t)NB; i += BLOCK) s.hist[i] = 0;
   if (t == 0) {
@@ -307,11 +327,11 @@ __device__ __forceinline__ void reset_row_state(Smem& s) {
   __syncthreads();
 }
 
-// Commits keys > T (slots continue from s.out_gt) and `ties` keys == T (slots
-// gt_total + 0..) from a (key, index) list in LDS.
-__device__ __forceinline__ void commit_list(Smem& s, const uint32_t* keys, const uint32_t* idx,
-                                            uint32_t n, uint32_t T, uint32_t gt_total, uint32_t K,
-                                            int32_t* __restrict__ out) {
+// Commits keys > T (slots continue from s.out_gt) and up to K - gt_total keys == T
+// (slots gt_total + 0..) from a key list in LDS with indices idx (or the position).
+__device__ __forceinline__ void commit_list(const uint32_t* keys, const uint32_t* idx, uint32_t n,
+                                            uint32_t T, uint32_t gt_total, uint32_t K, gout_t out) {
+  Smem& s = g_s;
   const uint32_t ties = K - gt_total;
   for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
     const uint32_t k = keys[i];
@@ -330,12 +350,13 @@ __device__ __forceinline__ void commit_list(Smem& s, const uint32_t* keys, const
 // Exact selection of K of x[0, L) read from global memory (L > K). [lo, hi] is a key
 // range expected to hold the K-th key; bins clamp outside it, so any range is
 // correct and a good one makes the boundary bin small. Pass 1 builds the
-// histogram; pass 2 commits every key above the boundary bin and collects the bin
+// histogram; pass 2 commits every key above the boundary bin and collects that bin
 // into LDS; the bin is then resolved exactly. If the bin exceeds the LDS buffer,
-// the bin is narrowed by further passes over the row instead.
-__device__ void exact_full_row(Smem& s, const float* __restrict__ x, uint32_t L, uint32_t K,
-                               uint32_t lo, uint32_t hi, int32_t* __restrict__ out, Control* ctl) {
-  reset_row_state(s);
+// it is narrowed by further passes over the row instead.
+__device__ __attribute__((noinline)) void exact_full_row(grow_t x, uint32_t L, uint32_t K, uint32_t lo,
+                                                         uint32_t hi, gout_t out, Control* ctl) {
+  Smem& s = g_s;
+  reset_row_state();
   const uint32_t sh = shift_for(hi - lo);
   for_each_element(x, L, [&](uint32_t u, uint32_t) {
     const uint32_t k = key_of_bits(u);
@@ -343,7 +364,7 @@ __device__ void exact_full_row(Smem& s, const float* __restrict__ x, uint32_t L,
     atomicAdd(&s.hist[d < (uint32_t)(NB - 1) ? d : (uint32_t)(NB - 1)], 1u);
   });
   __syncthreads();
-  block_find_bin(s, K);
+  block_find_bin(K);
   const uint32_t b = s.sel_bin, above = s.sel_above;
   const uint32_t cb = s.hist[b];
   const uint32_t need = K - above;
@@ -372,13 +393,13 @@ __device__ void exact_full_row(Smem& s, const float* __restrict__ x, uint32_t L,
   uint32_t T, gt2;
   if (fits) {
     const uint32_t* keys = &s.buf[CAP];
-    select_rank(s, [&](auto&& f) {
+    select_rank([&](auto&& f) {
       for (uint32_t i = threadIdx.x; i < cb; i += BLOCK) f(keys[i]);
     }, need, blo, bhi, T, gt2);
-    commit_list(s, keys, s.buf, cb, T, above + gt2, K, out);
+    commit_list(keys, s.buf, cb, T, above + gt2, K, out);
   } else {
     if (threadIdx.x == 0) stat_add(ctl, TOPK_STAT_FRONTIER_WIDE);
-    select_rank(s, [&](auto&& f) {
+    select_rank([&](auto&& f) {
       for_each_element(x, L, [&](uint32_t u, uint32_t) { f(key_of_bits(u)); });
     }, need, blo, bhi, T, gt2);
     const uint32_t gt_total = above + gt2;
@@ -397,8 +418,8 @@ __device__ void exact_full_row(Smem& s, const float* __restrict__ x, uint32_t L,
 
 // ---------------------------------------------------------- direct (in LDS)
 
-__device__ void direct_exact(Smem& s, const float* __restrict__ x, uint32_t L, uint32_t K,
-                             int32_t* __restrict__ out) {
+__device__ void direct_exact(grow_t x, uint32_t L, uint32_t K, gout_t out) {
+  Smem& s = g_s;
   uint32_t mn = KEY_MAX, mx = 0;
   for_each_element(x, L, [&](uint32_t u, uint32_t e) {
     const uint32_t k = key_of_bits(u);
@@ -406,12 +427,12 @@ __device__ void direct_exact(Smem& s, const float* __restrict__ x, uint32_t L, u
     mn = min(mn, k);
     mx = max(mx, k);
   });
-  block_minmax(s, mn, mx);
+  block_minmax(mn, mx);
   uint32_t T, gt;
-  select_rank(s, [&](auto&& f) {
-    for (uint32_t i = threadIdx.x; i < L; i += BLOCK) f(s.buf[i]);
+  select_rank([&](auto&& f) {
+    for (uint32_t i = threadIdx.x; i < L; i += BLOCK) f(g_s.buf[i]);
   }, K, s.mn, s.mx, T, gt);
-  commit_list(s, s.buf, nullptr, L, T, gt, K, out);
+  commit_list(s.buf, nullptr, L, T, gt, K, out);
 }
 
 // ---------------------------------------------------------------- sampled path
@@ -431,7 +452,7 @@ __device__ __forceinline__ bool admits(uint32_t u, uint32_t thr) {
 }
 
 template <bool POS>
-__device__ __forceinline__ bool quad_admits(const uint4& v, uint32_t thr) {
+__device__ __forceinline__ bool quad_admits(const u32x4& v, uint32_t thr) {
   if (POS) {
     const int32_t m = max(max((int32_t)v.x, (int32_t)v.y), max((int32_t)v.z, (int32_t)v.w));
     return m >= (int32_t)thr;
@@ -442,7 +463,7 @@ __device__ __forceinline__ bool quad_admits(const uint4& v, uint32_t thr) {
 }
 
 template <bool POS>
-__device__ __forceinline__ bool batch_admits(const uint4 (&v)[UNROLL], uint32_t thr) {
+__device__ __forceinline__ bool batch_admits(const u32x4 (&v)[UNROLL], uint32_t thr) {
   if (POS) {
     int32_t m = (int32_t)v[0].x;
 #pragma unroll
@@ -461,9 +482,10 @@ __device__ __forceinline__ bool batch_admits(const uint4 (&v)[UNROLL], uint32_t 
 // per wave for the base slot, prefix count for each lane's slot, histogram update
 // and the tau0 count. Every active lane of the wave must reach it.
 template <bool POS>
-__device__ __forceinline__ void admit_one(Smem& s, uint32_t u, uint32_t e, const PassCtx& c,
+__device__ __forceinline__ void admit_one(bool valid, uint32_t u, uint32_t e, const PassCtx c,
                                           uint32_t& c0w) {
-  const bool pred = admits<POS>(u, c.thr);
+  Smem& s = g_s;
+  const bool pred = valid && admits<POS>(u, c.thr);
   const uint64_t m = __ballot(pred);
   if (m == 0) return;
   const int leader = __builtin_ctzll(m);
@@ -483,48 +505,48 @@ __device__ __forceinline__ void admit_one(Smem& s, uint32_t u, uint32_t e, const
 }
 
 template <bool POS>
-__device__ __forceinline__ void admit_quad(Smem& s, const uint4& v, uint32_t e, const PassCtx& c,
-                                           uint32_t& c0w) {
+__device__ __forceinline__ void admit_quad(const u32x4& v, uint32_t e, const PassCtx c, uint32_t& c0w) {
   if (__ballot(quad_admits<POS>(v, c.thr)) == 0) return;
-  admit_one<POS>(s, v.x, e, c, c0w);
-  admit_one<POS>(s, v.y, e + 1, c, c0w);
-  admit_one<POS>(s, v.z, e + 2, c, c0w);
-  admit_one<POS>(s, v.w, e + 3, c, c0w);
+  admit_one<POS>(true, v.x, e, c, c0w);
+  admit_one<POS>(true, v.y, e + 1, c, c0w);
+  admit_one<POS>(true, v.z, e + 2, c, c0w);
+  admit_one<POS>(true, v.w, e + 3, c, c0w);
 }
 
-// The mandatory full-row pass: certification counts, candidate compaction and the
-// first histogram, fused. The next batch of loads is issued before the current one
-// is examined so that each thread keeps 2 x UNROLL 128-bit loads in flight.
+// The mandatory full-row pass when the sampled lines are not skipped: certification
+// counts, candidate compaction and the first histogram, fused. The next batch of
+// loads is issued before the current one is examined so that each thread keeps
+// 2 x UNROLL 128-bit loads in flight.
 template <bool POS>
-__device__ void fused_pass(Smem& s, const float* __restrict__ x, uint32_t L, const PassCtx& c) {
+__device__ void fused_pass(grow_t x, uint32_t L, const PassCtx c) {
+  Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   uint32_t c0w = 0;
-  const uint32_t* xu = reinterpret_cast<const uint32_t*>(x);
-  uint32_t head = (uint32_t)((4u - ((uint32_t)(reinterpret_cast<uintptr_t>(x) >> 2) & 3u)) & 3u);
+  uint32_t head = (uint32_t)((4u - ((uint32_t)((uintptr_t)x >> 2) & 3u)) & 3u);
   if (head > L) head = L;
-  if (t < head) admit_one<POS>(s, xu[t], t, c, c0w);
+  if (t < head) admit_one<POS>(true, x[t], t, c, c0w);
   const uint32_t nv = (L - head) >> 2;
-  const uint4* __restrict__ p4 = reinterpret_cast<const uint4*>(xu + head);
+  grow_t body = x + head;
   const uint32_t per = BLOCK * UNROLL;
   const uint32_t nfull = nv / per;
-  auto examine = [&](const uint4 (&v)[UNROLL], uint32_t it) {
+  auto examine = [&](const u32x4 (&v)[UNROLL], uint32_t it) {
     if (__ballot(batch_admits<POS>(v, c.thr)) != 0) {
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u)
-        admit_quad<POS>(s, v[u], head + 4u * (it * per + u * BLOCK + t), c, c0w);
+        admit_quad<POS>(v[u], head + 4u * (it * per + u * BLOCK + t), c, c0w);
     }
   };
   if (nfull > 0) {
     // The prefetch is unconditional inside the loop (the last batch is peeled) so
     // the compiler waits only for the batch being examined, not for the next one.
-    uint4 a[UNROLL];
+    u32x4 a[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) a[u] = p4[u * BLOCK + t];
+    for (int u = 0; u < UNROLL; ++u) a[u] = load4(body + 4u * (u * BLOCK + t));
     uint32_t it = 0;
     for (; it + 1 < nfull; ++it) {
-      uint4 nx[UNROLL];
+      u32x4 nx[UNROLL];
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u) nx[u] = p4[(it + 1) * per + u * BLOCK + t];
+      for (int u = 0; u < UNROLL; ++u) nx[u] = load4(body + 4u * ((it + 1) * per + u * BLOCK + t));
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the examination
       examine(a, it);
 #pragma unroll
@@ -532,17 +554,226 @@ __device__ void fused_pass(Smem& s, const float* __restrict__ x, uint32_t L, con
     }
     examine(a, it);
   }
-  for (uint32_t q = nfull * per + t; q < nv; q += BLOCK) admit_quad<POS>(s, p4[q], head + 4u * q, c, c0w);
+  for (uint32_t q = nfull * per + t; q < nv; q += BLOCK) admit_quad<POS>(load4(body + 4u * q), head + 4u * q, c, c0w);
   const uint32_t tail0 = head + 4u * nv;
-  if (t < L - tail0) admit_one<POS>(s, xu[tail0 + t], tail0 + t, c, c0w);
+  if (t < L - tail0) admit_one<POS>(true, x[tail0 + t], tail0 + t, c, c0w);
+  if (lane_id() == 0 && c0w != 0) atomicAdd(&s.cnt0, c0w);
+}
+
+// ------------------------------------------------ line-granular sampling
+//
+// HBM moves whole 128-byte lines, so the 4-byte read of x[j*128] costs a full line
+// (a quarter of the row's bytes at stride 128). The sampler therefore reads each
+// sampled line whole: the element at j*128 is still the sample key (the proposal
+// is unchanged), and the line's maximum key is kept alongside it. The full-row pass
+// then reads only the other three lines of every 512-byte period, and a sampled
+// line is read again only if its maximum reaches tau1 (a "hot" line), since no
+// other sampled line can hold an admitted element. Every element is examined
+// exactly once, by the pass or by the hot-line step.
+//
+// Geometry: offsets are counted in floats from base = x rounded down to a 128-byte
+// line, so element index = offset - off4 with off4 = (x & 127) / 4. The line of
+// x[j*128] starts at offset 128 j (adding 512 j bytes keeps the low seven address
+// bits). Period p = offsets [128 p, 128 p + 128): its first line is sampled when
+// p < n_s and its other three lines are not. Past period n_s - 1 the row can reach
+// only into the first line of period n_s, which is not sampled.
+
+constexpr uint32_t LINE_SAMPLE_MAX = 8192;              // n_s limit of line sampling
+constexpr int LM_PER_THREAD = LINE_SAMPLE_MAX / BLOCK;  // lines per thread in the hot step
+constexpr int SAMPLE_UNROLL = 8;
+
+// Reads the n_s sampled lines whole. skey[j] = key(x[j*128]); lmax[j] = max key of
+// the line's elements inside the row. Tracks the min/max sample key in s.mn/s.mx.
+__device__ void sample_lines(grow_t x, uint32_t L, uint32_t n_s, uint32_t* skey, uint32_t* lmax) {
+  const uint32_t t = threadIdx.x;
+  const uint32_t off4 = (uint32_t)((uintptr_t)x & 127u) >> 2;
+  grow_t base = x - off4;
+  const uint32_t c = t & 7;          // this lane's 16-byte chunk of the line
+  const uint32_t cs = off4 >> 2;     // chunk holding x[j*128]
+  const uint32_t is = off4 & 3u;     // component holding x[j*128]
+  const uint32_t lo = off4, hi = off4 + L;  // valid offsets [lo, hi)
+  const uint32_t gfirst = off4 & ~3u;        // chunk holding the row's first element
+  const uint32_t glast = (hi - 1u) & ~3u;    // chunk holding the row's last element
+  constexpr uint32_t LINES_PER_STEP = BLOCK / 8;
+  uint32_t mn = KEY_MAX, mx = 0;
+  for (uint32_t jb = 0; jb < n_s; jb += LINES_PER_STEP * SAMPLE_UNROLL) {
+    u32x4 v[SAMPLE_UNROLL];
+#pragma unroll
+    for (int u = 0; u < SAMPLE_UNROLL; ++u) {
+      const uint32_t j = jb + u * LINES_PER_STEP + (t >> 3);
+      const uint32_t g = 128u * j + 4u * c;
+      // Chunks outside the row read the row's first or last chunk instead (always in
+      // bounds, unconditional); their elements are masked out below.
+      v[u] = load4(base + (g < gfirst ? gfirst : (g < glast ? g : glast)));
+    }
+#pragma unroll
+    for (int u = 0; u < SAMPLE_UNROLL; ++u) {
+      const uint32_t j = jb + u * LINES_PER_STEP + (t >> 3);
+      const uint32_t g = 128u * j + 4u * c;
+      uint32_t m = 0;
+      if (j < n_s && g + 0 >= lo && g + 0 < hi) m = max(m, key_of_bits(v[u].x));
+      if (j < n_s && g + 1 >= lo && g + 1 < hi) m = max(m, key_of_bits(v[u].y));
+      if (j < n_s && g + 2 >= lo && g + 2 < hi) m = max(m, key_of_bits(v[u].z));
+      if (j < n_s && g + 3 >= lo && g + 3 < hi) m = max(m, key_of_bits(v[u].w));
+      m = max(m, (uint32_t)__shfl_xor(m, 1));
+      m = max(m, (uint32_t)__shfl_xor(m, 2));
+      m = max(m, (uint32_t)__shfl_xor(m, 4));
+      if (j < n_s) {
+        if (c == 0) lmax[j] = m;
+        if (c == cs) {
+          const uint32_t w = is == 0 ? v[u].x : is == 1 ? v[u].y : is == 2 ? v[u].z : v[u].w;
+          const uint32_t k = key_of_bits(w);
+          skey[j] = k;
+          mn = min(mn, k);
+          mx = max(mx, k);
+        }
+      }
+    }
+  }
+  block_minmax(mn, mx);
+}
+
+// Re-reads the sampled lines whose maximum reaches tau1 and admits their elements.
+// Bit m of hot_mask is set when line t + m*BLOCK is hot (the LDS maxima are gone).
+template <bool POS>
+__device__ void hot_lines(grow_t x, uint32_t L, uint32_t hot_mask, const PassCtx c) {
+  Smem& s = g_s;
+  const uint32_t t = threadIdx.x;
+  uint32_t c0w = 0;
+  const uint32_t off4 = (uint32_t)((uintptr_t)x & 127u) >> 2;
+  grow_t base = x - off4;
+  const uint32_t lo = off4, hi = off4 + L;
+  const uint32_t gfirst = off4 & ~3u, glast = (hi - 1u) & ~3u;
+#pragma unroll 1
+  for (int m = 0; m < LM_PER_THREAD; ++m) {
+    const uint32_t j = t + (uint32_t)m * BLOCK;
+    const bool hot = (hot_mask >> m) & 1u;
+    if (__ballot(hot) == 0) continue;
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+      u32x4 v[4] = {splat4(0u), splat4(0u), splat4(0u), splat4(0u)};
+      if (hot) {
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const uint32_t g = 128u * j + 16u * half + 4u * cc;
+          v[cc] = load4(base + (g < gfirst ? gfirst : (g < glast ? g : glast)));
+        }
+      }
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const uint32_t g = 128u * j + 16u * half + 4u * cc;
+        admit_one<POS>(hot && g + 0 >= lo && g + 0 < hi, v[cc].x, g + 0 - off4, c, c0w);
+        admit_one<POS>(hot && g + 1 >= lo && g + 1 < hi, v[cc].y, g + 1 - off4, c, c0w);
+        admit_one<POS>(hot && g + 2 >= lo && g + 2 < hi, v[cc].z, g + 2 - off4, c, c0w);
+        admit_one<POS>(hot && g + 3 >= lo && g + 3 < hi, v[cc].w, g + 3 - off4, c, c0w);
+      }
+    }
+  }
+  if (lane_id() == 0 && c0w != 0) atomicAdd(&s.cnt0, c0w);
+}
+
+// A value that never passes admits<POS> (tau1 key != 0 is required for NEG).
+template <bool POS>
+constexpr uint32_t never_admitted() { return POS ? 0x80000000u : 0xFFFFFFFFu; }
+
+// Offset of chunk k of the non-sampled lines: period k / 24, line 1 + (k % 24) / 8,
+// chunk k % 8.
+__device__ __forceinline__ uint32_t unsampled_offset(uint32_t k) {
+  const uint32_t p = k / 24u;
+  const uint32_t r = k - 24u * p;
+  return 128u * p + 32u * (1u + (r >> 3)) + 4u * (r & 7u);
+}
+
+// Loads the chunk at offset g, or the row's last chunk when g lies past the row, so
+// the load is unconditional and always in bounds (the loads of a batch then stay
+// back to back). Elements at or past the row end are masked when examined.
+__device__ __forceinline__ u32x4 load_chunk(grow_t base, uint32_t g, uint32_t glast) {
+  return load4(base + (g < glast ? g : glast));
+}
+
+// Replaces every element of the chunk at offset g that lies at or past the row end
+// hi with a value that is never admitted.
+template <bool POS>
+__device__ __forceinline__ u32x4 mask_tail(u32x4 v, uint32_t g, uint32_t hi) {
+  constexpr uint32_t NA = never_admitted<POS>();
+  v.x = (g + 0 >= hi) ? NA : v.x;
+  v.y = (g + 1 >= hi) ? NA : v.y;
+  v.z = (g + 2 >= hi) ? NA : v.z;
+  v.w = (g + 3 >= hi) ? NA : v.w;
+  return v;
+}
+
+// The full-row pass over the non-sampled lines (see the geometry note above).
+template <bool POS>
+__device__ void fused_pass_lines(grow_t x, uint32_t L, uint32_t n_s, const PassCtx c) {
+  Smem& s = g_s;
+  const uint32_t t = threadIdx.x;
+  uint32_t c0w = 0;
+  const uint32_t off4 = (uint32_t)((uintptr_t)x & 127u) >> 2;
+  grow_t base = x - off4;
+  const uint32_t hi = off4 + L;
+  const uint32_t glast = (hi - 1u) & ~3u;  // chunk holding the row's last element
+  const uint32_t nk = 24u * n_s;
+  const uint32_t per = BLOCK * UNROLL;
+  const uint32_t nfull = nk / per;
+  auto examine = [&](const u32x4 (&raw)[UNROLL], uint32_t it) {
+    u32x4 v[UNROLL];
+    uint32_t g[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      g[u] = unsampled_offset(it * per + u * BLOCK + t);
+      v[u] = mask_tail<POS>(raw[u], g[u], hi);
+    }
+    if (__ballot(batch_admits<POS>(v, c.thr)) != 0) {
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) admit_quad<POS>(v[u], g[u] - off4, c, c0w);
+    }
+  };
+  auto fetch = [&](u32x4 (&v)[UNROLL], uint32_t it) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) v[u] = load_chunk(base, unsampled_offset(it * per + u * BLOCK + t), glast);
+  };
+  if (nfull > 0) {
+    // Two batch buffers in ping-pong: while one batch is examined the next one is in
+    // flight, with no register copies between iterations (a copy would force the
+    // compiler to wait for the prefetch).
+    u32x4 a[UNROLL], b[UNROLL];
+    fetch(a, 0);
+    uint32_t it = 0;
+    for (; it + 2 < nfull; it += 2) {
+      fetch(b, it + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      examine(a, it);
+      fetch(a, it + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      examine(b, it + 1);
+    }
+    if (it + 1 < nfull) {
+      fetch(b, it + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      examine(a, it);
+      examine(b, it + 1);
+    } else {
+      examine(a, it);
+    }
+  }
+  for (uint32_t k = nfull * per + t; k < nk; k += BLOCK) {
+    const uint32_t g = unsampled_offset(k);
+    admit_quad<POS>(mask_tail<POS>(load_chunk(base, g, glast), g, hi), g - off4, c, c0w);
+  }
+  // The first line of period n_s, if the row reaches into it (never sampled).
+  if (t < 8) {
+    const uint32_t g = 128u * n_s + 4u * t;
+    if (g < hi) admit_quad<POS>(mask_tail<POS>(load_chunk(base, g, glast), g, hi), g - off4, c, c0w);
+  }
   if (lane_id() == 0 && c0w != 0) atomicAdd(&s.cnt0, c0w);
 }
 
 // Boundary refinement and commit after a certified pass: n = C(tau1) <= CAP
 // candidates are in LDS with the first histogram over (key - key(tau1)) >> sh.
-__device__ void refine_commit(Smem& s, uint32_t n, uint32_t K, const PassCtx& c,
-                              int32_t* __restrict__ out, Control* ctl) {
-  block_find_bin(s, K);
+__device__ void refine_commit(uint32_t n, uint32_t K, const PassCtx c, gout_t out, Control* ctl) {
+  Smem& s = g_s;
+  block_find_bin(K);
   const uint32_t b = s.sel_bin, above = s.sel_above;
   const uint32_t cb = s.hist[b];
   const uint32_t need = K - above;
@@ -570,14 +801,14 @@ __device__ void refine_commit(Smem& s, uint32_t n, uint32_t K, const PassCtx& c,
   __syncthreads();
   uint32_t T, gt2;
   if (fits) {
-    select_rank(s, [&](auto&& f) {
-      for (uint32_t i = threadIdx.x; i < cb; i += BLOCK) f(s.fl_key[i]);
+    select_rank([&](auto&& f) {
+      for (uint32_t i = threadIdx.x; i < cb; i += BLOCK) f(g_s.fl_key[i]);
     }, need, blo, bhi, T, gt2);
-    commit_list(s, s.fl_key, s.fl_idx, cb, T, above + gt2, K, out);
+    commit_list(s.fl_key, s.fl_idx, cb, T, above + gt2, K, out);
   } else {
     if (threadIdx.x == 0) stat_add(ctl, TOPK_STAT_FRONTIER_WIDE);
     const uint32_t* keys = &s.buf[CAP];
-    select_rank(s, [&](auto&& f) {
+    select_rank([&](auto&& f) {
       for (uint32_t i = threadIdx.x; i < n; i += BLOCK) f(keys[i]);
     }, need, blo, bhi, T, gt2);
     const uint32_t gt_total = above + gt2;
@@ -602,36 +833,40 @@ __device__ __forceinline__ uint32_t sample_rank(uint32_t target, uint32_t n_s, u
   return (uint32_t)r;
 }
 
-__device__ void sampled_row(Smem& s, const Params& p, const float* __restrict__ x, uint32_t L,
-                            int32_t* __restrict__ out) {
+__device__ void sampled_row(const Params& p, grow_t x, uint32_t L, gout_t out) {
+  Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   const uint32_t n_s = (L + STRIDE - 1) / STRIDE;
   if (n_s > (uint32_t)KEYS_CAP) {
     if (t == 0) stat_add(p.ctl, TOPK_STAT_LONG_EXACT);
-    exact_full_row(s, x, L, p.K, 0u, KEY_MAX, out, p.ctl);
+    exact_full_row(x, L, p.K, 0u, KEY_MAX, out, p.ctl);
     return;
   }
   if (t == 0) stat_add(p.ctl, TOPK_STAT_SAMPLED);
-  // Fixed-stride row-local view: x[j * 128], j < ceil(L / 128).
-  const uint32_t* xu = reinterpret_cast<const uint32_t*>(x);
-  uint32_t mn = KEY_MAX, mx = 0;
+  // Fixed-stride row-local view: keys of x[j * 128], j < ceil(L / 128), in s.buf[0, n_s).
+  const bool by_lines = n_s <= LINE_SAMPLE_MAX;
+  if (by_lines) {
+    sample_lines(x, L, n_s, &s.buf[0], &s.buf[CAP]);
+  } else {
+    uint32_t mn = KEY_MAX, mx = 0;
 #pragma unroll 8
-  for (uint32_t j = t; j < n_s; j += BLOCK) {
-    const uint32_t k = key_of_bits(xu[(size_t)j * STRIDE]);
-    s.buf[j] = k;
-    mn = min(mn, k);
-    mx = max(mx, k);
+    for (uint32_t j = t; j < n_s; j += BLOCK) {
+      const uint32_t k = key_of_bits(x[(size_t)j * STRIDE]);
+      s.buf[j] = k;
+      mn = min(mn, k);
+      mx = max(mx, k);
+    }
+    block_minmax(mn, mx);
   }
-  block_minmax(s, mn, mx);
   const uint32_t smin = s.mn, smax = s.mx;
   const uint32_t r1 = sample_rank(p.T1, n_s, L);
   const uint32_t r0 = sample_rank(p.T0, n_s, L);
   uint32_t t1key, t0key, unused;
-  select_rank(s, [&](auto&& f) {
-    for (uint32_t i = t; i < n_s; i += BLOCK) f(s.buf[i]);
+  select_rank([&](auto&& f) {
+    for (uint32_t i = t; i < n_s; i += BLOCK) f(g_s.buf[i]);
   }, r1, smin, smax, t1key, unused);
-  select_rank(s, [&](auto&& f) {
-    for (uint32_t i = t; i < n_s; i += BLOCK) f(s.buf[i]);
+  select_rank([&](auto&& f) {
+    for (uint32_t i = t; i < n_s; i += BLOCK) f(g_s.buf[i]);
   }, r0, t1key, smax, t0key, unused);
 
   PassCtx c;
@@ -640,62 +875,86 @@ __device__ void sampled_row(Smem& s, const Params& p, const float* __restrict__ 
   c.sh = shift_for(smax - t1key);
   const bool pos = t1key >= 0x80000000u;
   c.thr = pos ? (t1key ^ 0x80000000u) : ~t1key;
-  reset_row_state(s);
-  if (pos) fused_pass<true>(s, x, L, c);
-  else fused_pass<false>(s, x, L, c);
+  // Skipping sampled lines needs a value that is never admitted, which exists
+  // unless tau1 is the lowest possible key.
+  const bool skip = by_lines && t1key != 0u;
+  uint32_t hot_mask = 0;
+  if (skip) {
+#pragma unroll
+    for (int m = 0; m < LM_PER_THREAD; ++m) {
+      const uint32_t j = t + (uint32_t)m * BLOCK;
+      if (j < n_s && s.buf[CAP + j] >= t1key) hot_mask |= 1u << m;
+    }
+  }
+  reset_row_state();  // its barrier also ends every read of the line maxima in LDS
+  if (skip) {
+    if (pos) {
+      hot_lines<true>(x, L, hot_mask, c);
+      fused_pass_lines<true>(x, L, n_s, c);
+    } else {
+      hot_lines<false>(x, L, hot_mask, c);
+      fused_pass_lines<false>(x, L, n_s, c);
+    }
+  } else if (pos) {
+    fused_pass<true>(x, L, c);
+  } else {
+    fused_pass<false>(x, L, c);
+  }
   __syncthreads();
   const uint32_t c1 = s.cnt, c0 = s.cnt0;
   if (c1 > (uint32_t)CAP) {
     // Too many admitted to hold: the K-th key is >= tau1, recover exactly.
     if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_OVER);
-    exact_full_row(s, x, L, p.K, t1key, smax, out, p.ctl);
+    exact_full_row(x, L, p.K, t1key, smax, out, p.ctl);
   } else if (c1 < p.K) {
     // Even the nested threshold underfills: the K-th key is < tau1.
     if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_UNDER);
-    exact_full_row(s, x, L, p.K, smin, t1key, out, p.ctl);
+    exact_full_row(x, L, p.K, smin, t1key, out, p.ctl);
   } else {
     if (t == 0) stat_add(p.ctl, c0 >= p.K ? TOPK_STAT_TAU0 : TOPK_STAT_TAU1);
-    refine_commit(s, c1, p.K, c, out, p.ctl);
+    refine_commit(c1, p.K, c, out, p.ctl);
   }
 }
 
-__device__ void process_row(Smem& s, const Params& p, uint32_t row) {
+// One row, start to commit. Kept out of line so that registers are allocated per
+// row phase rather than across the persistent row loop.
+__device__ __attribute__((noinline)) void process_row(Params p, uint32_t row) {
   const uint32_t t = threadIdx.x;
-  int32_t len = p.row_len[row];
+  const int32_t len = p.row_len[row];
   uint32_t L = len < 0 ? 0u : (uint32_t)len;
   if (L > p.N) L = p.N;
-  const float* __restrict__ x = p.scores + (size_t)row * p.N;
-  int32_t* __restrict__ out = p.out + (size_t)row * p.K;
+  grow_t x = (grow_t)(p.scores) + (size_t)row * p.N;
+  gout_t out = (gout_t)(p.out) + (size_t)row * p.K;
   if (t == 0) stat_add(p.ctl, TOPK_STAT_ROWS);
   if (L <= p.K) {
     for (uint32_t j = t; j < p.K; j += BLOCK) out[j] = j < L ? (int32_t)j : p.sentinel;
     if (t == 0) stat_add(p.ctl, TOPK_STAT_SENTINEL);
     return;
   }
-  reset_row_state(s);
+  reset_row_state();
   const bool direct = (p.mode == TOPK_PATH_DIRECT) || (p.mode == TOPK_PATH_AUTO && L <= p.direct_max);
   if (direct) {
     if (t == 0) stat_add(p.ctl, TOPK_STAT_DIRECT);
-    if (L <= (uint32_t)KEYS_CAP) direct_exact(s, x, L, p.K, out);
-    else exact_full_row(s, x, L, p.K, 0u, KEY_MAX, out, p.ctl);
+    if (L <= (uint32_t)KEYS_CAP) direct_exact(x, L, p.K, out);
+    else exact_full_row(x, L, p.K, 0u, KEY_MAX, out, p.ctl);
   } else if (p.mode == TOPK_PATH_RECOVERY) {
     if (t == 0) stat_add(p.ctl, TOPK_STAT_FORCED_RECOVERY);
-    exact_full_row(s, x, L, p.K, 0u, KEY_MAX, out, p.ctl);
+    exact_full_row(x, L, p.K, 0u, KEY_MAX, out, p.ctl);
   } else {
-    sampled_row(s, p, x, L, out);
+    sampled_row(p, x, L, out);
   }
 }
 
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
 void topk_rows_kernel(Params p) {
-  __shared__ Smem s;
+  Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   for (;;) {
     if (t == 0) s.row = (int32_t)atomicAdd(&p.ctl->row_ticket, 1u);
     __syncthreads();
     const uint32_t row = (uint32_t)s.row;
     if (row >= p.M) break;
-    process_row(s, p, row);
+    process_row(p, row);
     __syncthreads();
   }
   // The last workgroup to leave rewinds the row ticket for the next call. Every
