@@ -76,16 +76,36 @@ constexpr int FL_CAP = 512;           // frontier (index, key) pairs
 constexpr uint32_t STRIDE = 128;      // sample stride s
 constexpr int UNROLL = 4;             // 128-bit loads per thread per batch
 constexpr uint32_t DIRECT_MAX_DEFAULT = 16384;
+constexpr uint32_t QMAX = 256;        // rows queued for cooperative recovery per call
+constexpr uint32_t REC_SEG = 16384;   // elements per recovery work item
 constexpr uint32_t KEY_MAX = 0xFFFFFFFFu;
 
 static_assert(NB % BLOCK == 0, "bins per thread must be integral");
 static_assert(TOPK_K_MAX * 7 / 4 + 1 <= CAP, "candidate buffer must hold the tau1 target");
 
 struct Control {
-  uint32_t row_ticket;
-  uint32_t done_ticket;
-  uint32_t pad[30];
+  uint32_t row_ticket;   // next row of the persistent row loop
+  uint32_t done_ticket;  // workgroups that left the row loop
+  uint32_t qcount;       // rows queued for cooperative recovery in this call
+  uint32_t rec_done;     // workgroups that finished the recovery collect kernel
+  uint32_t pad[28];
   unsigned long long stats[TOPK_STAT_COUNT];
+};
+
+// One row queued for cooperative exact recovery. Written by the workgroup that
+// queues the row; the histogram, counters and candidates are filled by the
+// recovery kernels.
+struct RecSlot {
+  uint32_t row;
+  uint32_t L;
+  uint32_t lo, hi;       // key range binned by the first histogram
+  uint32_t out_gt;       // output slots taken by keys above the boundary bin
+  uint32_t cnt;          // candidates collected from the boundary bin
+  uint32_t done;         // work items of this row finished by the collect kernel
+  uint32_t pad[25];
+  uint32_t hist[NB];
+  uint32_t cand_idx[CAP];
+  uint32_t cand_key[CAP];
 };
 
 struct Params {
@@ -101,6 +121,7 @@ struct Params {
   uint32_t T1;          // secondary candidate target, ceil(1.75 K)
   uint32_t direct_max;  // auto mode: rows up to this length take the direct path
   int32_t mode;
+  RecSlot* rec;         // QMAX recovery slots
 };
 
 struct Smem {
@@ -116,6 +137,7 @@ struct Smem {
   uint32_t out_tie;            // output slots taken by keys equal to the threshold
   uint32_t mn, mx;
   uint32_t sel_bin, sel_above;
+  uint32_t bcast;              // block-wide broadcast of a value read by thread 0
   int32_t row;
 };
 
@@ -826,6 +848,36 @@ __device__ void refine_commit(uint32_t n, uint32_t K, const PassCtx c, gout_t ou
   }
 }
 
+// Hands a row that needs exact full-row recovery to the cooperative recovery
+// kernels (which run after this kernel and spread the row over the whole GPU), or
+// recovers it here when the queue is full. Nothing has been written to the row's
+// output yet. [lo, hi] is the key range the recovery histogram bins.
+__device__ void recover_row(const Params& p, uint32_t row, grow_t x, uint32_t L, uint32_t lo, uint32_t hi,
+                            gout_t out) {
+  Smem& s = g_s;
+  const uint32_t t = threadIdx.x;
+  if (t == 0) s.bcast = atomicAdd(&p.ctl->qcount, 1u);
+  __syncthreads();
+  const uint32_t q = s.bcast;
+  __syncthreads();
+  if (q < QMAX) {
+    RecSlot* r = p.rec + q;
+    if (t == 0) {
+      r->row = row;
+      r->L = L;
+      r->lo = lo;
+      r->hi = hi;
+      r->out_gt = 0;
+      r->cnt = 0;
+      r->done = 0;
+      stat_add(p.ctl, TOPK_STAT_QUEUED);
+    }
+    for (uint32_t i = t; i < (uint32_t)NB; i += BLOCK) r->hist[i] = 0;
+  } else {
+    exact_full_row(x, L, p.K, lo, hi, out, p.ctl);
+  }
+}
+
 __device__ __forceinline__ uint32_t sample_rank(uint32_t target, uint32_t n_s, uint32_t L) {
   uint64_t r = ((uint64_t)target * n_s + L - 1) / L;
   if (r < 1) r = 1;
@@ -833,7 +885,7 @@ __device__ __forceinline__ uint32_t sample_rank(uint32_t target, uint32_t n_s, u
   return (uint32_t)r;
 }
 
-__device__ void sampled_row(const Params& p, grow_t x, uint32_t L, gout_t out) {
+__device__ void sampled_row(const Params& p, uint32_t row, grow_t x, uint32_t L, gout_t out) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   const uint32_t n_s = (L + STRIDE - 1) / STRIDE;
@@ -905,11 +957,11 @@ __device__ void sampled_row(const Params& p, grow_t x, uint32_t L, gout_t out) {
   if (c1 > (uint32_t)CAP) {
     // Too many admitted to hold: the K-th key is >= tau1, recover exactly.
     if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_OVER);
-    exact_full_row(x, L, p.K, t1key, smax, out, p.ctl);
+    recover_row(p, row, x, L, t1key, smax, out);
   } else if (c1 < p.K) {
     // Even the nested threshold underfills: the K-th key is < tau1.
     if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_UNDER);
-    exact_full_row(x, L, p.K, smin, t1key, out, p.ctl);
+    recover_row(p, row, x, L, smin, t1key, out);
   } else {
     if (t == 0) stat_add(p.ctl, c0 >= p.K ? TOPK_STAT_TAU0 : TOPK_STAT_TAU1);
     refine_commit(c1, p.K, c, out, p.ctl);
@@ -939,9 +991,9 @@ __device__ __attribute__((noinline)) void process_row(Params p, uint32_t row) {
     else exact_full_row(x, L, p.K, 0u, KEY_MAX, out, p.ctl);
   } else if (p.mode == TOPK_PATH_RECOVERY) {
     if (t == 0) stat_add(p.ctl, TOPK_STAT_FORCED_RECOVERY);
-    exact_full_row(x, L, p.K, 0u, KEY_MAX, out, p.ctl);
+    recover_row(p, row, x, L, 0u, KEY_MAX, out);
   } else {
-    sampled_row(p, x, L, out);
+    sampled_row(p, row, x, L, out);
   }
 }
 
@@ -966,6 +1018,168 @@ void topk_rows_kernel(Params p) {
     if (d == gridDim.x - 1) {
       atomicExch(&p.ctl->row_ticket, 0u);
       atomicExch(&p.ctl->done_ticket, 0u);
+    }
+  }
+}
+
+// ------------------------------------------------------ cooperative recovery
+//
+// Exact full-row recovery of the queued rows, spread over the whole GPU. Each row
+// is cut into REC_SEG-element work items. The histogram kernel bins every item
+// into the row's global histogram over [lo, hi] (clamped at both ends). The
+// collect kernel then derives, in every work item, the bin holding rank K,
+// commits the item's keys above that bin and appends the bin's keys to the row's
+// candidate buffer; the last work item of a row (ticket) selects the remaining
+// keys exactly from that buffer and commits them. Both kernels exit at once when
+// the queue is empty; the collect kernel's last workgroup rewinds the queue.
+
+struct RecHistSmem {
+  uint32_t hist[NB];
+};
+__shared__ RecHistSmem g_rh;  // the histogram kernel's LDS state
+
+__device__ __forceinline__ uint32_t rec_items(uint32_t L) { return (L + REC_SEG - 1) / REC_SEG; }
+
+__global__ __launch_bounds__(BLOCK) void recovery_hist_kernel(Params p) {
+  const uint32_t t = threadIdx.x;
+  const uint32_t nq = min(p.ctl->qcount, QMAX);
+  const uint32_t per_row = (p.N + REC_SEG - 1) / REC_SEG;
+  const uint32_t items = nq * per_row;
+  for (uint32_t item = blockIdx.x; item < items; item += gridDim.x) {
+    const uint32_t q = item / per_row;
+    const uint32_t begin = (item - q * per_row) * REC_SEG;
+    RecSlot* r = p.rec + q;
+    const uint32_t L = r->L;
+    if (begin >= L) continue;
+    const uint32_t n = min(REC_SEG, L - begin);
+    const uint32_t lo = r->lo, hi = r->hi;
+    const uint32_t sh = shift_for(hi - lo);
+    for (uint32_t i = t; i < (uint32_t)NB; i += BLOCK) g_rh.hist[i] = 0;
+    __syncthreads();
+    grow_t x = (grow_t)(p.scores) + (size_t)r->row * p.N + begin;
+    for_each_element(x, n, [&](uint32_t u, uint32_t) {
+      const uint32_t k = key_of_bits(u);
+      const uint32_t d = k < lo ? 0u : (k - lo) >> sh;
+      atomicAdd(&g_rh.hist[d < (uint32_t)(NB - 1) ? d : (uint32_t)(NB - 1)], 1u);
+    });
+    __syncthreads();
+    for (uint32_t i = t; i < (uint32_t)NB; i += BLOCK) {
+      const uint32_t c = g_rh.hist[i];
+      if (c != 0) atomicAdd(&r->hist[i], c);
+    }
+    __syncthreads();
+  }
+}
+
+// The last work item of a queued row: resolve the boundary bin exactly and commit.
+__device__ void finish_recovery(const Params& p, RecSlot* r, uint32_t above, uint32_t cb, uint32_t blo,
+                                uint32_t bhi, bool fits) {
+  Smem& s = g_s;
+  const uint32_t t = threadIdx.x;
+  const uint32_t K = p.K;
+  const uint32_t need = K - above;
+  const uint32_t L = r->L;
+  grow_t x = (grow_t)(p.scores) + (size_t)r->row * p.N;
+  gout_t out = (gout_t)(p.out) + (size_t)r->row * K;
+  if (t == 0) {
+    s.out_gt = above;
+    s.out_tie = 0;
+  }
+  uint32_t T, gt2;
+  if (fits) {
+    for (uint32_t i = t; i < cb; i += BLOCK) {
+      s.buf[i] = r->cand_idx[i];
+      s.buf[CAP + i] = r->cand_key[i];
+    }
+    __syncthreads();
+    select_rank([&](auto&& f) {
+      for (uint32_t i = threadIdx.x; i < cb; i += BLOCK) f(g_s.buf[CAP + i]);
+    }, need, blo, bhi, T, gt2);
+    commit_list(&s.buf[CAP], s.buf, cb, T, above + gt2, K, out);
+  } else {
+    if (t == 0) stat_add(p.ctl, TOPK_STAT_FRONTIER_WIDE);
+    __syncthreads();
+    select_rank([&](auto&& f) {
+      for_each_element(x, L, [&](uint32_t u, uint32_t) { f(key_of_bits(u)); });
+    }, need, blo, bhi, T, gt2);
+    const uint32_t gt_total = above + gt2;
+    const uint32_t ties = K - gt_total;
+    for_each_element(x, L, [&](uint32_t u, uint32_t e) {
+      const uint32_t k = key_of_bits(u);
+      const bool g = k > T && k <= bhi;
+      const uint32_t pp = wave_reserve(g, &s.out_gt);
+      if (g && pp < K) out[pp] = (int32_t)e;
+      const bool q_ = k == T;
+      const uint32_t q = wave_reserve(q_, &s.out_tie);
+      if (q_ && q < ties && gt_total + q < K) out[gt_total + q] = (int32_t)e;
+    });
+  }
+}
+
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
+void recovery_collect_kernel(Params p) {
+  Smem& s = g_s;
+  const uint32_t t = threadIdx.x;
+  const uint32_t K = p.K;
+  const uint32_t nq = min(p.ctl->qcount, QMAX);
+  const uint32_t per_row = (p.N + REC_SEG - 1) / REC_SEG;
+  const uint32_t items = nq * per_row;
+  for (uint32_t item = blockIdx.x; item < items; item += gridDim.x) {
+    const uint32_t q = item / per_row;
+    const uint32_t begin = (item - q * per_row) * REC_SEG;
+    RecSlot* r = p.rec + q;
+    const uint32_t L = r->L;
+    if (begin >= L) continue;
+    const uint32_t n = min(REC_SEG, L - begin);
+    // The boundary bin, from the completed histogram (every item derives the same).
+    for (uint32_t i = t; i < (uint32_t)NB; i += BLOCK) s.hist[i] = r->hist[i];
+    __syncthreads();
+    block_find_bin(K);
+    const uint32_t b = s.sel_bin, above = s.sel_above;
+    const uint32_t cb = s.hist[b];
+    const uint32_t lo = r->lo, hi = r->hi;
+    const uint32_t sh = shift_for(hi - lo);
+    const uint32_t braw = lo + (b << sh);
+    const uint32_t blo = (b == 0) ? 0u : braw;
+    const uint32_t wdt = (1u << sh) - 1u;
+    const uint32_t bhi = (b == (uint32_t)(NB - 1)) ? KEY_MAX
+                                                   : braw + ((KEY_MAX - braw) < wdt ? (KEY_MAX - braw) : wdt);
+    const bool fits = cb <= (uint32_t)CAP;
+    __syncthreads();
+    grow_t x = (grow_t)(p.scores) + (size_t)r->row * p.N + begin;
+    gout_t out = (gout_t)(p.out) + (size_t)r->row * K;
+    for_each_element(x, n, [&](uint32_t u, uint32_t e) {
+      const uint32_t k = key_of_bits(u);
+      const bool g = k > bhi;
+      const uint32_t pp = wave_reserve(g, &r->out_gt);
+      if (g && pp < K) out[pp] = (int32_t)(begin + e);
+      if (fits) {
+        const bool in = k >= blo && k <= bhi;
+        const uint32_t f = wave_reserve(in, &r->cnt);
+        if (in && f < (uint32_t)CAP) {
+          r->cand_idx[f] = begin + e;
+          r->cand_key[f] = k;
+        }
+      }
+    });
+    __threadfence();  // release this item's candidates and outputs before its ticket
+    __syncthreads();
+    if (t == 0) s.bcast = (atomicAdd(&r->done, 1u) == rec_items(L) - 1) ? 1u : 0u;
+    __syncthreads();
+    if (s.bcast) {
+      __threadfence();  // acquire every other item's candidates
+      finish_recovery(p, r, above, cb, blo, bhi, fits);
+    }
+    __syncthreads();
+  }
+  // The last workgroup to leave rewinds the queue for the next call; every
+  // workgroup has read qcount before it increments rec_done.
+  if (t == 0) {
+    __threadfence();
+    const uint32_t d = atomicAdd(&p.ctl->rec_done, 1u);
+    if (d == gridDim.x - 1) {
+      atomicExch(&p.ctl->qcount, 0u);
+      atomicExch(&p.ctl->rec_done, 0u);
     }
   }
 }
@@ -1010,8 +1224,10 @@ __global__ __launch_bounds__(BLOCK) void stream_read_probe_kernel(const float* _
 struct DevState {
   bool ready = false;
   int n_cu = 0;
-  int occ = 0;
+  int occ = 0;          // resident selector workgroups per CU
+  int occ_rec = 0;      // resident recovery-collect workgroups per CU
   Control* ctl = nullptr;
+  RecSlot* rec = nullptr;
 };
 
 constexpr int MAX_DEVICES = 64;
@@ -1052,18 +1268,28 @@ int get_state(bool capturing, DevState** out) {
                                                      BLOCK, 0);
     if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     if (occ < 1) return fail(TOPK_ERR_HIP, "selector kernel cannot be resident (occupancy %d)", occ);
-    Control* ctl = nullptr;
-    e = hipMalloc(reinterpret_cast<void**>(&ctl), sizeof(Control));
+    int occ_rec = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &occ_rec, reinterpret_cast<const void*>(recovery_collect_kernel), BLOCK, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    if (occ_rec < 1) return fail(TOPK_ERR_HIP, "recovery kernel cannot be resident");
+    // One allocation: the control block, then the recovery slots.
+    const size_t rec_off = (sizeof(Control) + 255) / 256 * 256;
+    const size_t bytes = rec_off + sizeof(RecSlot) * QMAX;
+    char* ws = nullptr;
+    e = hipMalloc(reinterpret_cast<void**>(&ws), bytes);
     if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
-    e = hipMemset(ctl, 0, sizeof(Control));
+    e = hipMemset(ws, 0, bytes);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
-      (void)hipFree(ctl);
+      (void)hipFree(ws);
       return hip_fail(e, "workspace initialisation");
     }
     st.n_cu = n_cu;
     st.occ = occ;
-    st.ctl = ctl;
+    st.occ_rec = occ_rec;
+    st.ctl = reinterpret_cast<Control*>(ws);
+    st.rec = reinterpret_cast<RecSlot*>(ws + rec_off);
     st.ready = true;
   }
   *out = &st;
@@ -1120,11 +1346,19 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
   p.T1 = (uint32_t)((7 * K + 3) / 4);
   p.direct_max = DIRECT_MAX_DEFAULT;
   p.mode = g_mode.load();
+  p.rec = st->rec;
   const int64_t resident = (int64_t)st->occ * st->n_cu;
   const unsigned grid = (unsigned)(M < resident ? M : resident);
   hipLaunchKernelGGL(topk_rows_kernel, dim3(grid), dim3(BLOCK), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch topk_rows_kernel");
+  // Exact recovery of the rows the selector queued (both exit at once if none).
+  hipLaunchKernelGGL(recovery_hist_kernel, dim3(st->n_cu * 4), dim3(BLOCK), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "launch recovery_hist_kernel");
+  hipLaunchKernelGGL(recovery_collect_kernel, dim3(st->n_cu * st->occ_rec), dim3(BLOCK), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "launch recovery_collect_kernel");
   return TOPK_OK;
 }
 

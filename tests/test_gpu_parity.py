@@ -178,6 +178,30 @@ def test_forced_modes_on_short_and_long_rows(mode):
     _check(s1, l1, out, label=f"c1 mode {mode}")
 
 
+def test_cooperative_recovery_queue_and_overflow():
+    # Forced recovery queues rows for the cooperative recovery kernels; past the
+    # queue's capacity (256 rows per call) rows are recovered in place.
+    N = 20000
+    for M in (5, 256, 300):
+        s, l = W.make_rows(M, N, [N - (i % 7) for i in range(M)], tail_p=0.01, seed=M, device=DEV)
+        out, st = _run(s, l, mode=tk.PATH_RECOVERY)
+        _check(s, l, out, label=f"recovery M={M}")
+        assert st["forced_recovery"] == M
+        assert st["queued"] == min(M, 256)
+
+
+def test_recovery_rows_mixed_with_normal_rows():
+    # Underfilling rows (queued) between ordinary sampled rows of one call.
+    L = 131072
+    adv = np.stack([_adversarial_row(L, 1000, 40 + i) for i in range(3)])
+    s1, l1 = _window_rows("c1", [(0, 5)])
+    s = torch.cat([s1[:, :L], torch.from_numpy(adv).to(DEV)]).contiguous()
+    l = torch.cat([l1.clamp(max=L), torch.full((3,), L, dtype=torch.int32, device=DEV)]).contiguous()
+    out, st = _run(s, l)
+    _check(s, l, out, label="mixed recovery")
+    assert st["queued"] >= 3 and st["recover_under"] >= 3
+
+
 # ---------------------------------------------------- inputs and edge cases
 
 
