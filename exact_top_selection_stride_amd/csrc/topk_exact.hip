@@ -82,6 +82,7 @@ constexpr uint32_t KEY_MAX = 0xFFFFFFFFu;
 
 static_assert(NB % BLOCK == 0, "bins per thread must be integral");
 static_assert(TOPK_K_MAX * 7 / 4 + 1 <= CAP, "candidate buffer must hold the tau1 target");
+static_assert(FL_CAP <= BLOCK, "frontier lists are ranked one element per thread");
 
 struct Control {
   uint32_t row_ticket;   // next row of the persistent row loop
@@ -101,8 +102,10 @@ struct RecSlot {
   uint32_t lo, hi;       // key range binned by the first histogram
   uint32_t out_gt;       // output slots taken by keys above the boundary bin
   uint32_t cnt;          // candidates collected from the boundary bin
-  uint32_t done;         // work items of this row finished by the collect kernel
-  uint32_t pad[25];
+  uint32_t bin_above;    // keys above the boundary bin
+  uint32_t bin_count;    // keys in the boundary bin
+  uint32_t bin_lo, bin_hi;
+  uint32_t pad[22];
   uint32_t hist[NB];
   uint32_t cand_idx[CAP];
   uint32_t cand_key[CAP];
@@ -297,6 +300,20 @@ __device__ void select_rank(ForKeys&& for_keys, uint32_t r, uint32_t lo, uint32_
     hi = blo + (d < wdt ? d : wdt);
   }
   __syncthreads();
+}
+
+// For a short key list in LDS (m <= BLOCK): thread i < m returns the number of keys
+// ahead of keys[i] in the strict order (key descending, position ascending).
+__device__ __forceinline__ uint32_t rank_in_list(const uint32_t* keys, uint32_t m) {
+  const uint32_t i = threadIdx.x;
+  if (i >= m) return KEY_MAX;
+  const uint32_t ki = keys[i];
+  uint32_t r = 0;
+  for (uint32_t j = 0; j < m; ++j) {
+    const uint32_t kj = keys[j];
+    r += (kj > ki || (kj == ki && j < i)) ? 1u : 0u;
+  }
+  return r;
 }
 
 template <class F>
@@ -602,10 +619,13 @@ __device__ void fused_pass(grow_t x, uint32_t L, const PassCtx c) {
 
 constexpr uint32_t LINE_SAMPLE_MAX = 8192;              // n_s limit of line sampling
 constexpr int LM_PER_THREAD = LINE_SAMPLE_MAX / BLOCK;  // lines per thread in the hot step
-constexpr int SAMPLE_UNROLL = 8;
+constexpr int SAMPLE_UNROLL = 6;
 
 // Reads the n_s sampled lines whole. skey[j] = key(x[j*128]); lmax[j] = max key of
 // the line's elements inside the row. Tracks the min/max sample key in s.mn/s.mx.
+// Eight lanes read one line (one 16-byte chunk each); batches of SAMPLE_UNROLL
+// loads per lane are double-buffered so the next batch is in flight while the
+// current one is reduced.
 __device__ void sample_lines(grow_t x, uint32_t L, uint32_t n_s, uint32_t* skey, uint32_t* lmax) {
   const uint32_t t = threadIdx.x;
   const uint32_t off4 = (uint32_t)((uintptr_t)x & 127u) >> 2;
@@ -617,20 +637,22 @@ __device__ void sample_lines(grow_t x, uint32_t L, uint32_t n_s, uint32_t* skey,
   const uint32_t gfirst = off4 & ~3u;        // chunk holding the row's first element
   const uint32_t glast = (hi - 1u) & ~3u;    // chunk holding the row's last element
   constexpr uint32_t LINES_PER_STEP = BLOCK / 8;
+  constexpr uint32_t STEP = LINES_PER_STEP * SAMPLE_UNROLL;  // lines per batch
   uint32_t mn = KEY_MAX, mx = 0;
-  for (uint32_t jb = 0; jb < n_s; jb += LINES_PER_STEP * SAMPLE_UNROLL) {
-    u32x4 v[SAMPLE_UNROLL];
+  // Chunks outside the row read the row's first or last chunk instead (always in
+  // bounds, unconditional); their elements are masked out when reduced.
+  auto fetch = [&](u32x4 (&v)[SAMPLE_UNROLL], uint32_t step) {
 #pragma unroll
     for (int u = 0; u < SAMPLE_UNROLL; ++u) {
-      const uint32_t j = jb + u * LINES_PER_STEP + (t >> 3);
+      const uint32_t j = step * STEP + u * LINES_PER_STEP + (t >> 3);
       const uint32_t g = 128u * j + 4u * c;
-      // Chunks outside the row read the row's first or last chunk instead (always in
-      // bounds, unconditional); their elements are masked out below.
       v[u] = load4(base + (g < gfirst ? gfirst : (g < glast ? g : glast)));
     }
+  };
+  auto reduce = [&](const u32x4 (&v)[SAMPLE_UNROLL], uint32_t step) {
 #pragma unroll
     for (int u = 0; u < SAMPLE_UNROLL; ++u) {
-      const uint32_t j = jb + u * LINES_PER_STEP + (t >> 3);
+      const uint32_t j = step * STEP + u * LINES_PER_STEP + (t >> 3);
       const uint32_t g = 128u * j + 4u * c;
       uint32_t m = 0;
       if (j < n_s && g + 0 >= lo && g + 0 < hi) m = max(m, key_of_bits(v[u].x));
@@ -651,6 +673,26 @@ __device__ void sample_lines(grow_t x, uint32_t L, uint32_t n_s, uint32_t* skey,
         }
       }
     }
+  };
+  const uint32_t nsteps = (n_s + STEP - 1) / STEP;
+  u32x4 a[SAMPLE_UNROLL], b[SAMPLE_UNROLL];
+  fetch(a, 0);
+  uint32_t i = 0;
+  for (; i + 2 < nsteps; i += 2) {
+    fetch(b, i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    reduce(a, i);
+    fetch(a, i + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    reduce(b, i + 1);
+  }
+  if (i + 1 < nsteps) {
+    fetch(b, i + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    reduce(a, i);
+    reduce(b, i + 1);
+  } else {
+    reduce(a, i);
   }
   block_minmax(mn, mx);
 }
@@ -823,10 +865,12 @@ __device__ void refine_commit(uint32_t n, uint32_t K, const PassCtx c, gout_t ou
   __syncthreads();
   uint32_t T, gt2;
   if (fits) {
-    select_rank([&](auto&& f) {
-      for (uint32_t i = threadIdx.x; i < cb; i += BLOCK) f(g_s.fl_key[i]);
-    }, need, blo, bhi, T, gt2);
-    commit_list(s.fl_key, s.fl_idx, cb, T, above + gt2, K, out);
+    // The frontier holds at most BLOCK keys: each thread ranks one of them, and the
+    // first `need` in (key descending, position ascending) order are committed.
+    const uint32_t rk = rank_in_list(s.fl_key, cb);
+    const bool sel = rk < need;
+    const uint32_t pp = wave_reserve(sel, &s.out_gt);
+    if (sel && pp < K) out[pp] = (int32_t)s.fl_idx[threadIdx.x];
   } else {
     if (threadIdx.x == 0) stat_add(ctl, TOPK_STAT_FRONTIER_WIDE);
     const uint32_t* keys = &s.buf[CAP];
@@ -869,12 +913,56 @@ __device__ void recover_row(const Params& p, uint32_t row, grow_t x, uint32_t L,
       r->hi = hi;
       r->out_gt = 0;
       r->cnt = 0;
-      r->done = 0;
       stat_add(p.ctl, TOPK_STAT_QUEUED);
     }
     for (uint32_t i = t; i < (uint32_t)NB; i += BLOCK) r->hist[i] = 0;
   } else {
     exact_full_row(x, L, p.K, lo, hi, out, p.ctl);
+  }
+}
+
+// tau1 and tau0: the r1-th and r0-th largest (r0 <= r1) of the n_s sample keys in
+// s.buf[0, n_s), all inside [mn, mx]. One radix round finds the bin holding rank r1;
+// when the keys in that bin and above fit the frontier buffer (the usual case, r1
+// is a few dozen), both ranks are read off by counting inside that short list.
+// Otherwise the general narrowing selection runs.
+__device__ void select_taus(uint32_t n_s, uint32_t r0, uint32_t r1, uint32_t mn, uint32_t mx,
+                            uint32_t& t0key, uint32_t& t1key) {
+  Smem& s = g_s;
+  const uint32_t t = threadIdx.x;
+  const uint32_t sh = shift_for(mx - mn);
+  for (uint32_t i = t; i < (uint32_t)NB; i += BLOCK) s.hist[i] = 0;
+  if (t == 0) s.fl_cnt = 0;
+  __syncthreads();
+  for (uint32_t i = t; i < n_s; i += BLOCK) atomicAdd(&s.hist[(s.buf[i] - mn) >> sh], 1u);
+  __syncthreads();
+  block_find_bin(r1);
+  const uint32_t b = s.sel_bin;
+  const uint32_t m = s.sel_above + s.hist[b];  // sample keys in bin b and above
+  const uint32_t blo = mn + (b << sh);
+  if (m <= (uint32_t)FL_CAP) {
+    for (uint32_t i = t; i < n_s; i += BLOCK) {
+      const uint32_t k = s.buf[i];
+      const bool in = k >= blo;
+      const uint32_t f = wave_reserve(in, &s.fl_cnt);
+      if (in && f < (uint32_t)FL_CAP) s.fl_key[f] = k;
+    }
+    __syncthreads();
+    const uint32_t rk = rank_in_list(s.fl_key, m);
+    if (rk == r1 - 1) s.sel_above = s.fl_key[t];
+    if (rk == r0 - 1) s.sel_bin = s.fl_key[t];
+    __syncthreads();
+    t1key = s.sel_above;
+    t0key = s.sel_bin;
+    __syncthreads();
+  } else {
+    uint32_t unused;
+    select_rank([&](auto&& f) {
+      for (uint32_t i = threadIdx.x; i < n_s; i += BLOCK) f(g_s.buf[i]);
+    }, r1, mn, mx, t1key, unused);
+    select_rank([&](auto&& f) {
+      for (uint32_t i = threadIdx.x; i < n_s; i += BLOCK) f(g_s.buf[i]);
+    }, r0, t1key, mx, t0key, unused);
   }
 }
 
@@ -913,13 +1001,8 @@ __device__ void sampled_row(const Params& p, uint32_t row, grow_t x, uint32_t L,
   const uint32_t smin = s.mn, smax = s.mx;
   const uint32_t r1 = sample_rank(p.T1, n_s, L);
   const uint32_t r0 = sample_rank(p.T0, n_s, L);
-  uint32_t t1key, t0key, unused;
-  select_rank([&](auto&& f) {
-    for (uint32_t i = t; i < n_s; i += BLOCK) f(g_s.buf[i]);
-  }, r1, smin, smax, t1key, unused);
-  select_rank([&](auto&& f) {
-    for (uint32_t i = t; i < n_s; i += BLOCK) f(g_s.buf[i]);
-  }, r0, t1key, smax, t0key, unused);
+  uint32_t t1key, t0key;
+  select_taus(n_s, r0, r1, smin, smax, t0key, t1key);
 
   PassCtx c;
   c.t1key = t1key;
@@ -1010,10 +1093,9 @@ void topk_rows_kernel(Params p) {
     __syncthreads();
   }
   // The last workgroup to leave rewinds the row ticket for the next call. Every
-  // workgroup increments done_ticket only after its final ticket draw, so no draw
-  // can follow the rewind.
+  // workgroup increments done_ticket only after its final ticket draw has returned,
+  // so no draw can follow the rewind (both are device-scope atomics).
   if (t == 0) {
-    __threadfence();
     const uint32_t d = atomicAdd(&p.ctl->done_ticket, 1u);
     if (d == gridDim.x - 1) {
       atomicExch(&p.ctl->row_ticket, 0u);
@@ -1029,16 +1111,16 @@ void topk_rows_kernel(Params p) {
 // into the row's global histogram over [lo, hi] (clamped at both ends). The
 // collect kernel then derives, in every work item, the bin holding rank K,
 // commits the item's keys above that bin and appends the bin's keys to the row's
-// candidate buffer; the last work item of a row (ticket) selects the remaining
-// keys exactly from that buffer and commits them. Both kernels exit at once when
-// the queue is empty; the collect kernel's last workgroup rewinds the queue.
+// candidate buffer. The finish kernel (one workgroup per row) selects the
+// remaining keys exactly from that buffer and commits them. Kernel boundaries
+// order the three steps, so no cross-workgroup fences are needed. All three exit
+// at once when the queue is empty; the finish kernel's last workgroup rewinds it.
 
 struct RecHistSmem {
   uint32_t hist[NB];
 };
 __shared__ RecHistSmem g_rh;  // the histogram kernel's LDS state
 
-__device__ __forceinline__ uint32_t rec_items(uint32_t L) { return (L + REC_SEG - 1) / REC_SEG; }
 
 __global__ __launch_bounds__(BLOCK) void recovery_hist_kernel(Params p) {
   const uint32_t t = threadIdx.x;
@@ -1071,54 +1153,20 @@ __global__ __launch_bounds__(BLOCK) void recovery_hist_kernel(Params p) {
   }
 }
 
-// The last work item of a queued row: resolve the boundary bin exactly and commit.
-__device__ void finish_recovery(const Params& p, RecSlot* r, uint32_t above, uint32_t cb, uint32_t blo,
-                                uint32_t bhi, bool fits) {
-  Smem& s = g_s;
-  const uint32_t t = threadIdx.x;
-  const uint32_t K = p.K;
-  const uint32_t need = K - above;
-  const uint32_t L = r->L;
-  grow_t x = (grow_t)(p.scores) + (size_t)r->row * p.N;
-  gout_t out = (gout_t)(p.out) + (size_t)r->row * K;
-  if (t == 0) {
-    s.out_gt = above;
-    s.out_tie = 0;
-  }
-  uint32_t T, gt2;
-  if (fits) {
-    for (uint32_t i = t; i < cb; i += BLOCK) {
-      s.buf[i] = r->cand_idx[i];
-      s.buf[CAP + i] = r->cand_key[i];
-    }
-    __syncthreads();
-    select_rank([&](auto&& f) {
-      for (uint32_t i = threadIdx.x; i < cb; i += BLOCK) f(g_s.buf[CAP + i]);
-    }, need, blo, bhi, T, gt2);
-    commit_list(&s.buf[CAP], s.buf, cb, T, above + gt2, K, out);
-  } else {
-    if (t == 0) stat_add(p.ctl, TOPK_STAT_FRONTIER_WIDE);
-    __syncthreads();
-    select_rank([&](auto&& f) {
-      for_each_element(x, L, [&](uint32_t u, uint32_t) { f(key_of_bits(u)); });
-    }, need, blo, bhi, T, gt2);
-    const uint32_t gt_total = above + gt2;
-    const uint32_t ties = K - gt_total;
-    for_each_element(x, L, [&](uint32_t u, uint32_t e) {
-      const uint32_t k = key_of_bits(u);
-      const bool g = k > T && k <= bhi;
-      const uint32_t pp = wave_reserve(g, &s.out_gt);
-      if (g && pp < K) out[pp] = (int32_t)e;
-      const bool q_ = k == T;
-      const uint32_t q = wave_reserve(q_, &s.out_tie);
-      if (q_ && q < ties && gt_total + q < K) out[gt_total + q] = (int32_t)e;
-    });
-  }
-}
+// Per-item state of the collect kernel (its LDS is small, so many workgroups fit).
+struct RecCollectSmem {
+  uint32_t hist[NB];
+  uint32_t wtmp[NWAVES];
+  uint32_t wtmp2[NWAVES];
+  uint32_t sel_bin, sel_above;
+  uint32_t base_gt, base_bin;
+};
 
-__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
-void recovery_collect_kernel(Params p) {
-  Smem& s = g_s;
+constexpr int REC_CHUNKS = REC_SEG / 4 / BLOCK + 1;  // 16-byte chunks per thread per item
+__shared__ RecCollectSmem g_rc;
+
+__global__ __launch_bounds__(BLOCK) void recovery_collect_kernel(Params p) {
+  RecCollectSmem& s = g_rc;
   const uint32_t t = threadIdx.x;
   const uint32_t K = p.K;
   const uint32_t nq = min(p.ctl->qcount, QMAX);
@@ -1132,9 +1180,44 @@ void recovery_collect_kernel(Params p) {
     if (begin >= L) continue;
     const uint32_t n = min(REC_SEG, L - begin);
     // The boundary bin, from the completed histogram (every item derives the same).
-    for (uint32_t i = t; i < (uint32_t)NB; i += BLOCK) s.hist[i] = r->hist[i];
+    uint32_t h[NB / BLOCK];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < NB / BLOCK; ++j) {
+      h[j] = r->hist[t * (NB / BLOCK) + j];
+      sum += h[j];
+      s.hist[t * (NB / BLOCK) + j] = h[j];
+    }
+    uint32_t incl = wave_incl_scan(sum);
+    const uint32_t w = t / WAVE;
+    if (lane_id() == WAVE - 1) s.wtmp[w] = incl;
+    if (t == 0) {
+      s.sel_bin = 0;
+      s.sel_above = 0;
+    }
     __syncthreads();
-    block_find_bin(K);
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (int i = 0; i < NWAVES; ++i) {
+      const uint32_t v = s.wtmp[i];
+      before += ((uint32_t)i < w) ? v : 0u;
+      total += v;
+    }
+    incl += before;
+    const uint32_t hi_cnt = total - incl;
+    if (hi_cnt < K && K <= hi_cnt + sum) {
+      uint32_t cum = hi_cnt;
+#pragma unroll
+      for (int j = NB / BLOCK - 1; j >= 0; --j) {
+        if (cum + h[j] >= K) {
+          s.sel_bin = t * (NB / BLOCK) + j;
+          s.sel_above = cum;
+          break;
+        }
+        cum += h[j];
+      }
+    }
+    __syncthreads();
     const uint32_t b = s.sel_bin, above = s.sel_above;
     const uint32_t cb = s.hist[b];
     const uint32_t lo = r->lo, hi = r->hi;
@@ -1145,37 +1228,156 @@ void recovery_collect_kernel(Params p) {
     const uint32_t bhi = (b == (uint32_t)(NB - 1)) ? KEY_MAX
                                                    : braw + ((KEY_MAX - braw) < wdt ? (KEY_MAX - braw) : wdt);
     const bool fits = cb <= (uint32_t)CAP;
-    __syncthreads();
+    if (begin == 0 && t == 0) {  // one item per row records the bin for the finish kernel
+      r->bin_above = above;
+      r->bin_count = cb;
+      r->bin_lo = blo;
+      r->bin_hi = bhi;
+    }
     grow_t x = (grow_t)(p.scores) + (size_t)r->row * p.N + begin;
     gout_t out = (gout_t)(p.out) + (size_t)r->row * K;
-    for_each_element(x, n, [&](uint32_t u, uint32_t e) {
-      const uint32_t k = key_of_bits(u);
-      const bool g = k > bhi;
-      const uint32_t pp = wave_reserve(g, &r->out_gt);
-      if (g && pp < K) out[pp] = (int32_t)(begin + e);
-      if (fits) {
-        const bool in = k >= blo && k <= bhi;
-        const uint32_t f = wave_reserve(in, &r->cnt);
-        if (in && f < (uint32_t)CAP) {
-          r->cand_idx[f] = begin + e;
-          r->cand_key[f] = k;
+    // The item stays in registers: count this thread's keys above the bin and in the
+    // bin, reserve the item's output and candidate slots with one atomic each, then
+    // write. Offsets are in floats from the 16-byte chunk holding x[0].
+    const uint32_t off = (uint32_t)((uintptr_t)x & 15u) >> 2;
+    grow_t ab = x - off;
+    const uint32_t glast = (off + n - 1u) & ~3u;
+    u32x4 v[REC_CHUNKS];
+#pragma unroll
+    for (int u = 0; u < REC_CHUNKS; ++u) {
+      const uint32_t g = 4u * (t + (uint32_t)u * BLOCK);
+      v[u] = load4(ab + (g < glast ? g : glast));
+    }
+    uint32_t na = 0, nb = 0;
+#pragma unroll
+    for (int u = 0; u < REC_CHUNKS; ++u) {
+      const uint32_t g = 4u * (t + (uint32_t)u * BLOCK);
+      const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t o = g + i;
+        const uint32_t k = key_of_bits(w4[i]);
+        const bool ok = o >= off && o < off + n;
+        na += (ok && k > bhi) ? 1u : 0u;
+        nb += (ok && fits && k >= blo && k <= bhi) ? 1u : 0u;
+      }
+    }
+    uint32_t ia = wave_incl_scan(na), ib = wave_incl_scan(nb);
+    if (lane_id() == WAVE - 1) {
+      s.wtmp[w] = ia;
+      s.wtmp2[w] = ib;
+    }
+    __syncthreads();
+    uint32_t pa = 0, pb = 0, ta = 0, tb = 0;
+#pragma unroll
+    for (int i = 0; i < NWAVES; ++i) {
+      const uint32_t va = s.wtmp[i], vb = s.wtmp2[i];
+      pa += ((uint32_t)i < w) ? va : 0u;
+      pb += ((uint32_t)i < w) ? vb : 0u;
+      ta += va;
+      tb += vb;
+    }
+    pa += ia - na;  // exclusive prefix of this thread
+    pb += ib - nb;
+    if (t == 0) {
+      s.base_gt = ta ? atomicAdd(&r->out_gt, ta) : 0u;
+      s.base_bin = tb ? atomicAdd(&r->cnt, tb) : 0u;
+    }
+    __syncthreads();
+    pa += s.base_gt;
+    pb += s.base_bin;
+#pragma unroll
+    for (int u = 0; u < REC_CHUNKS; ++u) {
+      const uint32_t g = 4u * (t + (uint32_t)u * BLOCK);
+      const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t o = g + i;
+        const uint32_t k = key_of_bits(w4[i]);
+        const bool ok = o >= off && o < off + n;
+        const uint32_t e = begin + o - off;  // element index in the row
+        if (ok && k > bhi) {
+          if (pa < K) out[pa] = (int32_t)e;
+          ++pa;
+        }
+        if (ok && fits && k >= blo && k <= bhi) {
+          if (pb < (uint32_t)CAP) {
+            r->cand_idx[pb] = e;
+            r->cand_key[pb] = k;
+          }
+          ++pb;
         }
       }
-    });
-    __threadfence();  // release this item's candidates and outputs before its ticket
+    }
     __syncthreads();
-    if (t == 0) s.bcast = (atomicAdd(&r->done, 1u) == rec_items(L) - 1) ? 1u : 0u;
-    __syncthreads();
-    if (s.bcast) {
-      __threadfence();  // acquire every other item's candidates
-      finish_recovery(p, r, above, cb, blo, bhi, fits);
+  }
+}
+
+// One workgroup per queued row: resolve the boundary bin exactly and commit the
+// remaining K - above keys. The kernel boundary orders it after every collect item.
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
+void recovery_finish_kernel(Params p) {
+  Smem& s = g_s;
+  const uint32_t t = threadIdx.x;
+  const uint32_t K = p.K;
+  const uint32_t nq = min(p.ctl->qcount, QMAX);
+  for (uint32_t q = blockIdx.x; q < nq; q += gridDim.x) {
+    RecSlot* r = p.rec + q;
+    const uint32_t above = r->bin_above, cb = r->bin_count;
+    const uint32_t blo = r->bin_lo, bhi = r->bin_hi;
+    const uint32_t need = K - above;
+    const uint32_t L = r->L;
+    grow_t x = (grow_t)(p.scores) + (size_t)r->row * p.N;
+    gout_t out = (gout_t)(p.out) + (size_t)r->row * K;
+    if (t == 0) {
+      s.out_gt = above;
+      s.out_tie = 0;
+    }
+    uint32_t T, gt2;
+    if (cb <= (uint32_t)FL_CAP) {
+      if (t < cb) {
+        s.fl_idx[t] = r->cand_idx[t];
+        s.fl_key[t] = r->cand_key[t];
+      }
+      __syncthreads();
+      const uint32_t rk = rank_in_list(s.fl_key, cb);
+      const bool sel = rk < need;
+      const uint32_t pp = wave_reserve(sel, &s.out_gt);
+      if (sel && pp < K) out[pp] = (int32_t)s.fl_idx[t];
+    } else if (cb <= (uint32_t)CAP) {
+      for (uint32_t i = t; i < cb; i += BLOCK) {
+        s.buf[i] = r->cand_idx[i];
+        s.buf[CAP + i] = r->cand_key[i];
+      }
+      __syncthreads();
+      select_rank([&](auto&& f) {
+        for (uint32_t i = threadIdx.x; i < cb; i += BLOCK) f(g_s.buf[CAP + i]);
+      }, need, blo, bhi, T, gt2);
+      commit_list(&s.buf[CAP], s.buf, cb, T, above + gt2, K, out);
+    } else {
+      // The boundary bin is wider than the buffer: narrow it with passes over the row.
+      if (t == 0) stat_add(p.ctl, TOPK_STAT_FRONTIER_WIDE);
+      __syncthreads();
+      select_rank([&](auto&& f) {
+        for_each_element(x, L, [&](uint32_t u, uint32_t) { f(key_of_bits(u)); });
+      }, need, blo, bhi, T, gt2);
+      const uint32_t gt_total = above + gt2;
+      const uint32_t ties = K - gt_total;
+      for_each_element(x, L, [&](uint32_t u, uint32_t e) {
+        const uint32_t k = key_of_bits(u);
+        const bool g = k > T && k <= bhi;
+        const uint32_t pp = wave_reserve(g, &s.out_gt);
+        if (g && pp < K) out[pp] = (int32_t)e;
+        const bool q_ = k == T;
+        const uint32_t qq = wave_reserve(q_, &s.out_tie);
+        if (q_ && qq < ties && gt_total + qq < K) out[gt_total + qq] = (int32_t)e;
+      });
     }
     __syncthreads();
   }
   // The last workgroup to leave rewinds the queue for the next call; every
   // workgroup has read qcount before it increments rec_done.
   if (t == 0) {
-    __threadfence();
     const uint32_t d = atomicAdd(&p.ctl->rec_done, 1u);
     if (d == gridDim.x - 1) {
       atomicExch(&p.ctl->qcount, 0u);
@@ -1270,7 +1472,7 @@ int get_state(bool capturing, DevState** out) {
     if (occ < 1) return fail(TOPK_ERR_HIP, "selector kernel cannot be resident (occupancy %d)", occ);
     int occ_rec = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &occ_rec, reinterpret_cast<const void*>(recovery_collect_kernel), BLOCK, 0);
+        &occ_rec, reinterpret_cast<const void*>(recovery_finish_kernel), BLOCK, 0);
     if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     if (occ_rec < 1) return fail(TOPK_ERR_HIP, "recovery kernel cannot be resident");
     // One allocation: the control block, then the recovery slots.
@@ -1356,9 +1558,13 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
   hipLaunchKernelGGL(recovery_hist_kernel, dim3(st->n_cu * 4), dim3(BLOCK), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch recovery_hist_kernel");
-  hipLaunchKernelGGL(recovery_collect_kernel, dim3(st->n_cu * st->occ_rec), dim3(BLOCK), 0, stream, p);
+  hipLaunchKernelGGL(recovery_collect_kernel, dim3(st->n_cu * 4), dim3(BLOCK), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch recovery_collect_kernel");
+  const unsigned fin_grid = (unsigned)(QMAX < (uint32_t)(st->n_cu * st->occ_rec) ? QMAX : st->n_cu * st->occ_rec);
+  hipLaunchKernelGGL(recovery_finish_kernel, dim3(fin_grid), dim3(BLOCK), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "launch recovery_finish_kernel");
   return TOPK_OK;
 }
 
