@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle leg")
     ap.add_argument("--check-rows", type=int, default=32, help="rows per group checked before timing")
-    ap.add_argument("--probe", action="store_true", help="also time the stream-read probe")
+    ap.add_argument("--no-probe", action="store_true", help="skip timing the stream-read probe")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy first (known bytes, for counter calibration)")
     return ap.parse_args()
@@ -253,7 +253,7 @@ def main():
         "kernel_source_digest": digest,
         "generation_s": round(t_gen, 2),
     }
-    if args.probe:
+    if not args.no_probe:
         sink = torch.empty(4096, device=dev)
         flat = window.view(-1)
         tk.stream_read_probe(flat, sink)

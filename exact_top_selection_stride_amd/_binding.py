@@ -31,6 +31,10 @@ PATH_ROWSPLIT = 2
 PATH_DIRECT = 3
 PATH_RECOVERY = 4
 
+EXEC_AUTO = 0
+EXEC_PERSISTENT = 1
+EXEC_ROW_PER_WG = 2
+
 STAT_NAMES = (
     "rows", "sentinel", "direct", "sampled", "tau0", "tau1", "recover_under", "recover_over",
     "rowsplit", "forced_recovery", "long_exact", "frontier_wide", "queued",
@@ -40,6 +44,7 @@ STAT_COUNT = 16
 EXPORTED = (
     "topk_exact", "topk_exact_reserve", "topk_exact_get_stats", "topk_exact_reset_stats",
     "topk_exact_set_path_override", "topk_exact_last_error", "topk_stream_read_probe",
+    "topk_exact_set_execution",
 )
 
 
@@ -71,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.topk_exact_reset_stats.argtypes = [vp]
         L.topk_exact_set_path_override.restype = ctypes.c_int
         L.topk_exact_set_path_override.argtypes = [ctypes.c_int]
+        L.topk_exact_set_execution.restype = ctypes.c_int
+        L.topk_exact_set_execution.argtypes = [ctypes.c_int]
         L.topk_exact_last_error.restype = ctypes.c_char_p
         L.topk_exact_last_error.argtypes = []
         L.topk_stream_read_probe.restype = ctypes.c_int
@@ -156,6 +163,19 @@ def path_override(mode: int):
         yield
     finally:
         set_path_override(PATH_AUTO)
+
+
+def set_execution(mode: int):
+    _check(lib().topk_exact_set_execution(int(mode)), "topk_exact_set_execution")
+
+
+@contextlib.contextmanager
+def execution(mode: int):
+    set_execution(mode)
+    try:
+        yield
+    finally:
+        set_execution(EXEC_AUTO)
 
 
 def stream_read_probe(x: torch.Tensor, sink: torch.Tensor, stream=None):

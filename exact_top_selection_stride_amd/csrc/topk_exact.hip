@@ -74,7 +74,7 @@ constexpr int CAP = 8192;             // candidate (index, key) pairs in LDS
 constexpr int KEYS_CAP = 2 * CAP;     // keys-only capacity of the same region
 constexpr int FL_CAP = 512;           // frontier (index, key) pairs
 constexpr uint32_t STRIDE = 128;      // sample stride s
-constexpr int UNROLL = 4;             // 128-bit loads per thread per batch
+constexpr int UNROLL = 3;             // 128-bit loads per thread per batch
 constexpr uint32_t DIRECT_MAX_DEFAULT = 16384;
 constexpr uint32_t QMAX = 256;        // rows queued for cooperative recovery per call
 constexpr uint32_t REC_SEG = 16384;   // elements per recovery work item
@@ -457,7 +457,7 @@ __device__ __attribute__((noinline)) void exact_full_row(grow_t x, uint32_t L, u
 
 // ---------------------------------------------------------- direct (in LDS)
 
-__device__ void direct_exact(grow_t x, uint32_t L, uint32_t K, gout_t out) {
+__device__ __forceinline__ void direct_exact(grow_t x, uint32_t L, uint32_t K, gout_t out) {
   Smem& s = g_s;
   uint32_t mn = KEY_MAX, mx = 0;
   for_each_element(x, L, [&](uint32_t u, uint32_t e) {
@@ -557,7 +557,7 @@ __device__ __forceinline__ void admit_quad(const u32x4& v, uint32_t e, const Pas
 // loads is issued before the current one is examined so that each thread keeps
 // 2 x UNROLL 128-bit loads in flight.
 template <bool POS>
-__device__ void fused_pass(grow_t x, uint32_t L, const PassCtx c) {
+__device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, const PassCtx c) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   uint32_t c0w = 0;
@@ -626,7 +626,7 @@ constexpr int SAMPLE_UNROLL = 6;
 // Eight lanes read one line (one 16-byte chunk each); batches of SAMPLE_UNROLL
 // loads per lane are double-buffered so the next batch is in flight while the
 // current one is reduced.
-__device__ void sample_lines(grow_t x, uint32_t L, uint32_t n_s, uint32_t* skey, uint32_t* lmax) {
+__device__ __forceinline__ void sample_lines(grow_t x, uint32_t L, uint32_t n_s, uint32_t* skey, uint32_t* lmax) {
   const uint32_t t = threadIdx.x;
   const uint32_t off4 = (uint32_t)((uintptr_t)x & 127u) >> 2;
   grow_t base = x - off4;
@@ -700,7 +700,7 @@ __device__ void sample_lines(grow_t x, uint32_t L, uint32_t n_s, uint32_t* skey,
 // Re-reads the sampled lines whose maximum reaches tau1 and admits their elements.
 // Bit m of hot_mask is set when line t + m*BLOCK is hot (the LDS maxima are gone).
 template <bool POS>
-__device__ void hot_lines(grow_t x, uint32_t L, uint32_t hot_mask, const PassCtx c) {
+__device__ __forceinline__ void hot_lines(grow_t x, uint32_t L, uint32_t hot_mask, const PassCtx c) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   uint32_t c0w = 0;
@@ -769,7 +769,7 @@ __device__ __forceinline__ u32x4 mask_tail(u32x4 v, uint32_t g, uint32_t hi) {
 
 // The full-row pass over the non-sampled lines (see the geometry note above).
 template <bool POS>
-__device__ void fused_pass_lines(grow_t x, uint32_t L, uint32_t n_s, const PassCtx c) {
+__device__ __forceinline__ void fused_pass_lines(grow_t x, uint32_t L, uint32_t n_s, const PassCtx c) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   uint32_t c0w = 0;
@@ -835,7 +835,7 @@ __device__ void fused_pass_lines(grow_t x, uint32_t L, uint32_t n_s, const PassC
 
 // Boundary refinement and commit after a certified pass: n = C(tau1) <= CAP
 // candidates are in LDS with the first histogram over (key - key(tau1)) >> sh.
-__device__ void refine_commit(uint32_t n, uint32_t K, const PassCtx c, gout_t out, Control* ctl) {
+__device__ __forceinline__ void refine_commit(uint32_t n, uint32_t K, const PassCtx c, gout_t out, Control* ctl) {
   Smem& s = g_s;
   block_find_bin(K);
   const uint32_t b = s.sel_bin, above = s.sel_above;
@@ -896,7 +896,7 @@ __device__ void refine_commit(uint32_t n, uint32_t K, const PassCtx c, gout_t ou
 // kernels (which run after this kernel and spread the row over the whole GPU), or
 // recovers it here when the queue is full. Nothing has been written to the row's
 // output yet. [lo, hi] is the key range the recovery histogram bins.
-__device__ void recover_row(const Params& p, uint32_t row, grow_t x, uint32_t L, uint32_t lo, uint32_t hi,
+__device__ __forceinline__ void recover_row(const Params& p, uint32_t row, grow_t x, uint32_t L, uint32_t lo, uint32_t hi,
                             gout_t out) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
@@ -926,7 +926,7 @@ __device__ void recover_row(const Params& p, uint32_t row, grow_t x, uint32_t L,
 // when the keys in that bin and above fit the frontier buffer (the usual case, r1
 // is a few dozen), both ranks are read off by counting inside that short list.
 // Otherwise the general narrowing selection runs.
-__device__ void select_taus(uint32_t n_s, uint32_t r0, uint32_t r1, uint32_t mn, uint32_t mx,
+__device__ __forceinline__ void select_taus(uint32_t n_s, uint32_t r0, uint32_t r1, uint32_t mn, uint32_t mx,
                             uint32_t& t0key, uint32_t& t1key) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
@@ -973,7 +973,7 @@ __device__ __forceinline__ uint32_t sample_rank(uint32_t target, uint32_t n_s, u
   return (uint32_t)r;
 }
 
-__device__ void sampled_row(const Params& p, uint32_t row, grow_t x, uint32_t L, gout_t out) {
+__device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_t x, uint32_t L, gout_t out) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   const uint32_t n_s = (L + STRIDE - 1) / STRIDE;
@@ -1051,9 +1051,10 @@ __device__ void sampled_row(const Params& p, uint32_t row, grow_t x, uint32_t L,
   }
 }
 
-// One row, start to commit. Kept out of line so that registers are allocated per
-// row phase rather than across the persistent row loop.
-__device__ __attribute__((noinline)) void process_row(Params p, uint32_t row) {
+// One row, start to commit. Everything on the row's path is inlined: an out-of-line
+// call per row would save and restore its callee-saved registers through scratch
+// memory for every row.
+__device__ __forceinline__ void process_row(const Params& p, uint32_t row) {
   const uint32_t t = threadIdx.x;
   const int32_t len = p.row_len[row];
   uint32_t L = len < 0 ? 0u : (uint32_t)len;
@@ -1080,10 +1081,19 @@ __device__ __attribute__((noinline)) void process_row(Params p, uint32_t row) {
   }
 }
 
+// The selector kernel. Persistent execution: a grid of resident workgroups pulls
+// rows from a device ticket until none is left. Otherwise one workgroup per row,
+// and the hardware dispatcher balances the rows over the CUs.
+template <bool PERSISTENT>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
 void topk_rows_kernel(Params p) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
+  if (!PERSISTENT) {
+    if (t == 0) s.row = (int32_t)blockIdx.x;
+    process_row(p, blockIdx.x);
+    return;
+  }
   for (;;) {
     if (t == 0) s.row = (int32_t)atomicAdd(&p.ctl->row_ticket, 1u);
     __syncthreads();
@@ -1391,19 +1401,27 @@ __global__ void zero_stats_kernel(Control* ctl) {
   if (t < (uint32_t)TOPK_STAT_COUNT) ctl->stats[t] = 0ull;
 }
 
+// Plain streaming read for the measured-ceiling report: workgroup b reads the
+// contiguous span [b*span, (b+1)*span) of 16-byte chunks, eight independent loads per
+// lane per step, and folds the bits so the loads cannot be elided.
 __global__ __launch_bounds__(BLOCK) void stream_read_probe_kernel(const float* __restrict__ x, uint64_t n,
                                                                   float* __restrict__ sink) {
-  const uint4* p4 = reinterpret_cast<const uint4*>(x);
+  const u32x4* p4 = reinterpret_cast<const u32x4*>(x);
   const uint64_t nv = n >> 2;
+  const uint64_t span = (nv + gridDim.x - 1) / gridDim.x;
+  const uint64_t beg = (uint64_t)blockIdx.x * span;
+  const uint64_t end = beg + span < nv ? beg + span : nv;
   uint32_t acc = 0;
-  const uint64_t stride = (uint64_t)gridDim.x * BLOCK;
-  uint64_t q = (uint64_t)blockIdx.x * BLOCK + threadIdx.x;
-  for (; q + 3 * stride < nv; q += 4 * stride) {
-    const uint4 a = p4[q], b = p4[q + stride], c = p4[q + 2 * stride], d = p4[q + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  uint64_t q = beg + threadIdx.x;
+  for (; q + 7 * BLOCK < end; q += 8 * BLOCK) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p4[q + (uint64_t)u * BLOCK];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; q < nv; q += stride) {
-    const uint4 a = p4[q];
+  for (; q < end; q += BLOCK) {
+    const u32x4 a = p4[q];
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   if (blockIdx.x == 0) {
@@ -1436,6 +1454,7 @@ constexpr int MAX_DEVICES = 64;
 std::mutex g_mu;
 DevState g_dev[MAX_DEVICES];
 std::atomic<int> g_mode{TOPK_PATH_AUTO};
+std::atomic<int> g_exec{TOPK_EXEC_AUTO};
 thread_local char g_err[512] = "";
 
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -1466,8 +1485,8 @@ int get_state(bool capturing, DevState** out) {
     int n_cu = 0, occ = 0;
     e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(topk_rows_kernel),
-                                                     BLOCK, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &occ, reinterpret_cast<const void*>(topk_rows_kernel<true>), BLOCK, 0);
     if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     if (occ < 1) return fail(TOPK_ERR_HIP, "selector kernel cannot be resident (occupancy %d)", occ);
     int occ_rec = 0;
@@ -1549,9 +1568,19 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
   p.direct_max = DIRECT_MAX_DEFAULT;
   p.mode = g_mode.load();
   p.rec = st->rec;
+  // Persistent execution for many long rows per resident workgroup; one workgroup
+  // per row otherwise (measured on MI355X: equal on 0.5-1M-wide rows, faster on
+  // short rows, where the per-row loop overhead is not amortised).
   const int64_t resident = (int64_t)st->occ * st->n_cu;
-  const unsigned grid = (unsigned)(M < resident ? M : resident);
-  hipLaunchKernelGGL(topk_rows_kernel, dim3(grid), dim3(BLOCK), 0, stream, p);
+  const int ex = g_exec.load();
+  const bool persistent = ex == TOPK_EXEC_PERSISTENT ||
+                          (ex == TOPK_EXEC_AUTO && M >= 4 * resident && N_alloc >= 262144);
+  if (persistent) {
+    const unsigned grid = (unsigned)(M < resident ? M : resident);
+    hipLaunchKernelGGL(topk_rows_kernel<true>, dim3(grid), dim3(BLOCK), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL(topk_rows_kernel<false>, dim3((unsigned)M), dim3(BLOCK), 0, stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch topk_rows_kernel");
   // Exact recovery of the rows the selector queued (both exit at once if none).
@@ -1619,6 +1648,14 @@ int topk_exact_set_path_override(int mode) {
   return TOPK_OK;
 }
 
+int topk_exact_set_execution(int mode) {
+  g_err[0] = '\0';
+  if (mode < TOPK_EXEC_AUTO || mode > TOPK_EXEC_ROW_PER_WG)
+    return fail(TOPK_ERR_BAD_ARG, "execution mode %d unknown", mode);
+  g_exec.store(mode);
+  return TOPK_OK;
+}
+
 const char* topk_exact_last_error(void) { return g_err; }
 
 int topk_stream_read_probe(const float* x, int64_t n, float* sink, hipStream_t stream) {
@@ -1633,8 +1670,9 @@ int topk_stream_read_probe(const float* x, int64_t n, float* sink, hipStream_t s
   DevState* st = nullptr;
   rc = get_state(capturing, &st);
   if (rc != TOPK_OK) return rc;
-  int64_t want = (n / 4 + BLOCK * 16 - 1) / (BLOCK * 16);
-  int64_t cap = (int64_t)st->n_cu * 8;
+  // Two workgroups per CU (the selector's residency), fewer for small inputs.
+  int64_t want = (n / 4 + BLOCK * 8 - 1) / (BLOCK * 8);
+  int64_t cap = (int64_t)st->n_cu * 2;
   if (cap > 4096) cap = 4096;
   const unsigned grid = (unsigned)(want < 1 ? 1 : (want < cap ? want : cap));
   hipLaunchKernelGGL(stream_read_probe_kernel, dim3(grid), dim3(BLOCK), 0, stream, x, (uint64_t)n, sink);

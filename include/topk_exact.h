@@ -65,6 +65,11 @@ typedef enum {
 #define TOPK_PATH_DIRECT 3    /* every row with L > K takes the direct exact path */
 #define TOPK_PATH_RECOVERY 4  /* every row with L > K takes exact full-row recovery */
 
+/* Execution modes: how rows map to workgroups (default TOPK_EXEC_AUTO). */
+#define TOPK_EXEC_AUTO 0        /* shape-based choice below */
+#define TOPK_EXEC_PERSISTENT 1  /* resident workgroups loop over rows via a device ticket */
+#define TOPK_EXEC_ROW_PER_WG 2  /* one workgroup per row, balanced by the hardware dispatcher */
+
 /* Statistics slots returned by topk_exact_get_stats (row counts since the last reset). */
 enum {
   TOPK_STAT_ROWS = 0,            /* rows processed */
@@ -117,6 +122,12 @@ int topk_exact_reset_stats(hipStream_t stream);
 /* Forces one execution path for later calls (TOPK_PATH_*); a captured graph keeps the
  * mode that was set when it was captured. Process-wide. */
 int topk_exact_set_path_override(int mode);
+
+/* Selects how rows map to workgroups for later calls (TOPK_EXEC_*). Auto uses
+ * persistent execution when M is at least four times the resident workgroup count
+ * and N_alloc >= 262144, one workgroup per row otherwise. Both give identical
+ * results; a captured graph keeps the mode set when it was captured. Process-wide. */
+int topk_exact_set_execution(int mode);
 
 /* Text of the last error raised on this host thread ("" if none). */
 const char* topk_exact_last_error(void);

@@ -58,6 +58,14 @@ def test_argument_validation_without_gpu():
     assert L.topk_stream_read_probe(None, 0, None, None) == B.TOPK_OK
 
 
+def test_execution_mode_roundtrip():
+    L = tk.lib()
+    assert L.topk_exact_set_execution(7) == B.TOPK_ERR_BAD_ARG
+    assert L.topk_exact_set_execution(-1) == B.TOPK_ERR_BAD_ARG
+    for mode in (B.EXEC_PERSISTENT, B.EXEC_ROW_PER_WG, B.EXEC_AUTO):
+        tk.set_execution(mode)
+
+
 def test_path_override_roundtrip():
     for mode in (B.PATH_SAMPLED, B.PATH_ROWSPLIT, B.PATH_DIRECT, B.PATH_RECOVERY, B.PATH_AUTO):
         tk.set_path_override(mode)

@@ -267,13 +267,28 @@ def test_other_k(Ksmall):
         _check(ss, ll, out, K=Ksmall, label=f"K={Ksmall}")
 
 
+@pytest.mark.parametrize("execution", [tk.EXEC_PERSISTENT, tk.EXEC_ROW_PER_WG])
+def test_execution_modes_agree_with_oracle(execution):
+    # Both row-to-workgroup mappings on short, medium and long rows, with recovery rows.
+    cases = [W.make_window(W.get("c0"), DEV), _window_rows("c1", [(0, 12), (8000, 12)]),
+             _window_rows("c3b", [(10, 3)]), _window_rows("c4_n16384_m512", [(0, 30)])]
+    L = 131072
+    adv = torch.from_numpy(np.stack([_adversarial_row(L, 1000, 70 + i) for i in range(2)])).to(DEV)
+    cases.append((adv, torch.full((2,), L, dtype=torch.int32, device=DEV)))
+    with tk.execution(execution):
+        for s, l in cases:
+            out, st = _run(s, l)
+            _check(s, l, out, label=f"execution {execution} shape {tuple(s.shape)}")
+
+
 def test_consecutive_calls_reuse_the_ticket():
     # Row tickets rewind after every call: calls of different M back to back.
     s, l = _window_rows("c1", [(0, 40)])
-    for M in (40, 3, 1, 17, 40):
-        out = tk.topk_exact(s[:M], l[:M].contiguous(), K=K)
-        torch.cuda.synchronize()
-        _check(s[:M], l[:M], out, label=f"M={M}")
+    with tk.execution(tk.EXEC_PERSISTENT):
+        for M in (40, 3, 1, 17, 40):
+            out = tk.topk_exact(s[:M], l[:M].contiguous(), K=K)
+            torch.cuda.synchronize()
+            _check(s[:M], l[:M], out, label=f"M={M}")
 
 
 def test_graph_replay():
