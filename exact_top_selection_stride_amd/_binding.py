@@ -34,6 +34,7 @@ PATH_RECOVERY = 4
 EXEC_AUTO = 0
 EXEC_PERSISTENT = 1
 EXEC_ROW_PER_WG = 2
+EXEC_ROWSPLIT = 3
 
 STAT_NAMES = (
     "rows", "sentinel", "direct", "sampled", "tau0", "tau1", "recover_under", "recover_over",

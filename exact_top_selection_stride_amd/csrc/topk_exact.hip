@@ -78,6 +78,7 @@ constexpr int UNROLL = 3;             // 128-bit loads per thread per batch
 constexpr uint32_t DIRECT_MAX_DEFAULT = 16384;
 constexpr uint32_t QMAX = 256;        // rows queued for cooperative recovery per call
 constexpr uint32_t REC_SEG = 16384;   // elements per recovery work item
+constexpr int64_t ROWSPLIT_MIN_N = 65536;  // auto row-split only for rows at least this wide
 constexpr uint32_t KEY_MAX = 0xFFFFFFFFu;
 
 static_assert(NB % BLOCK == 0, "bins per thread must be integral");
@@ -125,6 +126,9 @@ struct Params {
   uint32_t direct_max;  // auto mode: rows up to this length take the direct path
   int32_t mode;
   RecSlot* rec;         // QMAX recovery slots
+  struct RowSplitState* rs;  // per-row state of the row-split kernels
+  uint32_t ps;          // row-split: workgroups per row sampling
+  uint32_t pp;          // row-split: workgroups per row passing
 };
 
 struct Smem {
@@ -621,12 +625,14 @@ constexpr uint32_t LINE_SAMPLE_MAX = 8192;              // n_s limit of line sam
 constexpr int LM_PER_THREAD = LINE_SAMPLE_MAX / BLOCK;  // lines per thread in the hot step
 constexpr int SAMPLE_UNROLL = 6;
 
-// Reads the n_s sampled lines whole. skey[j] = key(x[j*128]); lmax[j] = max key of
-// the line's elements inside the row. Tracks the min/max sample key in s.mn/s.mx.
+// Reads the sampled lines j0 <= j < j1 whole. skey[j] = key(x[j*128]); lmax[j] = max
+// key of the line's elements inside the row; mn/mx fold this thread's sample keys.
 // Eight lanes read one line (one 16-byte chunk each); batches of SAMPLE_UNROLL
 // loads per lane are double-buffered so the next batch is in flight while the
-// current one is reduced.
-__device__ __forceinline__ void sample_lines(grow_t x, uint32_t L, uint32_t n_s, uint32_t* skey, uint32_t* lmax) {
+// current one is reduced. P is an LDS or a global pointer type.
+template <class P>
+__device__ __forceinline__ void sample_lines_range(grow_t x, uint32_t L, uint32_t j0, uint32_t j1, P skey,
+                                                   P lmax, uint32_t& mn, uint32_t& mx) {
   const uint32_t t = threadIdx.x;
   const uint32_t off4 = (uint32_t)((uintptr_t)x & 127u) >> 2;
   grow_t base = x - off4;
@@ -638,13 +644,12 @@ __device__ __forceinline__ void sample_lines(grow_t x, uint32_t L, uint32_t n_s,
   const uint32_t glast = (hi - 1u) & ~3u;    // chunk holding the row's last element
   constexpr uint32_t LINES_PER_STEP = BLOCK / 8;
   constexpr uint32_t STEP = LINES_PER_STEP * SAMPLE_UNROLL;  // lines per batch
-  uint32_t mn = KEY_MAX, mx = 0;
   // Chunks outside the row read the row's first or last chunk instead (always in
   // bounds, unconditional); their elements are masked out when reduced.
   auto fetch = [&](u32x4 (&v)[SAMPLE_UNROLL], uint32_t step) {
 #pragma unroll
     for (int u = 0; u < SAMPLE_UNROLL; ++u) {
-      const uint32_t j = step * STEP + u * LINES_PER_STEP + (t >> 3);
+      const uint32_t j = j0 + step * STEP + u * LINES_PER_STEP + (t >> 3);
       const uint32_t g = 128u * j + 4u * c;
       v[u] = load4(base + (g < gfirst ? gfirst : (g < glast ? g : glast)));
     }
@@ -652,17 +657,17 @@ __device__ __forceinline__ void sample_lines(grow_t x, uint32_t L, uint32_t n_s,
   auto reduce = [&](const u32x4 (&v)[SAMPLE_UNROLL], uint32_t step) {
 #pragma unroll
     for (int u = 0; u < SAMPLE_UNROLL; ++u) {
-      const uint32_t j = step * STEP + u * LINES_PER_STEP + (t >> 3);
+      const uint32_t j = j0 + step * STEP + u * LINES_PER_STEP + (t >> 3);
       const uint32_t g = 128u * j + 4u * c;
       uint32_t m = 0;
-      if (j < n_s && g + 0 >= lo && g + 0 < hi) m = max(m, key_of_bits(v[u].x));
-      if (j < n_s && g + 1 >= lo && g + 1 < hi) m = max(m, key_of_bits(v[u].y));
-      if (j < n_s && g + 2 >= lo && g + 2 < hi) m = max(m, key_of_bits(v[u].z));
-      if (j < n_s && g + 3 >= lo && g + 3 < hi) m = max(m, key_of_bits(v[u].w));
+      if (j < j1 && g + 0 >= lo && g + 0 < hi) m = max(m, key_of_bits(v[u].x));
+      if (j < j1 && g + 1 >= lo && g + 1 < hi) m = max(m, key_of_bits(v[u].y));
+      if (j < j1 && g + 2 >= lo && g + 2 < hi) m = max(m, key_of_bits(v[u].z));
+      if (j < j1 && g + 3 >= lo && g + 3 < hi) m = max(m, key_of_bits(v[u].w));
       m = max(m, (uint32_t)__shfl_xor(m, 1));
       m = max(m, (uint32_t)__shfl_xor(m, 2));
       m = max(m, (uint32_t)__shfl_xor(m, 4));
-      if (j < n_s) {
+      if (j < j1) {
         if (c == 0) lmax[j] = m;
         if (c == cs) {
           const uint32_t w = is == 0 ? v[u].x : is == 1 ? v[u].y : is == 2 ? v[u].z : v[u].w;
@@ -674,7 +679,8 @@ __device__ __forceinline__ void sample_lines(grow_t x, uint32_t L, uint32_t n_s,
       }
     }
   };
-  const uint32_t nsteps = (n_s + STEP - 1) / STEP;
+  const uint32_t nsteps = (j1 - j0 + STEP - 1) / STEP;
+  if (nsteps == 0) return;
   u32x4 a[SAMPLE_UNROLL], b[SAMPLE_UNROLL];
   fetch(a, 0);
   uint32_t i = 0;
@@ -694,13 +700,19 @@ __device__ __forceinline__ void sample_lines(grow_t x, uint32_t L, uint32_t n_s,
   } else {
     reduce(a, i);
   }
+}
+
+// The whole row's sample into LDS, with the min/max sample key in s.mn/s.mx.
+__device__ __forceinline__ void sample_lines(grow_t x, uint32_t L, uint32_t n_s, uint32_t* skey, uint32_t* lmax) {
+  uint32_t mn = KEY_MAX, mx = 0;
+  sample_lines_range(x, L, 0u, n_s, skey, lmax, mn, mx);
   block_minmax(mn, mx);
 }
 
 // Re-reads the sampled lines whose maximum reaches tau1 and admits their elements.
-// Bit m of hot_mask is set when line t + m*BLOCK is hot (the LDS maxima are gone).
+// Bit m of hot_mask is set when line j0 + t + m*BLOCK is hot.
 template <bool POS>
-__device__ __forceinline__ void hot_lines(grow_t x, uint32_t L, uint32_t hot_mask, const PassCtx c) {
+__device__ __forceinline__ void hot_lines(grow_t x, uint32_t L, uint32_t j0, uint32_t hot_mask, const PassCtx c) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   uint32_t c0w = 0;
@@ -710,7 +722,7 @@ __device__ __forceinline__ void hot_lines(grow_t x, uint32_t L, uint32_t hot_mas
   const uint32_t gfirst = off4 & ~3u, glast = (hi - 1u) & ~3u;
 #pragma unroll 1
   for (int m = 0; m < LM_PER_THREAD; ++m) {
-    const uint32_t j = t + (uint32_t)m * BLOCK;
+    const uint32_t j = j0 + t + (uint32_t)m * BLOCK;
     const bool hot = (hot_mask >> m) & 1u;
     if (__ballot(hot) == 0) continue;
 #pragma unroll 1
@@ -768,8 +780,11 @@ __device__ __forceinline__ u32x4 mask_tail(u32x4 v, uint32_t g, uint32_t hi) {
 }
 
 // The full-row pass over the non-sampled lines (see the geometry note above).
+// Chunks k0 <= k < k1 of the non-sampled lines; with tail set, also the first line of
+// period n_s (which the row may reach into and which is never sampled).
 template <bool POS>
-__device__ __forceinline__ void fused_pass_lines(grow_t x, uint32_t L, uint32_t n_s, const PassCtx c) {
+__device__ __forceinline__ void fused_pass_lines(grow_t x, uint32_t L, uint32_t n_s, uint32_t k0, uint32_t k1,
+                                                 bool tail, const PassCtx c) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   uint32_t c0w = 0;
@@ -777,7 +792,7 @@ __device__ __forceinline__ void fused_pass_lines(grow_t x, uint32_t L, uint32_t 
   grow_t base = x - off4;
   const uint32_t hi = off4 + L;
   const uint32_t glast = (hi - 1u) & ~3u;  // chunk holding the row's last element
-  const uint32_t nk = 24u * n_s;
+  const uint32_t nk = k1 - k0;
   const uint32_t per = BLOCK * UNROLL;
   const uint32_t nfull = nk / per;
   auto examine = [&](const u32x4 (&raw)[UNROLL], uint32_t it) {
@@ -785,7 +800,7 @@ __device__ __forceinline__ void fused_pass_lines(grow_t x, uint32_t L, uint32_t 
     uint32_t g[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      g[u] = unsampled_offset(it * per + u * BLOCK + t);
+      g[u] = unsampled_offset(k0 + it * per + u * BLOCK + t);
       v[u] = mask_tail<POS>(raw[u], g[u], hi);
     }
     if (__ballot(batch_admits<POS>(v, c.thr)) != 0) {
@@ -795,7 +810,7 @@ __device__ __forceinline__ void fused_pass_lines(grow_t x, uint32_t L, uint32_t 
   };
   auto fetch = [&](u32x4 (&v)[UNROLL], uint32_t it) {
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) v[u] = load_chunk(base, unsampled_offset(it * per + u * BLOCK + t), glast);
+    for (int u = 0; u < UNROLL; ++u) v[u] = load_chunk(base, unsampled_offset(k0 + it * per + u * BLOCK + t), glast);
   };
   if (nfull > 0) {
     // Two batch buffers in ping-pong: while one batch is examined the next one is in
@@ -821,12 +836,12 @@ __device__ __forceinline__ void fused_pass_lines(grow_t x, uint32_t L, uint32_t 
       examine(a, it);
     }
   }
-  for (uint32_t k = nfull * per + t; k < nk; k += BLOCK) {
+  for (uint32_t k = k0 + nfull * per + t; k < k1; k += BLOCK) {
     const uint32_t g = unsampled_offset(k);
     admit_quad<POS>(mask_tail<POS>(load_chunk(base, g, glast), g, hi), g - off4, c, c0w);
   }
   // The first line of period n_s, if the row reaches into it (never sampled).
-  if (t < 8) {
+  if (tail && t < 8) {
     const uint32_t g = 128u * n_s + 4u * t;
     if (g < hi) admit_quad<POS>(mask_tail<POS>(load_chunk(base, g, glast), g, hi), g - off4, c, c0w);
   }
@@ -1024,11 +1039,11 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
   reset_row_state();  // its barrier also ends every read of the line maxima in LDS
   if (skip) {
     if (pos) {
-      hot_lines<true>(x, L, hot_mask, c);
-      fused_pass_lines<true>(x, L, n_s, c);
+      hot_lines<true>(x, L, 0u, hot_mask, c);
+      fused_pass_lines<true>(x, L, n_s, 0u, 24u * n_s, true, c);
     } else {
-      hot_lines<false>(x, L, hot_mask, c);
-      fused_pass_lines<false>(x, L, n_s, c);
+      hot_lines<false>(x, L, 0u, hot_mask, c);
+      fused_pass_lines<false>(x, L, n_s, 0u, 24u * n_s, true, c);
     }
   } else if (pos) {
     fused_pass<true>(x, L, c);
@@ -1396,6 +1411,225 @@ void recovery_finish_kernel(Params p) {
   }
 }
 
+// -------------------------------------------------------------- row-split
+//
+// Row-split execution (the pages' KV-split, [PD] question 2; [AX]): when rows are
+// few and long, one row's work is divided among several workgroups whose counts,
+// candidates and histograms are merged for a final unit that certifies and refines.
+// Here it is four kernels ordered by kernel boundaries (no workgroup waits on
+// another):
+//   split_sample (P_s x M)  each workgroup reads a share of the row's sampled lines
+//                           whole into the row's global sample area;
+//   split_select (M)        tau0 / tau1 once per row from the full sample;
+//   split_pass   (P_p x M)  hot lines and the fused pass over a share of the
+//                           512-byte periods; candidates, histogram and counts are
+//                           merged into the row's state (one atomic per workgroup,
+//                           one per non-empty bin);
+//   split_finish (M)        certify, then refine and commit or queue for recovery.
+// Rows the split does not apply to (L <= K, direct-exact, forced recovery, rows past
+// the line-sample limit) are processed whole by split_finish. split_finish also
+// rewinds the row state for the next call.
+
+constexpr uint32_t RS_MAX_ROWS = 1024;  // rows per call the row-split state holds
+
+struct RowSplitState {
+  uint32_t whole;       // 1: the split does not apply, split_finish takes the row whole
+  uint32_t mn_inv;      // bitwise NOT of the min sample key (atomicMax)
+  uint32_t mx;          // max sample key (atomicMax)
+  uint32_t c1;          // C(tau1): all admitted keys, even past CAP
+  uint32_t c0;          // C(tau0)
+  uint32_t t1key, t0key;
+  uint32_t pad[25];
+  uint32_t hist[NB];
+  uint32_t cand_idx[CAP];
+  uint32_t cand_key[CAP];
+  uint32_t skey[LINE_SAMPLE_MAX];
+  uint32_t lmax[LINE_SAMPLE_MAX];
+};
+
+__device__ __forceinline__ uint32_t row_length(const Params& p, uint32_t row) {
+  const int32_t len = p.row_len[row];
+  uint32_t L = len < 0 ? 0u : (uint32_t)len;
+  return L > p.N ? p.N : L;
+}
+
+__device__ __forceinline__ bool split_applies(const Params& p, uint32_t L) {
+  if (L <= p.K) return false;
+  if (p.mode == TOPK_PATH_DIRECT || p.mode == TOPK_PATH_RECOVERY) return false;
+  if (p.mode == TOPK_PATH_AUTO && L <= p.direct_max) return false;
+  return (L + STRIDE - 1) / STRIDE <= LINE_SAMPLE_MAX;
+}
+
+struct SplitSampleSmem {
+  uint32_t mn, mx;
+};
+__shared__ SplitSampleSmem g_ssm;
+
+__global__ __launch_bounds__(BLOCK) void split_sample_kernel(Params p) {
+  const uint32_t t = threadIdx.x, part = blockIdx.x, row = blockIdx.y;
+  RowSplitState* rs = p.rs + row;
+  const uint32_t L = row_length(p, row);
+  if (!split_applies(p, L)) {
+    if (part == 0 && t == 0) rs->whole = 1u;
+    return;
+  }
+  if (t == 0) {
+    g_ssm.mn = KEY_MAX;
+    g_ssm.mx = 0;
+  }
+  __syncthreads();
+  const uint32_t n_s = (L + STRIDE - 1) / STRIDE;
+  const uint32_t j0 = (uint32_t)((uint64_t)part * n_s / p.ps);
+  const uint32_t j1 = (uint32_t)((uint64_t)(part + 1) * n_s / p.ps);
+  grow_t x = (grow_t)(p.scores) + (size_t)row * p.N;
+  uint32_t mn = KEY_MAX, mx = 0;
+  sample_lines_range(x, L, j0, j1, (GLB uint32_t*)rs->skey, (GLB uint32_t*)rs->lmax, mn, mx);
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if (lane_id() == 0) {
+    atomicMin(&g_ssm.mn, mn);
+    atomicMax(&g_ssm.mx, mx);
+  }
+  __syncthreads();
+  if (t == 0) {
+    atomicMax(&rs->mn_inv, ~g_ssm.mn);
+    atomicMax(&rs->mx, g_ssm.mx);
+    if (part == 0) {
+      stat_add(p.ctl, TOPK_STAT_ROWS);
+      stat_add(p.ctl, TOPK_STAT_SAMPLED);
+      stat_add(p.ctl, TOPK_STAT_ROWSPLIT);
+    }
+  }
+}
+
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
+void split_select_kernel(Params p) {
+  Smem& s = g_s;
+  const uint32_t t = threadIdx.x, row = blockIdx.x;
+  RowSplitState* rs = p.rs + row;
+  if (rs->whole) return;
+  const uint32_t L = row_length(p, row);
+  const uint32_t n_s = (L + STRIDE - 1) / STRIDE;
+  for (uint32_t i = t; i < n_s; i += BLOCK) s.buf[i] = rs->skey[i];
+  __syncthreads();
+  uint32_t t0key, t1key;
+  select_taus(n_s, sample_rank(p.T0, n_s, L), sample_rank(p.T1, n_s, L), ~rs->mn_inv, rs->mx, t0key, t1key);
+  if (t == 0) {
+    rs->t1key = t1key;
+    rs->t0key = t0key;
+  }
+}
+
+__device__ __forceinline__ PassCtx pass_ctx(uint32_t t1key, uint32_t t0key, uint32_t smax) {
+  PassCtx c;
+  c.t1key = t1key;
+  c.t0key = t0key;
+  c.sh = shift_for(smax - t1key);
+  c.thr = t1key >= 0x80000000u ? (t1key ^ 0x80000000u) : ~t1key;
+  return c;
+}
+
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
+void split_pass_kernel(Params p) {
+  Smem& s = g_s;
+  const uint32_t t = threadIdx.x, part = blockIdx.x, row = blockIdx.y;
+  RowSplitState* rs = p.rs + row;
+  if (rs->whole) return;
+  const uint32_t L = row_length(p, row);
+  const uint32_t n_s = (L + STRIDE - 1) / STRIDE;
+  const uint32_t t1key = rs->t1key;
+  if (t1key == 0u) {
+    // Every key is admitted at the lowest threshold: count the row as overflowing
+    // so that it is recovered exactly.
+    if (part == 0 && t == 0) atomicAdd(&rs->c1, (uint32_t)CAP + 1u);
+    return;
+  }
+  const PassCtx c = pass_ctx(t1key, rs->t0key, rs->mx);
+  grow_t x = (grow_t)(p.scores) + (size_t)row * p.N;
+  const uint32_t q0 = (uint32_t)((uint64_t)part * n_s / p.pp);
+  const uint32_t q1 = (uint32_t)((uint64_t)(part + 1) * n_s / p.pp);
+  uint32_t hot_mask = 0;
+#pragma unroll
+  for (int m = 0; m < LM_PER_THREAD; ++m) {
+    const uint32_t j = q0 + t + (uint32_t)m * BLOCK;
+    if (j < q1 && rs->lmax[j] >= t1key) hot_mask |= 1u << m;
+  }
+  reset_row_state();
+  const bool tail = part == p.pp - 1;
+  if (t1key >= 0x80000000u) {
+    hot_lines<true>(x, L, q0, hot_mask, c);
+    fused_pass_lines<true>(x, L, n_s, 24u * q0, 24u * q1, tail, c);
+  } else {
+    hot_lines<false>(x, L, q0, hot_mask, c);
+    fused_pass_lines<false>(x, L, n_s, 24u * q0, 24u * q1, tail, c);
+  }
+  __syncthreads();
+  // Merge into the row: one atomic reserves this workgroup's candidate range.
+  const uint32_t n = s.cnt;
+  if (t == 0) {
+    s.bcast = n ? atomicAdd(&rs->c1, n) : 0u;
+    if (s.cnt0) atomicAdd(&rs->c0, s.cnt0);
+  }
+  __syncthreads();
+  const uint32_t base = s.bcast;
+  const uint32_t keep = n < (uint32_t)CAP ? n : (uint32_t)CAP;
+  for (uint32_t i = t; i < keep; i += BLOCK) {
+    if (base + i < (uint32_t)CAP) {
+      rs->cand_idx[base + i] = s.buf[i];
+      rs->cand_key[base + i] = s.buf[CAP + i];
+    }
+  }
+  for (uint32_t b = t; b < (uint32_t)NB; b += BLOCK) {
+    const uint32_t h = s.hist[b];
+    if (h) atomicAdd(&rs->hist[b], h);
+  }
+}
+
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
+void split_finish_kernel(Params p) {
+  Smem& s = g_s;
+  const uint32_t t = threadIdx.x, row = blockIdx.x;
+  RowSplitState* rs = p.rs + row;
+  if (t == 0) s.row = (int32_t)row;
+  if (rs->whole) {
+    process_row(p, row);
+  } else {
+    const uint32_t L = row_length(p, row);
+    grow_t x = (grow_t)(p.scores) + (size_t)row * p.N;
+    gout_t out = (gout_t)(p.out) + (size_t)row * p.K;
+    const uint32_t c1 = rs->c1, c0 = rs->c0;
+    const uint32_t t1key = rs->t1key, t0key = rs->t0key;
+    const uint32_t smin = ~rs->mn_inv, smax = rs->mx;
+    if (c1 > (uint32_t)CAP) {
+      if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_OVER);
+      recover_row(p, row, x, L, t1key, smax, out);
+    } else if (c1 < p.K) {
+      if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_UNDER);
+      recover_row(p, row, x, L, smin, t1key, out);
+    } else {
+      if (t == 0) stat_add(p.ctl, c0 >= p.K ? TOPK_STAT_TAU0 : TOPK_STAT_TAU1);
+      reset_row_state();
+      for (uint32_t b = t; b < (uint32_t)NB; b += BLOCK) s.hist[b] = rs->hist[b];
+      for (uint32_t i = t; i < c1; i += BLOCK) {
+        s.buf[i] = rs->cand_idx[i];
+        s.buf[CAP + i] = rs->cand_key[i];
+      }
+      __syncthreads();
+      refine_commit(c1, p.K, pass_ctx(t1key, t0key, smax), out, p.ctl);
+    }
+  }
+  // Rewind the row's state for the next call (every read of it is done).
+  __syncthreads();
+  for (uint32_t b = t; b < (uint32_t)NB; b += BLOCK) rs->hist[b] = 0;
+  if (t == 0) {
+    rs->whole = 0;
+    rs->mn_inv = 0;
+    rs->mx = 0;
+    rs->c1 = 0;
+    rs->c0 = 0;
+  }
+}
+
 __global__ void zero_stats_kernel(Control* ctl) {
   const uint32_t t = threadIdx.x;
   if (t < (uint32_t)TOPK_STAT_COUNT) ctl->stats[t] = 0ull;
@@ -1448,6 +1682,7 @@ struct DevState {
   int occ_rec = 0;      // resident recovery-collect workgroups per CU
   Control* ctl = nullptr;
   RecSlot* rec = nullptr;
+  RowSplitState* rs = nullptr;  // row-split state for RS_MAX_ROWS rows, made on first use
 };
 
 constexpr int MAX_DEVICES = 64;
@@ -1517,6 +1752,24 @@ int get_state(bool capturing, DevState** out) {
   return TOPK_OK;
 }
 
+// Creates the row-split state of a device (not while capturing).
+int ensure_rowsplit(DevState* st) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (st->rs) return TOPK_OK;
+  RowSplitState* rs = nullptr;
+  const size_t bytes = sizeof(RowSplitState) * RS_MAX_ROWS;
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(&rs), bytes);
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc(row-split state)");
+  e = hipMemset(rs, 0, bytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    (void)hipFree(rs);
+    return hip_fail(e, "row-split state initialisation");
+  }
+  st->rs = rs;
+  return TOPK_OK;
+}
+
 int stream_capturing(hipStream_t stream, bool* capturing) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   hipError_t e = hipStreamIsCapturing(stream, &cs);
@@ -1568,21 +1821,62 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
   p.direct_max = DIRECT_MAX_DEFAULT;
   p.mode = g_mode.load();
   p.rec = st->rec;
-  // Persistent execution for many long rows per resident workgroup; one workgroup
-  // per row otherwise (measured on MI355X: equal on 0.5-1M-wide rows, faster on
-  // short rows, where the per-row loop overhead is not amortised).
+  p.rs = nullptr;
+  p.ps = 1;
+  p.pp = 1;
+  // Execution by shape. Row-split when rows are few (at most a quarter of the
+  // resident workgroup slots) and long: their scan and sampling are divided among
+  // several workgroups. Measured on MI355X (512 resident slots), row-split is 4x
+  // faster for 1-32 rows of 1M and 1.1-1.6x at 128 rows, even at 256 rows and
+  // slower at 512, where one workgroup per row already fills the chip and the extra
+  // kernel boundaries and merges cost more than they save. Persistent execution
+  // for many long rows per resident workgroup. One workgroup per row otherwise
+  // (equal to persistent on 0.5-1M-wide rows, faster on short rows, where the
+  // per-row loop overhead is not amortised).
   const int64_t resident = (int64_t)st->occ * st->n_cu;
   const int ex = g_exec.load();
-  const bool persistent = ex == TOPK_EXEC_PERSISTENT ||
-                          (ex == TOPK_EXEC_AUTO && M >= 4 * resident && N_alloc >= 262144);
-  if (persistent) {
-    const unsigned grid = (unsigned)(M < resident ? M : resident);
-    hipLaunchKernelGGL(topk_rows_kernel<true>, dim3(grid), dim3(BLOCK), 0, stream, p);
-  } else {
-    hipLaunchKernelGGL(topk_rows_kernel<false>, dim3((unsigned)M), dim3(BLOCK), 0, stream, p);
+  bool split = M <= (int64_t)RS_MAX_ROWS &&
+               (ex == TOPK_EXEC_ROWSPLIT || p.mode == TOPK_PATH_ROWSPLIT ||
+                (ex == TOPK_EXEC_AUTO && 4 * M <= resident && N_alloc >= ROWSPLIT_MIN_N));
+  if (split && !st->rs) {
+    if (capturing) {
+      split = false;  // no state and no allocation under capture: run unsplit (same result)
+    } else {
+      rc = ensure_rowsplit(st);
+      if (rc != TOPK_OK) return rc;
+    }
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "launch topk_rows_kernel");
+  hipError_t e;
+  if (split) {
+    // Workgroups per row: enough units to keep every resident slot busy several
+    // times over, but no unit smaller than ~256 sampled lines / ~170 periods.
+    const int64_t n_s_max = (N_alloc + STRIDE - 1) / STRIDE;
+    int64_t pp = (4 * resident + M - 1) / M, ps = (2 * resident + M - 1) / M;
+    pp = pp < 1 ? 1 : (pp > 16 ? 16 : pp);
+    ps = ps < 1 ? 1 : (ps > 16 ? 16 : ps);
+    const int64_t pp_cap = n_s_max / 170 > 1 ? n_s_max / 170 : 1;
+    const int64_t ps_cap = n_s_max / 256 > 1 ? n_s_max / 256 : 1;
+    p.pp = (uint32_t)(pp < pp_cap ? pp : pp_cap);
+    p.ps = (uint32_t)(ps < ps_cap ? ps : ps_cap);
+    p.rs = st->rs;
+    hipLaunchKernelGGL(split_sample_kernel, dim3(p.ps, (unsigned)M), dim3(BLOCK), 0, stream, p);
+    hipLaunchKernelGGL(split_select_kernel, dim3((unsigned)M), dim3(BLOCK), 0, stream, p);
+    hipLaunchKernelGGL(split_pass_kernel, dim3(p.pp, (unsigned)M), dim3(BLOCK), 0, stream, p);
+    hipLaunchKernelGGL(split_finish_kernel, dim3((unsigned)M), dim3(BLOCK), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "launch row-split kernels");
+  } else {
+    const bool persistent = ex == TOPK_EXEC_PERSISTENT ||
+                            (ex == TOPK_EXEC_AUTO && M >= 4 * resident && N_alloc >= 262144);
+    if (persistent) {
+      const unsigned grid = (unsigned)(M < resident ? M : resident);
+      hipLaunchKernelGGL(topk_rows_kernel<true>, dim3(grid), dim3(BLOCK), 0, stream, p);
+    } else {
+      hipLaunchKernelGGL(topk_rows_kernel<false>, dim3((unsigned)M), dim3(BLOCK), 0, stream, p);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "launch topk_rows_kernel");
+  }
   // Exact recovery of the rows the selector queued (both exit at once if none).
   hipLaunchKernelGGL(recovery_hist_kernel, dim3(st->n_cu * 4), dim3(BLOCK), 0, stream, p);
   e = hipGetLastError();
@@ -1603,7 +1897,11 @@ int topk_exact_reserve(int64_t M_max, int64_t N_alloc_max, int32_t K) {
     return fail(TOPK_ERR_BAD_SHAPE, "bad reserve shape");
   if (K < 1 || K > TOPK_K_MAX) return fail(TOPK_ERR_BAD_K, "K = %d outside [1, %d]", K, TOPK_K_MAX);
   DevState* st = nullptr;
-  return get_state(false, &st);
+  int rc = get_state(false, &st);
+  if (rc != TOPK_OK) return rc;
+  // Row-split may be chosen for calls of at most RS_MAX_ROWS rows: create its state now.
+  if (M_max <= (int64_t)RS_MAX_ROWS) return ensure_rowsplit(st);
+  return TOPK_OK;
 }
 
 int topk_exact_get_stats(uint64_t* host_counts, int n, hipStream_t stream) {
@@ -1650,7 +1948,7 @@ int topk_exact_set_path_override(int mode) {
 
 int topk_exact_set_execution(int mode) {
   g_err[0] = '\0';
-  if (mode < TOPK_EXEC_AUTO || mode > TOPK_EXEC_ROW_PER_WG)
+  if (mode < TOPK_EXEC_AUTO || mode > TOPK_EXEC_ROWSPLIT)
     return fail(TOPK_ERR_BAD_ARG, "execution mode %d unknown", mode);
   g_exec.store(mode);
   return TOPK_OK;

@@ -61,7 +61,8 @@ typedef enum {
 /* Path override modes (test and benchmark use; default TOPK_PATH_AUTO). */
 #define TOPK_PATH_AUTO 0      /* per-row choice: sentinel, direct-exact or sampled */
 #define TOPK_PATH_SAMPLED 1   /* every row with L > K takes the sampled path */
-#define TOPK_PATH_ROWSPLIT 2  /* every row with L > K takes the row-split sampled path */
+#define TOPK_PATH_ROWSPLIT 2  /* every row with L > K takes the sampled path, split over
+                                 several workgroups (calls of at most 1024 rows) */
 #define TOPK_PATH_DIRECT 3    /* every row with L > K takes the direct exact path */
 #define TOPK_PATH_RECOVERY 4  /* every row with L > K takes exact full-row recovery */
 
@@ -69,6 +70,7 @@ typedef enum {
 #define TOPK_EXEC_AUTO 0        /* shape-based choice below */
 #define TOPK_EXEC_PERSISTENT 1  /* resident workgroups loop over rows via a device ticket */
 #define TOPK_EXEC_ROW_PER_WG 2  /* one workgroup per row, balanced by the hardware dispatcher */
+#define TOPK_EXEC_ROWSPLIT 3    /* several workgroups per row (calls of at most 1024 rows) */
 
 /* Statistics slots returned by topk_exact_get_stats (row counts since the last reset). */
 enum {
@@ -107,9 +109,9 @@ enum {
 int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc,
                int32_t K, int32_t* out_idx, int32_t sentinel, hipStream_t stream);
 
-/* Creates the current device's workspace sized for calls up to (M_max, N_alloc_max, K)
- * and resolves launch parameters. Synchronous; call it outside stream capture before
- * capturing topk_exact. Calls with larger sizes grow the workspace when not capturing. */
+/* Creates the current device's workspace (control block, recovery queue and, when
+ * M_max <= 1024, the row-split state) and resolves launch parameters. Synchronous;
+ * call it outside stream capture before capturing topk_exact. */
 int topk_exact_reserve(int64_t M_max, int64_t N_alloc_max, int32_t K);
 
 /* Copies up to n (<= TOPK_STAT_COUNT) statistics counters of the current device into
@@ -124,9 +126,14 @@ int topk_exact_reset_stats(hipStream_t stream);
 int topk_exact_set_path_override(int mode);
 
 /* Selects how rows map to workgroups for later calls (TOPK_EXEC_*). Auto uses
+ * row-split when M is at most a quarter of the resident workgroup count and
+ * N_alloc >= 65536,
  * persistent execution when M is at least four times the resident workgroup count
- * and N_alloc >= 262144, one workgroup per row otherwise. Both give identical
- * results; a captured graph keeps the mode set when it was captured. Process-wide. */
+ * and N_alloc >= 262144, and one workgroup per row otherwise. Every mode gives a
+ * result satisfying the same contract; a captured graph keeps the mode set when it
+ * was captured. Row-split needs per-row state for up to 1024 rows (~140 MB), made by
+ * topk_exact_reserve(M_max <= 1024, ...) or by the first call that uses it; a call
+ * under capture without that state runs unsplit. Process-wide. */
 int topk_exact_set_execution(int mode);
 
 /* Text of the last error raised on this host thread ("" if none). */

@@ -61,8 +61,9 @@ def test_argument_validation_without_gpu():
 def test_execution_mode_roundtrip():
     L = tk.lib()
     assert L.topk_exact_set_execution(7) == B.TOPK_ERR_BAD_ARG
+    assert L.topk_exact_set_execution(4) == B.TOPK_ERR_BAD_ARG
     assert L.topk_exact_set_execution(-1) == B.TOPK_ERR_BAD_ARG
-    for mode in (B.EXEC_PERSISTENT, B.EXEC_ROW_PER_WG, B.EXEC_AUTO):
+    for mode in (B.EXEC_PERSISTENT, B.EXEC_ROW_PER_WG, B.EXEC_ROWSPLIT, B.EXEC_AUTO):
         tk.set_execution(mode)
 
 

@@ -168,7 +168,7 @@ def test_sentinel_lengths():
         assert torch.all(o[0] == sentinel) and o[1, 0] == 0 and torch.all(o[1, 1:] == sentinel)
 
 
-@pytest.mark.parametrize("mode", [tk.PATH_SAMPLED, tk.PATH_DIRECT, tk.PATH_RECOVERY])
+@pytest.mark.parametrize("mode", [tk.PATH_SAMPLED, tk.PATH_DIRECT, tk.PATH_RECOVERY, tk.PATH_ROWSPLIT])
 def test_forced_modes_on_short_and_long_rows(mode):
     s0, l0 = W.make_window(W.get("c0"), DEV)
     out, st = _run(s0, l0, mode=mode)
@@ -267,7 +267,7 @@ def test_other_k(Ksmall):
         _check(ss, ll, out, K=Ksmall, label=f"K={Ksmall}")
 
 
-@pytest.mark.parametrize("execution", [tk.EXEC_PERSISTENT, tk.EXEC_ROW_PER_WG])
+@pytest.mark.parametrize("execution", [tk.EXEC_PERSISTENT, tk.EXEC_ROW_PER_WG, tk.EXEC_ROWSPLIT])
 def test_execution_modes_agree_with_oracle(execution):
     # Both row-to-workgroup mappings on short, medium and long rows, with recovery rows.
     cases = [W.make_window(W.get("c0"), DEV), _window_rows("c1", [(0, 12), (8000, 12)]),
@@ -279,6 +279,34 @@ def test_execution_modes_agree_with_oracle(execution):
         for s, l in cases:
             out, st = _run(s, l)
             _check(s, l, out, label=f"execution {execution} shape {tuple(s.shape)}")
+
+
+def test_rowsplit_merges_segments():
+    # Row-split on long rows (several workgroups per row), with a forced underfill
+    # row, an overflow row with a negative threshold, a long unaligned row and a
+    # short row taken whole; the stats prove the split kernels ran.
+    L = 131072
+    rows = [_adversarial_row(L, 1000, 90), _adversarial_row(L, 2030, 91)]
+    ovf = np.full(L, 50.0, dtype=np.float32)
+    ovf[_sample_positions(L)] = -1000.0
+    rows.append(ovf)
+    s1, l1 = _window_rows("c1", [(3, 4)])
+    s = torch.cat([torch.from_numpy(np.stack(rows)).to(DEV), s1]).contiguous()
+    l = torch.cat([torch.full((3,), L, dtype=torch.int32, device=DEV), l1]).contiguous()
+    l[4] = 5000  # short row: direct path, taken whole
+    with tk.execution(tk.EXEC_ROWSPLIT):
+        out, st = _run(s, l)
+    _check(s, l, out, label="row-split mix")
+    assert st["rowsplit"] == 6 and st["direct"] == 1
+    assert st["recover_under"] >= 1 and st["recover_over"] >= 1 and st["tau1"] >= 1
+    s3, l3 = _window_rows("c3b", [(0, 4)])
+    for n_alloc in (1048576, 1048575):
+        ss = s3[:, :n_alloc].contiguous()
+        ll = l3.clamp(max=n_alloc).contiguous()
+        with tk.execution(tk.EXEC_ROWSPLIT):
+            out, st = _run(ss, ll)
+        _check(ss, ll, out, label=f"row-split 1M n_alloc={n_alloc}")
+        assert st["rowsplit"] == 4
 
 
 def test_consecutive_calls_reuse_the_ticket():
@@ -344,3 +372,14 @@ def test_full_size_c2_sampled_rows():
 
 def test_full_size_c3a_sampled_rows():
     _full_size_sampled_rows("c3a", 15, [0, 255, 511])
+
+
+def test_full_size_few_long_rows_take_rowsplit():
+    # 64 rows of the 1M causal window: auto dispatch splits each row over several
+    # workgroups (few rows per resident slot); sampled rows against the oracle.
+    w = W.get("c3a")
+    s, l = W.make_window(w, DEV, row_start=8192 - 64, n_rows=64)
+    out, st = _run(s, l)
+    assert st["rows"] == 64 and st["rowsplit"] == 64
+    idx = torch.tensor([0, 31, 63], device=DEV)
+    _check(s[idx], l[idx], out[idx], label="1M x 64 rows, row-split")
