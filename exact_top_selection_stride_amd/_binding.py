@@ -45,7 +45,7 @@ STAT_COUNT = 16
 EXPORTED = (
     "topk_exact", "topk_exact_reserve", "topk_exact_get_stats", "topk_exact_reset_stats",
     "topk_exact_set_path_override", "topk_exact_last_error", "topk_stream_read_probe",
-    "topk_exact_set_execution",
+    "topk_exact_set_execution", "topk_exact_time_next_call",
 )
 
 
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.topk_exact_set_path_override.argtypes = [ctypes.c_int]
         L.topk_exact_set_execution.restype = ctypes.c_int
         L.topk_exact_set_execution.argtypes = [ctypes.c_int]
+        L.topk_exact_time_next_call.restype = ctypes.c_int
+        L.topk_exact_time_next_call.argtypes = [vp, vp]
         L.topk_exact_last_error.restype = ctypes.c_char_p
         L.topk_exact_last_error.argtypes = []
         L.topk_stream_read_probe.restype = ctypes.c_int
@@ -177,6 +179,22 @@ def execution(mode: int):
         yield
     finally:
         set_execution(EXEC_AUTO)
+
+
+def time_next_call(start, stop):
+    """Arms the one-shot selector timing of the next topk_exact call on this thread.
+
+    start/stop: torch.cuda.Event(enable_timing=True) that have been recorded at least
+    once (so the HIP events exist), or None for both to disarm. After the timed call
+    completes, start.elapsed_time(stop) is the selector kernels' time in ms.
+    """
+    if (start is None) != (stop is None):
+        raise ValueError("start and stop must both be events or both be None")
+    h0 = start.cuda_event if start is not None else 0
+    h1 = stop.cuda_event if stop is not None else 0
+    if start is not None and (not h0 or not h1):
+        raise ValueError("record both events once before arming the hook")
+    _check(lib().topk_exact_time_next_call(h0 or None, h1 or None), "topk_exact_time_next_call")
 
 
 def stream_read_probe(x: torch.Tensor, sink: torch.Tensor, stream=None):

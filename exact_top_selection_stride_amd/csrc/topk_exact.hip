@@ -1770,6 +1770,9 @@ int ensure_rowsplit(DevState* st) {
   return TOPK_OK;
 }
 
+// One-shot selector timing for the next call on this host thread.
+thread_local hipEvent_t g_time_start = nullptr, g_time_stop = nullptr;
+
 int stream_capturing(hipStream_t stream, bool* capturing) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   hipError_t e = hipStreamIsCapturing(stream, &cs);
@@ -1847,6 +1850,14 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
     }
   }
   hipError_t e;
+  hipEvent_t ev_start = nullptr, ev_stop = nullptr;
+  if (!capturing && g_time_start) {
+    ev_start = g_time_start;
+    ev_stop = g_time_stop;
+    g_time_start = g_time_stop = nullptr;
+    e = hipEventRecord(ev_start, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(start)");
+  }
   if (split) {
     // Workgroups per row: enough units to keep every resident slot busy several
     // times over, but no unit smaller than ~256 sampled lines / ~170 periods.
@@ -1877,7 +1888,11 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "launch topk_rows_kernel");
   }
-  // Exact recovery of the rows the selector queued (both exit at once if none).
+  if (ev_stop) {
+    e = hipEventRecord(ev_stop, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(stop)");
+  }
+  // Exact recovery of the rows the selector queued (they exit at once if none).
   hipLaunchKernelGGL(recovery_hist_kernel, dim3(st->n_cu * 4), dim3(BLOCK), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch recovery_hist_kernel");
@@ -1951,6 +1966,15 @@ int topk_exact_set_execution(int mode) {
   if (mode < TOPK_EXEC_AUTO || mode > TOPK_EXEC_ROWSPLIT)
     return fail(TOPK_ERR_BAD_ARG, "execution mode %d unknown", mode);
   g_exec.store(mode);
+  return TOPK_OK;
+}
+
+int topk_exact_time_next_call(hipEvent_t start, hipEvent_t stop) {
+  g_err[0] = '\0';
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(TOPK_ERR_NULL_POINTER, "start and stop must both be set or both be null");
+  g_time_start = start;
+  g_time_stop = stop;
   return TOPK_OK;
 }
 

@@ -136,6 +136,16 @@ int topk_exact_set_path_override(int mode);
  * under capture without that state runs unsplit. Process-wide. */
 int topk_exact_set_execution(int mode);
 
+/* Measurement hook: arms a one-shot timing of the next topk_exact call made on this
+ * host thread. That call records `start` on its stream just before its first
+ * selector kernel and `stop` just after its last one, before the exact-recovery
+ * kernels, so hipEventElapsedTime(start, stop) is the selector kernels' device time.
+ * The events belong to the caller, were created on the current device with timing
+ * enabled, and must stay alive until they have completed. A call under stream capture
+ * records nothing and leaves the hook armed; (NULL, NULL) disarms it. Returns
+ * TOPK_ERR_NULL_POINTER if exactly one event is NULL. */
+int topk_exact_time_next_call(hipEvent_t start, hipEvent_t stop);
+
 /* Text of the last error raised on this host thread ("" if none). */
 const char* topk_exact_last_error(void);
 

@@ -56,6 +56,10 @@ def test_argument_validation_without_gpu():
     assert L.topk_exact_reserve(1, 10, 0) == B.TOPK_ERR_BAD_K
     assert L.topk_stream_read_probe(None, -1, None, None) == B.TOPK_ERR_BAD_SHAPE
     assert L.topk_stream_read_probe(None, 0, None, None) == B.TOPK_OK
+    # The timing hook takes both events or neither; (NULL, NULL) disarms it.
+    assert L.topk_exact_time_next_call(fake, None) == B.TOPK_ERR_NULL_POINTER
+    assert L.topk_exact_time_next_call(None, fake) == B.TOPK_ERR_NULL_POINTER
+    assert L.topk_exact_time_next_call(None, None) == B.TOPK_OK
 
 
 def test_execution_mode_roundtrip():

@@ -319,6 +319,26 @@ def test_consecutive_calls_reuse_the_ticket():
             _check(s[:M], l[:M], out, label=f"M={M}")
 
 
+def test_selector_timing_hook():
+    # The hook's events bracket the selector kernels inside the call's own events.
+    s, l = _window_rows("c1", [(0, 64)])
+    stream = torch.cuda.Stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    with torch.cuda.stream(stream):
+        for e in ev:
+            e.record(stream)
+        torch.cuda.synchronize()
+        tk.time_next_call(ev[1], ev[2])
+        ev[0].record(stream)
+        out = tk.topk_exact(s, l, K=K)
+        ev[3].record(stream)
+    torch.cuda.synchronize()
+    _check(s, l, out, label="timed call")
+    inner, outer = ev[1].elapsed_time(ev[2]), ev[0].elapsed_time(ev[3])
+    assert 0.0 < inner <= outer
+    assert ev[0].elapsed_time(ev[1]) >= 0.0 and ev[2].elapsed_time(ev[3]) >= 0.0
+
+
 def test_graph_replay():
     s, l = _window_rows("c1", [(0, 12)])
     s0, l0 = W.make_window(W.get("c0"), DEV)
