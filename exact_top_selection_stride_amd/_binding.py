@@ -23,7 +23,7 @@ TOPK_ERR_BAD_SENTINEL = 4
 TOPK_ERR_WORKSPACE = 5
 TOPK_ERR_HIP = 6
 TOPK_ERR_BAD_ARG = 7
-TOPK_K_MAX = 2048
+TOPK_K_MAX = 4096
 
 PATH_AUTO = 0
 PATH_SAMPLED = 1

@@ -82,6 +82,9 @@ constexpr int64_t ROWSPLIT_MIN_N = 65536;  // auto row-split only for rows at le
 constexpr uint32_t KEY_MAX = 0xFFFFFFFFu;
 
 static_assert(NB % BLOCK == 0, "bins per thread must be integral");
+// K = 2048 is the operating point of the method; larger K (up to TOPK_K_MAX) keeps
+// the same targets, so tau1 admits about 1.75 K of the CAP slots and the rows whose
+// candidates overflow them take exact recovery.
 static_assert(TOPK_K_MAX * 7 / 4 + 1 <= CAP, "candidate buffer must hold the tau1 target");
 static_assert(FL_CAP <= BLOCK, "frontier lists are ranked one element per thread");
 

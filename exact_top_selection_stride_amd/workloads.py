@@ -67,6 +67,16 @@ for _n in C4_WIDTHS:
     for _m in C4_ROWS:
         WORKLOADS[f"c4_n{_n}_m{_m}"] = _c4(_n, _m)
 
+# Decode-shaped calls: a few long rows (the first M rows of the causal window,
+# lengths N - 8191 onwards) at 128K and 1M widths, with the C1/C3 value recipe.
+DECODE_ROWS = (1, 4, 16, 64)
+DECODE_WIDTHS = (131072, 1048576)
+for _n in DECODE_WIDTHS:
+    for _m in DECODE_ROWS:
+        WORKLOADS[f"dec_n{_n}_m{_m}"] = Workload(
+            f"dec_n{_n}_m{_m}", _n, _m, 1, 0.01, "causal", seed=BASE_SEED + 5,
+            note="decode shape: few long rows, row-split execution")
+
 
 def get(name: str) -> Workload:
     try:

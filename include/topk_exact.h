@@ -56,7 +56,7 @@ typedef enum {
   TOPK_ERR_BAD_ARG = 7       /* another argument is out of range (stats/override calls) */
 } topk_status_t;
 
-#define TOPK_K_MAX 2048
+#define TOPK_K_MAX 4096
 
 /* Path override modes (test and benchmark use; default TOPK_PATH_AUTO). */
 #define TOPK_PATH_AUTO 0      /* per-row choice: sentinel, direct-exact or sampled */

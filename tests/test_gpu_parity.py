@@ -258,7 +258,7 @@ def test_value_edge_cases(kind):
         _check(s, l, out, label=f"{kind} mode {mode}")
 
 
-@pytest.mark.parametrize("Ksmall", [1, 7, 64, 1000, 2047])
+@pytest.mark.parametrize("Ksmall", [1, 7, 64, 1000, 2047, 3000, 4096])
 def test_other_k(Ksmall):
     s, l = _window_rows("c1", [(0, 4)])
     s0, l0 = W.make_window(W.get("c0"), DEV)
@@ -392,6 +392,29 @@ def test_full_size_c2_sampled_rows():
 
 def test_full_size_c3a_sampled_rows():
     _full_size_sampled_rows("c3a", 15, [0, 255, 511])
+
+
+@pytest.mark.parametrize("name", [f"dec_n{n}_m{m}" for n in W.DECODE_WIDTHS for m in W.DECODE_ROWS])
+def test_decode_shapes(name):
+    # Few long rows: auto dispatch splits each row over several workgroups; every row
+    # is checked against the oracle.
+    w = W.get(name)
+    s, l = W.make_window(w, DEV)
+    out, st = _run(s, l)
+    _check(s, l, out, label=name)
+    assert st["rows"] == w.M and st["rowsplit"] == w.M
+
+
+@pytest.mark.parametrize("K4", [4096])
+def test_large_k_on_long_rows(K4):
+    # K = 4096 on 1M rows in persistent and row-split execution: tau1 admits about
+    # 1.75 K, so some rows overflow the candidate buffer and are recovered exactly.
+    s, l = _window_rows("c3b", [(0, 4), (6000, 4)])
+    for ex in (tk.EXEC_PERSISTENT, tk.EXEC_ROWSPLIT):
+        with tk.execution(ex):
+            out, st = _run(s, l, K=K4)
+        _check(s, l, out, K=K4, label=f"K={K4} execution {ex}")
+        assert st["rows"] == 8
 
 
 def test_full_size_few_long_rows_take_rowsplit():
