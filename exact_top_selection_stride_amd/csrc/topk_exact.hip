@@ -1152,6 +1152,8 @@ void topk_rows_kernel(Params p) {
 // order the three steps, so no cross-workgroup fences are needed. All three exit
 // at once when the queue is empty; the finish kernel's last workgroup rewinds it.
 
+constexpr int REC_CHUNKS = REC_SEG / 4 / BLOCK + 1;  // 16-byte chunks per thread per item
+
 struct RecHistSmem {
   uint32_t hist[NB];
 };
@@ -1172,14 +1174,35 @@ __global__ __launch_bounds__(BLOCK) void recovery_hist_kernel(Params p) {
     const uint32_t n = min(REC_SEG, L - begin);
     const uint32_t lo = r->lo, hi = r->hi;
     const uint32_t sh = shift_for(hi - lo);
+    // The whole item is loaded at once (one memory latency per item): offsets are in
+    // floats from the 16-byte chunk holding x[0]; chunks past the item read its last
+    // chunk and their elements are masked.
+    grow_t x = (grow_t)(p.scores) + (size_t)r->row * p.N + begin;
+    const uint32_t off = (uint32_t)((uintptr_t)x & 15u) >> 2;
+    grow_t ab = x - off;
+    const uint32_t glast = (off + n - 1u) & ~3u;
+    u32x4 v[REC_CHUNKS];
+#pragma unroll
+    for (int u = 0; u < REC_CHUNKS; ++u) {
+      const uint32_t g = 4u * (t + (uint32_t)u * BLOCK);
+      v[u] = load4(ab + (g < glast ? g : glast));
+    }
     for (uint32_t i = t; i < (uint32_t)NB; i += BLOCK) g_rh.hist[i] = 0;
     __syncthreads();
-    grow_t x = (grow_t)(p.scores) + (size_t)r->row * p.N + begin;
-    for_each_element(x, n, [&](uint32_t u, uint32_t) {
-      const uint32_t k = key_of_bits(u);
-      const uint32_t d = k < lo ? 0u : (k - lo) >> sh;
-      atomicAdd(&g_rh.hist[d < (uint32_t)(NB - 1) ? d : (uint32_t)(NB - 1)], 1u);
-    });
+#pragma unroll
+    for (int u = 0; u < REC_CHUNKS; ++u) {
+      const uint32_t g = 4u * (t + (uint32_t)u * BLOCK);
+      const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t o = g + i;
+        if (o >= off && o < off + n) {
+          const uint32_t k = key_of_bits(w4[i]);
+          const uint32_t d = k < lo ? 0u : (k - lo) >> sh;
+          atomicAdd(&g_rh.hist[d < (uint32_t)(NB - 1) ? d : (uint32_t)(NB - 1)], 1u);
+        }
+      }
+    }
     __syncthreads();
     for (uint32_t i = t; i < (uint32_t)NB; i += BLOCK) {
       const uint32_t c = g_rh.hist[i];
@@ -1198,7 +1221,6 @@ struct RecCollectSmem {
   uint32_t base_gt, base_bin;
 };
 
-constexpr int REC_CHUNKS = REC_SEG / 4 / BLOCK + 1;  // 16-byte chunks per thread per item
 __shared__ RecCollectSmem g_rc;
 
 __global__ __launch_bounds__(BLOCK) void recovery_collect_kernel(Params p) {
@@ -1215,6 +1237,21 @@ __global__ __launch_bounds__(BLOCK) void recovery_collect_kernel(Params p) {
     const uint32_t L = r->L;
     if (begin >= L) continue;
     const uint32_t n = min(REC_SEG, L - begin);
+    // The item stays in registers; its loads are issued first so that they overlap
+    // the boundary-bin search below. Then this thread's keys above the bin and in
+    // the bin are counted, the item's output and candidate slots are reserved with
+    // one atomic each, and written. Offsets are in floats from the 16-byte chunk
+    // holding x[0].
+    grow_t x = (grow_t)(p.scores) + (size_t)r->row * p.N + begin;
+    const uint32_t off = (uint32_t)((uintptr_t)x & 15u) >> 2;
+    grow_t ab = x - off;
+    const uint32_t glast = (off + n - 1u) & ~3u;
+    u32x4 v[REC_CHUNKS];
+#pragma unroll
+    for (int u = 0; u < REC_CHUNKS; ++u) {
+      const uint32_t g = 4u * (t + (uint32_t)u * BLOCK);
+      v[u] = load4(ab + (g < glast ? g : glast));
+    }
     // The boundary bin, from the completed histogram (every item derives the same).
     uint32_t h[NB / BLOCK];
     uint32_t sum = 0;
@@ -1270,20 +1307,7 @@ __global__ __launch_bounds__(BLOCK) void recovery_collect_kernel(Params p) {
       r->bin_lo = blo;
       r->bin_hi = bhi;
     }
-    grow_t x = (grow_t)(p.scores) + (size_t)r->row * p.N + begin;
     gout_t out = (gout_t)(p.out) + (size_t)r->row * K;
-    // The item stays in registers: count this thread's keys above the bin and in the
-    // bin, reserve the item's output and candidate slots with one atomic each, then
-    // write. Offsets are in floats from the 16-byte chunk holding x[0].
-    const uint32_t off = (uint32_t)((uintptr_t)x & 15u) >> 2;
-    grow_t ab = x - off;
-    const uint32_t glast = (off + n - 1u) & ~3u;
-    u32x4 v[REC_CHUNKS];
-#pragma unroll
-    for (int u = 0; u < REC_CHUNKS; ++u) {
-      const uint32_t g = 4u * (t + (uint32_t)u * BLOCK);
-      v[u] = load4(ab + (g < glast ? g : glast));
-    }
     uint32_t na = 0, nb = 0;
 #pragma unroll
     for (int u = 0; u < REC_CHUNKS; ++u) {
