@@ -45,7 +45,7 @@ STAT_COUNT = 16
 EXPORTED = (
     "topk_exact", "topk_exact_reserve", "topk_exact_get_stats", "topk_exact_reset_stats",
     "topk_exact_set_path_override", "topk_exact_last_error", "topk_stream_read_probe",
-    "topk_exact_set_execution", "topk_exact_time_next_call",
+    "topk_exact_set_execution", "topk_exact_time_next_call", "topk_exact_set_proposal",
 )
 
 
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.topk_exact_set_path_override.argtypes = [ctypes.c_int]
         L.topk_exact_set_execution.restype = ctypes.c_int
         L.topk_exact_set_execution.argtypes = [ctypes.c_int]
+        L.topk_exact_set_proposal.restype = ctypes.c_int
+        L.topk_exact_set_proposal.argtypes = [i32, i32, i32]
         L.topk_exact_time_next_call.restype = ctypes.c_int
         L.topk_exact_time_next_call.argtypes = [vp, vp]
         L.topk_exact_last_error.restype = ctypes.c_char_p
@@ -179,6 +181,22 @@ def execution(mode: int):
         yield
     finally:
         set_execution(EXEC_AUTO)
+
+
+def set_proposal(stride: int = 128, rho0: float = 1.5, rho1: float = 1.75):
+    """Sample stride and candidate targets (rho0*K, rho1*K) for later calls; the method's
+    values are the defaults. Any setting gives an exact result."""
+    _check(lib().topk_exact_set_proposal(int(stride), int(round(rho0 * 1000)), int(round(rho1 * 1000))),
+           "topk_exact_set_proposal")
+
+
+@contextlib.contextmanager
+def proposal(stride: int = 128, rho0: float = 1.5, rho1: float = 1.75):
+    set_proposal(stride, rho0, rho1)
+    try:
+        yield
+    finally:
+        _check(lib().topk_exact_set_proposal(0, 0, 0), "topk_exact_set_proposal")
 
 
 def time_next_call(start, stop):

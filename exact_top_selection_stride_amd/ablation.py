@@ -1,0 +1,100 @@
+"""Ablation harness for the proposal mechanism on MI355X.
+
+Sweeps the sample stride s and the primary target rho0 (secondary rho1 = rho0 + 0.25)
+of the sampled path, and the direct exact proposal, over the short-row widths where
+the pages place the crossover between sampled and exact proposals (page
+"几何平均快 1.55 倍，但短行采样会输：腾讯怎么测精确 Top-K", section
+"采样不是处处都该开": stride and target ablations, sampled against exact proposal at
+16K to 64K). Every setting gives the same exact result; what changes is the time per
+call and how often each certification path is taken, which is what the sweep prints.
+
+    python -m exact_top_selection_stride_amd.ablation [--widths 16384 32768 65536]
+           [--rows 4096] [--strides 16 32 64 128 256] [--rho0 1 1.25 1.5 1.75] [--steps 20]
+
+One JSON line per setting: workload, mode, stride, rho0, rho1, median call time over
+graph replays, rows/s and the path rates from the device counters of the first calls.
+Inputs are the bf16-rounded causal C4 windows of `workloads.py`.
+"""
+import argparse
+import json
+import statistics
+import sys
+
+import torch
+
+from . import _binding as tk
+from . import workloads as W
+
+
+def _time_call(groups, outs, K, steps, stream):
+    graphs = []
+    with torch.cuda.stream(stream):
+        for g, (s, l) in enumerate(groups):
+            tk.topk_exact(s, l, K=K, out=outs[g], stream=stream)  # outside capture first
+        torch.cuda.synchronize()
+        for g, (s, l) in enumerate(groups):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=stream):
+                tk.topk_exact(s, l, K=K, out=outs[g], stream=stream)
+            graphs.append(gr)
+    torch.cuda.synchronize()
+    ev = []
+    with torch.cuda.stream(stream):
+        for i in range(steps + 4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            graphs[i % len(graphs)].replay()
+            e1.record(stream)
+            if i >= 4:
+                ev.append((e0, e1))
+    torch.cuda.synchronize()
+    return statistics.median(a.elapsed_time(b) for a, b in ev)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--widths", type=int, nargs="+", default=list(W.C4_WIDTHS))
+    ap.add_argument("--rows", type=int, default=4096)
+    ap.add_argument("--strides", type=int, nargs="+", default=[16, 32, 64, 128, 256])
+    ap.add_argument("--rho0", type=float, nargs="+", default=[1.0, 1.25, 1.5, 1.75])
+    ap.add_argument("--steps", type=int, default=20)
+    args = ap.parse_args(argv)
+    if not torch.cuda.is_available():
+        print("the ablation harness needs a GPU", file=sys.stderr)
+        return 2
+    K = 2048
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.Stream(device=dev)
+    for n in args.widths:
+        w = W.get(f"c4_n{n}_m{args.rows}")
+        window, lengths = W.make_window(w, dev)
+        groups = [(window[g * w.M:(g + 1) * w.M], lengths[g * w.M:(g + 1) * w.M].contiguous())
+                  for g in range(w.groups)]
+        outs = [torch.empty((w.M, K), dtype=torch.int32, device=dev) for _ in groups]
+        tk.reserve(w.M, w.n_alloc, K)
+        settings = [("direct", 128, 1.5, 1.75)]
+        settings += [("sampled", s, r, r + 0.25) for s in args.strides for r in args.rho0]
+        for mode, stride, rho0, rho1 in settings:
+            path = tk.PATH_DIRECT if mode == "direct" else tk.PATH_SAMPLED
+            with tk.path_override(path), tk.proposal(stride, rho0, rho1):
+                tk.reset_stats()
+                for g, (s, l) in enumerate(groups):
+                    tk.topk_exact(s, l, K=K, out=outs[g])
+                torch.cuda.synchronize()
+                st = tk.get_stats()
+                ms = _time_call(groups, outs, K, args.steps, stream)
+            rows = max(st["rows"], 1)
+            print(json.dumps({
+                "workload": w.name, "mode": mode, "stride": stride, "rho0": rho0, "rho1": rho1,
+                "median_call_ms": round(ms, 5), "rows_per_s": round(w.M / ms * 1e3),
+                "tau0_rate": st["tau0"] / rows, "tau1_rate": st["tau1"] / rows,
+                "recovery_rate": (st["recover_under"] + st["recover_over"]) / rows,
+                "long_exact_rate": st["long_exact"] / rows,
+            }), flush=True)
+        del window, lengths, groups, outs
+        torch.cuda.empty_cache()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

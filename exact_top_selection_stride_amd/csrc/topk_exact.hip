@@ -124,8 +124,10 @@ struct Params {
   uint32_t N;
   uint32_t K;
   int32_t sentinel;
-  uint32_t T0;          // primary candidate target, ceil(1.5 K)
-  uint32_t T1;          // secondary candidate target, ceil(1.75 K)
+  uint32_t T0;          // primary candidate target, ceil(1.5 K) by default
+  uint32_t T1;          // secondary candidate target, ceil(1.75 K) by default
+  uint32_t stride;      // sample stride s, 128 by default
+  uint32_t line_min;    // sampled rows with at least this many sample lines use line sampling
   uint32_t direct_max;  // auto mode: rows up to this length take the direct path
   int32_t mode;
   RecSlot* rec;         // QMAX recovery slots
@@ -1002,22 +1004,26 @@ __device__ __forceinline__ uint32_t sample_rank(uint32_t target, uint32_t n_s, u
 __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_t x, uint32_t L, gout_t out) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
-  const uint32_t n_s = (L + STRIDE - 1) / STRIDE;
+  const uint32_t n_s = (L + p.stride - 1) / p.stride;
   if (n_s > (uint32_t)KEYS_CAP) {
     if (t == 0) stat_add(p.ctl, TOPK_STAT_LONG_EXACT);
     exact_full_row(x, L, p.K, 0u, KEY_MAX, out, p.ctl);
     return;
   }
   if (t == 0) stat_add(p.ctl, TOPK_STAT_SAMPLED);
-  // Fixed-stride row-local view: keys of x[j * 128], j < ceil(L / 128), in s.buf[0, n_s).
-  const bool by_lines = n_s <= LINE_SAMPLE_MAX;
+  // Fixed-stride row-local view: keys of x[j * s], j < ceil(L / s), in s.buf[0, n_s).
+  // Line-granular sampling (and the line skipping it enables) holds at the method's
+  // stride of 128 and is used where it pays (p.line_min, chosen by shape on the host);
+  // otherwise, and for other strides, the sample is read element by element and the
+  // full pass reads the whole row.
+  const bool by_lines = p.stride == STRIDE && n_s <= LINE_SAMPLE_MAX && n_s >= p.line_min;
   if (by_lines) {
     sample_lines(x, L, n_s, &s.buf[0], &s.buf[CAP]);
   } else {
     uint32_t mn = KEY_MAX, mx = 0;
 #pragma unroll 8
     for (uint32_t j = t; j < n_s; j += BLOCK) {
-      const uint32_t k = key_of_bits(x[(size_t)j * STRIDE]);
+      const uint32_t k = key_of_bits(x[(size_t)j * p.stride]);
       s.buf[j] = k;
       mn = min(mn, k);
       mx = max(mx, k);
@@ -1492,6 +1498,7 @@ __device__ __forceinline__ bool split_applies(const Params& p, uint32_t L) {
   if (L <= p.K) return false;
   if (p.mode == TOPK_PATH_DIRECT || p.mode == TOPK_PATH_RECOVERY) return false;
   if (p.mode == TOPK_PATH_AUTO && L <= p.direct_max) return false;
+  if (p.stride != STRIDE) return false;
   return (L + STRIDE - 1) / STRIDE <= LINE_SAMPLE_MAX;
 }
 
@@ -1726,6 +1733,10 @@ std::mutex g_mu;
 DevState g_dev[MAX_DEVICES];
 std::atomic<int> g_mode{TOPK_PATH_AUTO};
 std::atomic<int> g_exec{TOPK_EXEC_AUTO};
+// Proposal parameters: sample stride and the two candidate targets in thousandths of K.
+std::atomic<int> g_stride{(int)STRIDE};
+std::atomic<int> g_rho0{1500};
+std::atomic<int> g_rho1{1750};
 thread_local char g_err[512] = "";
 
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -1855,8 +1866,10 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
   p.N = (uint32_t)N_alloc;
   p.K = (uint32_t)K;
   p.sentinel = sentinel;
-  p.T0 = (uint32_t)((3 * K + 1) / 2);
-  p.T1 = (uint32_t)((7 * K + 3) / 4);
+  // Targets ceil(rho * K) with rho in thousandths: 1.5 K and 1.75 K by default.
+  p.T0 = (uint32_t)(((int64_t)g_rho0.load() * K + 999) / 1000);
+  p.T1 = (uint32_t)(((int64_t)g_rho1.load() * K + 999) / 1000);
+  p.stride = (uint32_t)g_stride.load();
   p.direct_max = DIRECT_MAX_DEFAULT;
   p.mode = g_mode.load();
   p.rec = st->rec;
@@ -1874,6 +1887,14 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
   // per-row loop overhead is not amortised).
   const int64_t resident = (int64_t)st->occ * st->n_cu;
   const int ex = g_exec.load();
+  // Line sampling reads the sampled lines whole and skips them in the full pass; a
+  // sampled line is read again when its maximum reaches tau1 ("hot"). Measured on
+  // MI355X with the synthetic windows, it pays only on the longest rows (τ deep in
+  // the tail, so few hot lines) when workgroups run several rows each: 8192 x 1M
+  // 5.85 -> 5.58 ms with it, but 4096 x 512K 1.53 -> 1.66 ms and 512 x 1M (one row per
+  // workgroup, sampling in lockstep) 0.445 -> 0.471 ms, 512 x 128K +12% and 64K rows
+  // +13%. A forced sampled path keeps it wherever it applies.
+  p.line_min = (p.mode == TOPK_PATH_SAMPLED) ? 0u : ((M >= 2 * resident) ? 6144u : 0xFFFFFFFFu);
   bool split = M <= (int64_t)RS_MAX_ROWS &&
                (ex == TOPK_EXEC_ROWSPLIT || p.mode == TOPK_PATH_ROWSPLIT ||
                 (ex == TOPK_EXEC_AUTO && 4 * M <= resident && N_alloc >= ROWSPLIT_MIN_N));
@@ -2011,6 +2032,23 @@ int topk_exact_time_next_call(hipEvent_t start, hipEvent_t stop) {
     return fail(TOPK_ERR_NULL_POINTER, "start and stop must both be set or both be null");
   g_time_start = start;
   g_time_stop = stop;
+  return TOPK_OK;
+}
+
+int topk_exact_set_proposal(int32_t stride, int32_t rho0_permille, int32_t rho1_permille) {
+  g_err[0] = '\0';
+  if (stride == 0 && rho0_permille == 0 && rho1_permille == 0) {
+    stride = (int32_t)STRIDE;
+    rho0_permille = 1500;
+    rho1_permille = 1750;
+  }
+  if (stride < 1 || stride > 65536) return fail(TOPK_ERR_BAD_ARG, "stride %d outside [1, 65536]", stride);
+  if (rho0_permille < 500 || rho1_permille < rho0_permille || rho1_permille > 4000)
+    return fail(TOPK_ERR_BAD_ARG, "targets %d, %d (thousandths of K) need 500 <= rho0 <= rho1 <= 4000",
+                rho0_permille, rho1_permille);
+  g_stride.store(stride);
+  g_rho0.store(rho0_permille);
+  g_rho1.store(rho1_permille);
   return TOPK_OK;
 }
 

@@ -136,6 +136,17 @@ int topk_exact_set_path_override(int mode);
  * under capture without that state runs unsplit. Process-wide. */
 int topk_exact_set_execution(int mode);
 
+/* Proposal parameters for later calls (ablations of the pages' mechanism tables,
+ * [Cx] section "采样不是处处都该开"): the sample stride s (sample keys x[j*s], j <
+ * ceil(L/s)) and the primary / secondary candidate targets rho0*K and rho1*K, given
+ * in thousandths of K. The method's values are s = 128, rho0 = 1.5, rho1 = 1.75
+ * (restored by passing 0, 0, 0). Every setting gives an exact result; only the work
+ * changes. Strides other than 128 read the sample element by element, take the full
+ * pass without line skipping and never use row-split. Returns TOPK_ERR_BAD_ARG unless
+ * 1 <= stride <= 65536 and 500 <= rho0 <= rho1 <= 4000. Process-wide; a captured graph
+ * keeps the setting made before its capture. */
+int topk_exact_set_proposal(int32_t stride, int32_t rho0_permille, int32_t rho1_permille);
+
 /* Measurement hook: arms a one-shot timing of the next topk_exact call made on this
  * host thread. That call records `start` on its stream just before its first
  * selector kernel and `stop` just after its last one, before the exact-recovery

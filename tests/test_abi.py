@@ -56,6 +56,14 @@ def test_argument_validation_without_gpu():
     assert L.topk_exact_reserve(1, 10, 0) == B.TOPK_ERR_BAD_K
     assert L.topk_stream_read_probe(None, -1, None, None) == B.TOPK_ERR_BAD_SHAPE
     assert L.topk_stream_read_probe(None, 0, None, None) == B.TOPK_OK
+    # Proposal parameters: stride in [1, 65536], 500 <= rho0 <= rho1 <= 4000 (thousandths).
+    assert L.topk_exact_set_proposal(0, 1500, 1750) == B.TOPK_ERR_BAD_ARG
+    assert L.topk_exact_set_proposal(70000, 1500, 1750) == B.TOPK_ERR_BAD_ARG
+    assert L.topk_exact_set_proposal(128, 1750, 1500) == B.TOPK_ERR_BAD_ARG
+    assert L.topk_exact_set_proposal(128, 400, 1500) == B.TOPK_ERR_BAD_ARG
+    assert L.topk_exact_set_proposal(128, 1500, 4001) == B.TOPK_ERR_BAD_ARG
+    assert L.topk_exact_set_proposal(64, 1000, 1250) == B.TOPK_OK
+    assert L.topk_exact_set_proposal(0, 0, 0) == B.TOPK_OK
     # The timing hook takes both events or neither; (NULL, NULL) disarms it.
     assert L.topk_exact_time_next_call(fake, None) == B.TOPK_ERR_NULL_POINTER
     assert L.topk_exact_time_next_call(None, fake) == B.TOPK_ERR_NULL_POINTER

@@ -417,6 +417,24 @@ def test_large_k_on_long_rows(K4):
         assert st["rows"] == 8
 
 
+@pytest.mark.parametrize("stride,rho0,rho1", [(16, 1.5, 1.75), (32, 1.75, 2.0), (64, 1.0, 1.25), (128, 1.0, 1.25),
+                                             (128, 1.25, 1.5), (256, 1.5, 1.75), (1, 1.5, 1.75)])
+def test_proposal_ablation_stays_exact(stride, rho0, rho1):
+    # Any sample stride and candidate targets give the exact result; only the work and
+    # the path rates change. 64K bf16 rows (ties), C1 rows and a few 1M rows, with the
+    # sampled path forced on the short ones.
+    cases = [(_window_rows("c4_n65536_m512", [(0, 24)]), tk.PATH_SAMPLED),
+             (_window_rows("c1", [(0, 8), (8000, 8)]), tk.PATH_AUTO),
+             (_window_rows("c3b", [(7, 2)]), tk.PATH_AUTO)]
+    with tk.proposal(stride, rho0, rho1):
+        for (s, l), mode in cases:
+            for ex in (tk.EXEC_PERSISTENT, tk.EXEC_ROW_PER_WG):
+                with tk.execution(ex):
+                    out, st = _run(s, l, mode=mode)
+                _check(s, l, out, label=f"stride {stride} rho {rho0}/{rho1} shape {tuple(s.shape)} exec {ex}")
+                assert st["rows"] == s.shape[0]
+
+
 def test_full_size_few_long_rows_take_rowsplit():
     # 64 rows of the 1M causal window: auto dispatch splits each row over several
     # workgroups (few rows per resident slot); sampled rows against the oracle.
