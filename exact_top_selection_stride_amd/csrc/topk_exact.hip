@@ -1552,7 +1552,18 @@ void split_select_kernel(Params p) {
   if (rs->whole) return;
   const uint32_t L = row_length(p, row);
   const uint32_t n_s = (L + STRIDE - 1) / STRIDE;
-  for (uint32_t i = t; i < n_s; i += BLOCK) s.buf[i] = rs->skey[i];
+  // All of the sample's loads are issued before any is stored (one latency).
+  uint32_t v[LM_PER_THREAD];
+#pragma unroll
+  for (int m = 0; m < LM_PER_THREAD; ++m) {
+    const uint32_t i = t + (uint32_t)m * BLOCK;
+    v[m] = i < n_s ? rs->skey[i] : 0u;
+  }
+#pragma unroll
+  for (int m = 0; m < LM_PER_THREAD; ++m) {
+    const uint32_t i = t + (uint32_t)m * BLOCK;
+    if (i < n_s) s.buf[i] = v[m];
+  }
   __syncthreads();
   uint32_t t0key, t1key;
   select_taus(n_s, sample_rank(p.T0, n_s, L), sample_rank(p.T1, n_s, L), ~rs->mn_inv, rs->mx, t0key, t1key);
@@ -1650,11 +1661,27 @@ void split_finish_kernel(Params p) {
       recover_row(p, row, x, L, smin, t1key, out);
     } else {
       if (t == 0) stat_add(p.ctl, c0 >= p.K ? TOPK_STAT_TAU0 : TOPK_STAT_TAU1);
+      // The merged histogram and candidates move to LDS with all loads issued first.
+      constexpr int HPT = NB / BLOCK, CPT = CAP / BLOCK;
+      uint32_t h[HPT], ci[CPT], ck[CPT];
+#pragma unroll
+      for (int m = 0; m < HPT; ++m) h[m] = rs->hist[t + (uint32_t)m * BLOCK];
+#pragma unroll
+      for (int m = 0; m < CPT; ++m) {
+        const uint32_t i = t + (uint32_t)m * BLOCK;
+        ci[m] = i < c1 ? rs->cand_idx[i] : 0u;
+        ck[m] = i < c1 ? rs->cand_key[i] : 0u;
+      }
       reset_row_state();
-      for (uint32_t b = t; b < (uint32_t)NB; b += BLOCK) s.hist[b] = rs->hist[b];
-      for (uint32_t i = t; i < c1; i += BLOCK) {
-        s.buf[i] = rs->cand_idx[i];
-        s.buf[CAP + i] = rs->cand_key[i];
+#pragma unroll
+      for (int m = 0; m < HPT; ++m) s.hist[t + (uint32_t)m * BLOCK] = h[m];
+#pragma unroll
+      for (int m = 0; m < CPT; ++m) {
+        const uint32_t i = t + (uint32_t)m * BLOCK;
+        if (i < c1) {
+          s.buf[i] = ci[m];
+          s.buf[CAP + i] = ck[m];
+        }
       }
       __syncthreads();
       refine_commit(c1, p.K, pass_ctx(t1key, t0key, smax), out, p.ctl);
@@ -1949,14 +1976,19 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
     e = hipEventRecord(ev_stop, stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord(stop)");
   }
-  // Exact recovery of the rows the selector queued (they exit at once if none).
-  hipLaunchKernelGGL(recovery_hist_kernel, dim3(st->n_cu * 4), dim3(BLOCK), 0, stream, p);
+  // Exact recovery of the rows the selector queued (they exit at once if none). At most
+  // min(M, QMAX) rows can be queued, so small calls launch correspondingly small grids.
+  const int64_t rec_rows = M < (int64_t)QMAX ? M : (int64_t)QMAX;
+  const int64_t rec_items = rec_rows * ((N_alloc + REC_SEG - 1) / REC_SEG);
+  const unsigned rec_grid = (unsigned)(rec_items < (int64_t)st->n_cu * 4 ? rec_items : (int64_t)st->n_cu * 4);
+  hipLaunchKernelGGL(recovery_hist_kernel, dim3(rec_grid), dim3(BLOCK), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch recovery_hist_kernel");
-  hipLaunchKernelGGL(recovery_collect_kernel, dim3(st->n_cu * 4), dim3(BLOCK), 0, stream, p);
+  hipLaunchKernelGGL(recovery_collect_kernel, dim3(rec_grid), dim3(BLOCK), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch recovery_collect_kernel");
-  const unsigned fin_grid = (unsigned)(QMAX < (uint32_t)(st->n_cu * st->occ_rec) ? QMAX : st->n_cu * st->occ_rec);
+  const int64_t fin_cap = (int64_t)st->n_cu * st->occ_rec;
+  const unsigned fin_grid = (unsigned)(rec_rows < fin_cap ? rec_rows : fin_cap);
   hipLaunchKernelGGL(recovery_finish_kernel, dim3(fin_grid), dim3(BLOCK), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch recovery_finish_kernel");
