@@ -7,8 +7,7 @@
 //   [AX] "Sample-Guided Exact Top-K Selection for Long-Context Sparse Attention"
 //        (arxivdaily abstract page)
 //
-// Per row of the score matrix (one 512-thread workgroup per row at a time,
-// workgroups pull rows from a device ticket: persistent execution, [AX]):
+// Per row of the score matrix (one 512-thread workgroup works on a row at a time):
 //   1. Rows with L <= K write 0..L-1 and the sentinel; no score is read
 //      ([Cx] section "什么叫精确，时间怎么量").
 //   2. Short rows (direct-exact, [Cx] section "采样不是处处都该开": exact
@@ -17,12 +16,14 @@
 //   3. Longer rows take the sampled path ([PD] question 2, Fig. 4):
 //      a. the fixed-stride view x[j*128] proposes tau0 (target 1.5K
 //         candidates) and the nested, wider tau1 (target 1.75K) as ranks of
-//         the sample ([Cx] section "采样不是处处都该开"; [PD] question 2);
-//      b. one mandatory full-row pass reads the row with 128-bit loads,
-//         admits keys >= tau1 into an LDS candidate buffer by wave ballot and
-//         prefix count, counts C(tau0) and C(tau1), and builds the first
-//         radix histogram of the admitted keys ([PD] question 2, Fig. 4 stage
-//         2; [AX]);
+//         the sample ([Cx] section "采样不是处处都该开"; [PD] question 2). On
+//         the longest rows the sampled 128-byte lines are read whole and
+//         skipped by the full pass (line sampling, below);
+//      b. one mandatory full-row pass reads the row with 128-bit non-temporal
+//         loads, admits keys >= tau1 into an LDS candidate buffer by wave
+//         ballot and prefix count, counts C(tau0) and C(tau1), and builds the
+//         first radix histogram of the admitted keys ([PD] question 2, Fig. 4
+//         stage 2; [AX]);
 //      c. certification: C(tau0) >= K, else C(tau1) >= K (the nested set is
 //         already in LDS, so this fallback rereads nothing), else exact
 //         full-row recovery; a candidate overflow also goes to recovery.
@@ -31,9 +32,13 @@
 //         holds rank K are committed at once, that bin's candidates move to a
 //         small frontier buffer and radix digits narrow it until the K-th key
 //         is exact ([PD] question 2, Fig. 4 stage 3).
-//   4. Exact full-row recovery is a two-pass radix select from HBM: a
-//      histogram pass, then a pass that commits every key above the boundary
-//      bin and collects that bin into LDS for the final exact step.
+//   4. Exact full-row recovery is a radix select over the whole row, run after
+//      the selector by three small kernels that spread the queued rows over the
+//      GPU: a histogram pass, a pass that commits every key above the boundary
+//      bin and collects that bin, and a finish step per row.
+// Rows map to workgroups by shape ([AX]; [PD] question 2): several workgroups
+// per row for few long rows (row-split), a persistent grid pulling rows from a
+// device ticket for many long rows, one workgroup per row otherwise.
 //
 // Keys: a float's 32-bit pattern u maps to key(u) = u ^ (sign ? 0xFFFFFFFF :
 // 0x80000000), whose unsigned order is IEEE totalOrder. The hot loop never
@@ -43,8 +48,10 @@
 //
 // Code conventions: the workgroup's LDS state is one file-scope __shared__
 // object, and score/output rows are handled through address-space-1 (global)
-// pointers, so the per-row function can stay out of line (register allocation
-// per phase) while every access still compiles to ds_* / global_* instructions.
+// pointers, so every helper, inlined anywhere, compiles its accesses to ds_* /
+// global_* instructions (never flat ones). The whole per-row path is inlined
+// into each kernel: an out-of-line call per row would save and restore its
+// callee-saved registers through scratch memory for every row.
 
 #include "topk_exact.h"
 
@@ -625,7 +632,8 @@ __device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, const PassCtx c
 // then reads only the other three lines of every 512-byte period, and a sampled
 // line is read again only if its maximum reaches tau1 (a "hot" line), since no
 // other sampled line can hold an admitted element. Every element is examined
-// exactly once, by the pass or by the hot-line step.
+// exactly once, by the pass or by the hot-line step. It pays where few sampled lines
+// are hot (tau1 deep in the tail of long rows); the host enables it by shape.
 //
 // Geometry: offsets are counted in floats from base = x rounded down to a 128-byte
 // line, so element index = offset - off4 with off4 = (x & 127) / 4. The line of

@@ -60,7 +60,8 @@ typedef enum {
 
 /* Path override modes (test and benchmark use; default TOPK_PATH_AUTO). */
 #define TOPK_PATH_AUTO 0      /* per-row choice: sentinel, direct-exact or sampled */
-#define TOPK_PATH_SAMPLED 1   /* every row with L > K takes the sampled path */
+#define TOPK_PATH_SAMPLED 1   /* every row with L > K takes the sampled path (with line-granular
+                                 sampling wherever its geometry applies) */
 #define TOPK_PATH_ROWSPLIT 2  /* every row with L > K takes the sampled path, split over
                                  several workgroups (calls of at most 1024 rows) */
 #define TOPK_PATH_DIRECT 3    /* every row with L > K takes the direct exact path */
