@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 METRIC = "Top-K rows/s and achieved HBM GB/s (frac of peak), K=2048, FP32 ragged rows"
 HBM_PEAK_GBPS = 8000.0
 K_DEFAULT = 2048
+EXECUTIONS = {"auto": 0, "persistent": 1, "row": 2, "rowsplit": 3}  # TOPK_EXEC_* values
 
 
 def parse():
@@ -41,6 +42,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU work for the oracle leg")
     ap.add_argument("--check-rows", type=int, default=32, help="rows per group checked before timing")
     ap.add_argument("--no-probe", action="store_true", help="skip timing the stream-read probe")
+    ap.add_argument("--execution", choices=sorted(EXECUTIONS), default="auto",
+                    help="row-to-workgroup mapping (auto: the library's shape-based choice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy first (known bytes, for counter calibration)")
     return ap.parse_args()
@@ -138,6 +141,7 @@ def main():
               for g in range(w.groups)]
     outs = [torch.empty((w.M, K), dtype=torch.int32, device=dev) for _ in range(w.groups)]
     tk.reserve(w.M, w.n_alloc, K)
+    tk.set_execution(EXECUTIONS[args.execution])
 
     # Contract gate on every group before anything is timed.
     tk.reset_stats()
@@ -254,14 +258,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N_alloc": w.n_alloc, "K": K, "groups": w.groups,
                    "lengths": w.lengths, "tail_p": w.tail_p, "bf16_rounded": w.bf16,
-                   "launch": "eager" if args.eager else "hipGraph replay"},
+                   "launch": "eager" if args.eager else "hipGraph replay", "execution": args.execution},
         "hbm_gbps": steps_bytes / wall / 1e9,
         "hbm_frac_of_peak": steps_bytes / wall / 1e9 / HBM_PEAK_GBPS,
         "median_call_ms": statistics.median(per_call_ms),
         "mean_call_ms": sum(per_call_ms) / args.steps,
         "p10_call_ms": sorted(per_call_ms)[int(0.1 * (len(per_call_ms) - 1))],
         "p90_call_ms": sorted(per_call_ms)[int(0.9 * (len(per_call_ms) - 1))],
-        "roofline": {"bound": "hbm", "kernel": "topk_rows_kernel", "achieved": achieved,
+        "roofline": {"bound": "hbm",
+                     "kernel": "split_{sample,select,pass,finish}_kernel" if stats.get("rowsplit") else "topk_rows_kernel",
+                     "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic, "mean_launch_ms": kernel_total_s / args.steps * 1e3,
                      "timing": "library-recorded HIP events around the selector kernels, "

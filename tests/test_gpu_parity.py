@@ -394,6 +394,14 @@ def test_full_size_c3a_sampled_rows():
     _full_size_sampled_rows("c3a", 15, [0, 255, 511])
 
 
+def test_full_size_c3a_forced_rowsplit():
+    # The 512 x 1M launch configuration through the row-split kernels (auto dispatch
+    # keeps one workgroup per row there, which is faster on MI355X).
+    with tk.execution(tk.EXEC_ROWSPLIT):
+        st = _full_size_sampled_rows("c3a", 3, [0, 100, 511])
+    assert st["rowsplit"] == 512
+
+
 @pytest.mark.parametrize("name", [f"dec_n{n}_m{m}" for n in W.DECODE_WIDTHS for m in W.DECODE_ROWS])
 def test_decode_shapes(name):
     # Few long rows: auto dispatch splits each row over several workgroups; every row
