@@ -873,6 +873,10 @@ __device__ __forceinline__ void fused_pass_lines(grow_t x, uint32_t L, uint32_t 
 // candidates are in LDS with the first histogram over (key - key(tau1)) >> sh.
 __device__ __forceinline__ void refine_commit(uint32_t n, uint32_t K, const PassCtx c, gout_t out, Control* ctl) {
   Smem& s = g_s;
+  if (threadIdx.x == 0) {  // extremes of the boundary bin's keys (block_find_bin's barrier orders this)
+    s.mn = KEY_MAX;
+    s.mx = 0;
+  }
   block_find_bin(K);
   const uint32_t b = s.sel_bin, above = s.sel_above;
   const uint32_t cb = s.hist[b];
@@ -882,20 +886,33 @@ __device__ __forceinline__ void refine_commit(uint32_t n, uint32_t K, const Pass
   const uint32_t bhi = (b == (uint32_t)(NB - 1)) ? KEY_MAX
                                                  : blo + ((KEY_MAX - blo) < wdt ? (KEY_MAX - blo) : wdt);
   const bool fits = cb <= (uint32_t)FL_CAP;
-  // Commit the resolved bins above b; move bin b to the frontier buffer.
+  // Commit the resolved bins above b; move bin b to the frontier buffer, or, when it
+  // is too wide for it, note the extremes of its keys.
+  uint32_t bmn = KEY_MAX, bmx = 0;
   for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
     const uint32_t k = s.buf[CAP + i];
     const uint32_t id = s.buf[i];
     const bool g = k > bhi;
     const uint32_t p = wave_reserve(g, &s.out_gt);
     if (g && p < K) out[p] = (int32_t)id;
+    const bool in = k >= blo && k <= bhi;
     if (fits) {
-      const bool in = k >= blo && k <= bhi;
       const uint32_t f = wave_reserve(in, &s.fl_cnt);
       if (in && f < (uint32_t)FL_CAP) {
         s.fl_idx[f] = id;
         s.fl_key[f] = k;
       }
+    } else if (in) {
+      bmn = min(bmn, k);
+      bmx = max(bmx, k);
+    }
+  }
+  if (!fits) {
+    bmn = wave_min_u32(bmn);
+    bmx = wave_max_u32(bmx);
+    if (lane_id() == 0) {
+      atomicMin(&s.mn, bmn);
+      atomicMax(&s.mx, bmx);
     }
   }
   __syncthreads();
@@ -910,9 +927,16 @@ __device__ __forceinline__ void refine_commit(uint32_t n, uint32_t K, const Pass
   } else {
     if (threadIdx.x == 0) stat_add(ctl, TOPK_STAT_FRONTIER_WIDE);
     const uint32_t* keys = &s.buf[CAP];
-    select_rank([&](auto&& f) {
-      for (uint32_t i = threadIdx.x; i < n; i += BLOCK) f(keys[i]);
-    }, need, blo, bhi, T, gt2);
+    if (s.mn == s.mx) {
+      // The whole boundary bin is one repeated key (typical of bf16-rounded scores):
+      // it is the K-th key, and `need` of its copies complete the output.
+      T = s.mn;
+      gt2 = 0;
+    } else {
+      select_rank([&](auto&& f) {
+        for (uint32_t i = threadIdx.x; i < n; i += BLOCK) f(keys[i]);
+      }, need, blo, bhi, T, gt2);
+    }
     const uint32_t gt_total = above + gt2;
     const uint32_t ties = K - gt_total;
     for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {

@@ -309,6 +309,31 @@ def test_rowsplit_merges_segments():
         assert st["rowsplit"] == 4
 
 
+@pytest.mark.parametrize("two_keys", [False, True])
+def test_wide_boundary_bin_of_ties(two_keys):
+    # 3000 copies of one value (or 1500 each of two adjacent floats) above a body below
+    # 40: tau1 lands on them, so the boundary bin holds more keys than the frontier
+    # buffer; with one key it is resolved as ties directly, with two by narrowing.
+    L, rows = 65536, []
+    for seed in range(4):
+        rng = np.random.default_rng(500 + seed)
+        x = rng.uniform(0.0, 40.0, size=L).astype(np.float32)
+        pos = rng.choice(L, size=3000, replace=False)
+        x[pos] = np.float32(50.0)
+        if two_keys:
+            x[pos[:1500]] = np.nextafter(np.float32(50.0), np.float32(60.0))
+        rows.append(x)
+    s = torch.from_numpy(np.stack(rows)).to(DEV)
+    l = torch.full((4,), L, dtype=torch.int32, device=DEV)
+    for mode in (tk.PATH_SAMPLED, tk.PATH_AUTO):
+        for ex in (tk.EXEC_PERSISTENT, tk.EXEC_ROW_PER_WG):
+            with tk.execution(ex):
+                out, st = _run(s, l, mode=mode)
+            _check(s, l, out, label=f"wide tie bin two_keys={two_keys} mode {mode} exec {ex}")
+            if mode == tk.PATH_SAMPLED:
+                assert st["frontier_wide"] == 4
+
+
 def test_consecutive_calls_reuse_the_ticket():
     # Row tickets rewind after every call: calls of different M back to back.
     s, l = _window_rows("c1", [(0, 40)])
