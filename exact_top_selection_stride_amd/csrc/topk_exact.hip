@@ -80,6 +80,7 @@ constexpr int NB = 1 << NB_BITS;      // radix histogram bins
 constexpr int CAP = 8192;             // candidate (index, key) pairs in LDS
 constexpr int KEYS_CAP = 2 * CAP;     // keys-only capacity of the same region
 constexpr int FL_CAP = 512;           // frontier (index, key) pairs
+constexpr uint32_t FL_RANK_MAX = 64;  // frontiers up to this size are resolved by rank counting
 constexpr uint32_t STRIDE = 128;      // sample stride s
 constexpr int UNROLL = 3;             // 128-bit loads per thread per batch
 constexpr uint32_t DIRECT_MAX_DEFAULT = 16384;
@@ -902,28 +903,52 @@ __device__ __forceinline__ void refine_commit(uint32_t n, uint32_t K, const Pass
         s.fl_idx[f] = id;
         s.fl_key[f] = k;
       }
-    } else if (in) {
+    }
+    if (in) {
       bmn = min(bmn, k);
       bmx = max(bmx, k);
     }
   }
-  if (!fits) {
-    bmn = wave_min_u32(bmn);
-    bmx = wave_max_u32(bmx);
-    if (lane_id() == 0) {
-      atomicMin(&s.mn, bmn);
-      atomicMax(&s.mx, bmx);
-    }
+  bmn = wave_min_u32(bmn);
+  bmx = wave_max_u32(bmx);
+  if (lane_id() == 0) {
+    atomicMin(&s.mn, bmn);
+    atomicMax(&s.mx, bmx);
   }
   __syncthreads();
   uint32_t T, gt2;
-  if (fits) {
-    // The frontier holds at most BLOCK keys: each thread ranks one of them, and the
-    // first `need` in (key descending, position ascending) order are committed.
+  if (fits && cb <= FL_RANK_MAX) {
+    // A short frontier: each thread ranks one of its keys, and the first `need` in
+    // (key descending, position ascending) order are committed.
     const uint32_t rk = rank_in_list(s.fl_key, cb);
     const bool sel = rk < need;
     const uint32_t pp = wave_reserve(sel, &s.out_gt);
     if (sel && pp < K) out[pp] = (int32_t)s.fl_idx[threadIdx.x];
+  } else if (fits) {
+    // A longer frontier (one key per thread): find the K-th key T inside it, from the
+    // extremes when it is a single repeated key, else by radix narrowing over
+    // [min, max]; commit the keys above T and `need - gt` of the copies of T (ties at
+    // the boundary may go either way).
+    const uint32_t mn = s.mn, mx = s.mx;
+    if (mn == mx) {
+      T = mn;
+      gt2 = 0;
+    } else {
+      select_rank([&](auto&& f) {
+        if (threadIdx.x < cb) f(g_s.fl_key[threadIdx.x]);
+      }, need, mn, mx, T, gt2);
+    }
+    const uint32_t gt_total = above + gt2;
+    const uint32_t ties = K - gt_total;
+    const bool has = threadIdx.x < cb;
+    const uint32_t k = has ? s.fl_key[threadIdx.x] : 0u;
+    const uint32_t id = has ? s.fl_idx[threadIdx.x] : 0u;
+    const bool g = has && k > T;
+    const uint32_t pg = wave_reserve(g, &s.out_gt);
+    if (g && pg < K) out[pg] = (int32_t)id;
+    const bool e = has && k == T;
+    const uint32_t q = wave_reserve(e, &s.out_tie);
+    if (e && q < ties && gt_total + q < K) out[gt_total + q] = (int32_t)id;
   } else {
     if (threadIdx.x == 0) stat_add(ctl, TOPK_STAT_FRONTIER_WIDE);
     const uint32_t* keys = &s.buf[CAP];
