@@ -482,7 +482,14 @@ __device__ __attribute__((noinline)) void exact_full_row(grow_t x, uint32_t L, u
 
 // ---------------------------------------------------------- direct (in LDS)
 
-__device__ __forceinline__ void direct_exact(grow_t x, uint32_t L, uint32_t K, gout_t out) {
+// Direct exact selection of a short row: the row is staged in LDS as keys (one HBM
+// read), its first histogram over [min, max] is built there, and the LDS list is
+// refined like a certified candidate list (refine_list, below).
+template <bool KEYS_ONLY>
+__device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t base, uint32_t sh, gout_t out,
+                                            Control* ctl);
+
+__device__ __forceinline__ void direct_exact(grow_t x, uint32_t L, uint32_t K, gout_t out, Control* ctl) {
   Smem& s = g_s;
   uint32_t mn = KEY_MAX, mx = 0;
   for_each_element(x, L, [&](uint32_t u, uint32_t e) {
@@ -492,11 +499,11 @@ __device__ __forceinline__ void direct_exact(grow_t x, uint32_t L, uint32_t K, g
     mx = max(mx, k);
   });
   block_minmax(mn, mx);
-  uint32_t T, gt;
-  select_rank([&](auto&& f) {
-    for (uint32_t i = threadIdx.x; i < L; i += BLOCK) f(g_s.buf[i]);
-  }, K, s.mn, s.mx, T, gt);
-  commit_list(s.buf, nullptr, L, T, gt, K, out);
+  const uint32_t lo = s.mn, hi = s.mx;
+  const uint32_t sh = shift_for(hi - lo);
+  for (uint32_t i = threadIdx.x; i < L; i += BLOCK) atomicAdd(&s.hist[(s.buf[i] - lo) >> sh], 1u);
+  __syncthreads();
+  refine_list<true>(L, K, lo, sh, out, ctl);
 }
 
 // ---------------------------------------------------------------- sampled path
@@ -870,10 +877,19 @@ __device__ __forceinline__ void fused_pass_lines(grow_t x, uint32_t L, uint32_t 
   if (lane_id() == 0 && c0w != 0) atomicAdd(&s.cnt0, c0w);
 }
 
-// Boundary refinement and commit after a certified pass: n = C(tau1) <= CAP
-// candidates are in LDS with the first histogram over (key - key(tau1)) >> sh.
-__device__ __forceinline__ void refine_commit(uint32_t n, uint32_t K, const PassCtx c, gout_t out, Control* ctl) {
+// Boundary refinement and commit of an LDS list of n keys whose first histogram,
+// over (key - base) >> sh (top bin clamped), is in s.hist, with the row counters
+// zeroed: the bins above the bin holding rank K are committed in one pass, that
+// bin's keys move to the frontier buffer (or, when too many, only their extremes are
+// noted), and the frontier is resolved exactly.
+template <bool KEYS_ONLY>
+__device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t base, uint32_t sh, gout_t out,
+                                            Control* ctl) {
   Smem& s = g_s;
+  // The list: (index, key) pairs at s.buf[i], s.buf[CAP + i], or keys only at s.buf[i]
+  // with the position as the index.
+  auto key_at = [&](uint32_t i) -> uint32_t { return KEYS_ONLY ? g_s.buf[i] : g_s.buf[CAP + i]; };
+  auto id_at = [&](uint32_t i) -> uint32_t { return KEYS_ONLY ? i : g_s.buf[i]; };
   if (threadIdx.x == 0) {  // extremes of the boundary bin's keys (block_find_bin's barrier orders this)
     s.mn = KEY_MAX;
     s.mx = 0;
@@ -882,8 +898,8 @@ __device__ __forceinline__ void refine_commit(uint32_t n, uint32_t K, const Pass
   const uint32_t b = s.sel_bin, above = s.sel_above;
   const uint32_t cb = s.hist[b];
   const uint32_t need = K - above;
-  const uint32_t blo = c.t1key + (b << c.sh);
-  const uint32_t wdt = (1u << c.sh) - 1u;
+  const uint32_t blo = base + (b << sh);
+  const uint32_t wdt = (1u << sh) - 1u;
   const uint32_t bhi = (b == (uint32_t)(NB - 1)) ? KEY_MAX
                                                  : blo + ((KEY_MAX - blo) < wdt ? (KEY_MAX - blo) : wdt);
   const bool fits = cb <= (uint32_t)FL_CAP;
@@ -891,8 +907,8 @@ __device__ __forceinline__ void refine_commit(uint32_t n, uint32_t K, const Pass
   // is too wide for it, note the extremes of its keys.
   uint32_t bmn = KEY_MAX, bmx = 0;
   for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
-    const uint32_t k = s.buf[CAP + i];
-    const uint32_t id = s.buf[i];
+    const uint32_t k = key_at(i);
+    const uint32_t id = id_at(i);
     const bool g = k > bhi;
     const uint32_t p = wave_reserve(g, &s.out_gt);
     if (g && p < K) out[p] = (int32_t)id;
@@ -951,7 +967,6 @@ __device__ __forceinline__ void refine_commit(uint32_t n, uint32_t K, const Pass
     if (e && q < ties && gt_total + q < K) out[gt_total + q] = (int32_t)id;
   } else {
     if (threadIdx.x == 0) stat_add(ctl, TOPK_STAT_FRONTIER_WIDE);
-    const uint32_t* keys = &s.buf[CAP];
     if (s.mn == s.mx) {
       // The whole boundary bin is one repeated key (typical of bf16-rounded scores):
       // it is the K-th key, and `need` of its copies complete the output.
@@ -959,14 +974,14 @@ __device__ __forceinline__ void refine_commit(uint32_t n, uint32_t K, const Pass
       gt2 = 0;
     } else {
       select_rank([&](auto&& f) {
-        for (uint32_t i = threadIdx.x; i < n; i += BLOCK) f(keys[i]);
+        for (uint32_t i = threadIdx.x; i < n; i += BLOCK) f(key_at(i));
       }, need, blo, bhi, T, gt2);
     }
     const uint32_t gt_total = above + gt2;
     const uint32_t ties = K - gt_total;
     for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
-      const uint32_t k = keys[i];
-      const uint32_t id = s.buf[i];
+      const uint32_t k = key_at(i);
+      const uint32_t id = id_at(i);
       const bool g = k > T && k <= bhi;
       const uint32_t p = wave_reserve(g, &s.out_gt);
       if (g && p < K) out[p] = (int32_t)id;
@@ -975,6 +990,12 @@ __device__ __forceinline__ void refine_commit(uint32_t n, uint32_t K, const Pass
       if (e && q < ties && gt_total + q < K) out[gt_total + q] = (int32_t)id;
     }
   }
+}
+
+// After a certified sampled pass: n = C(tau1) <= CAP candidates in LDS with the first
+// histogram over (key - key(tau1)) >> sh.
+__device__ __forceinline__ void refine_commit(uint32_t n, uint32_t K, const PassCtx c, gout_t out, Control* ctl) {
+  refine_list<false>(n, K, c.t1key, c.sh, out, ctl);
 }
 
 // Hands a row that needs exact full-row recovery to the cooperative recovery
@@ -1160,7 +1181,7 @@ __device__ __forceinline__ void process_row(const Params& p, uint32_t row) {
   const bool direct = (p.mode == TOPK_PATH_DIRECT) || (p.mode == TOPK_PATH_AUTO && L <= p.direct_max);
   if (direct) {
     if (t == 0) stat_add(p.ctl, TOPK_STAT_DIRECT);
-    if (L <= (uint32_t)KEYS_CAP) direct_exact(x, L, p.K, out);
+    if (L <= (uint32_t)KEYS_CAP) direct_exact(x, L, p.K, out, p.ctl);
     else exact_full_row(x, L, p.K, 0u, KEY_MAX, out, p.ctl);
   } else if (p.mode == TOPK_PATH_RECOVERY) {
     if (t == 0) stat_add(p.ctl, TOPK_STAT_FORCED_RECOVERY);
