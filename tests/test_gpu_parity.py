@@ -237,7 +237,7 @@ def test_suffix_is_never_read(fill):
                                   "small_ints"])
 def test_value_edge_cases(kind):
     g = torch.Generator(device=DEV).manual_seed(77)
-    M, N = 6, 140000
+    M, N = 9, 140000
     if kind == "negative":
         s = torch.randn(M, N, device=DEV, generator=g) * 2.5 - 30.0
     elif kind == "mixed_sign":
@@ -252,7 +252,8 @@ def test_value_edge_cases(kind):
         s[torch.rand(M, N, device=DEV, generator=g) < 0.995] = float("-inf")
     else:
         s = torch.randint(0, 8, (M, N), device=DEV, generator=g).float()
-    l = torch.tensor([N, N - 1, N - 2, N - 3, 70000, 20000], dtype=torch.int32, device=DEV)
+    # Long rows (sampled / full-row exact) and short ones (the LDS-staged direct path).
+    l = torch.tensor([N, N - 1, N - 2, N - 3, 70000, 20000, 16384, 9000, 3000], dtype=torch.int32, device=DEV)
     for mode in (tk.PATH_AUTO, tk.PATH_SAMPLED, tk.PATH_DIRECT, tk.PATH_RECOVERY):
         out, _ = _run(s, l, mode=mode)
         _check(s, l, out, label=f"{kind} mode {mode}")
