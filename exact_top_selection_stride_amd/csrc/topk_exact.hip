@@ -522,39 +522,16 @@ __device__ __forceinline__ bool admits(uint32_t u, uint32_t thr) {
   return POS ? ((int32_t)u >= (int32_t)thr) : (u <= thr);
 }
 
+// A value that never passes admits<POS> (tau1 key != 0 is required for NEG).
 template <bool POS>
-__device__ __forceinline__ bool quad_admits(const u32x4& v, uint32_t thr) {
-  if (POS) {
-    const int32_t m = max(max((int32_t)v.x, (int32_t)v.y), max((int32_t)v.z, (int32_t)v.w));
-    return m >= (int32_t)thr;
-  } else {
-    const uint32_t m = min(min(v.x, v.y), min(v.z, v.w));
-    return m <= thr;
-  }
-}
-
-template <bool POS>
-__device__ __forceinline__ bool batch_admits(const u32x4 (&v)[UNROLL], uint32_t thr) {
-  if (POS) {
-    int32_t m = (int32_t)v[0].x;
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u)
-      m = max(max(m, max((int32_t)v[u].x, (int32_t)v[u].y)), max((int32_t)v[u].z, (int32_t)v[u].w));
-    return m >= (int32_t)thr;
-  } else {
-    uint32_t m = v[0].x;
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) m = min(min(m, min(v[u].x, v[u].y)), min(v[u].z, v[u].w));
-    return m <= thr;
-  }
-}
+constexpr uint32_t never_admitted() { return POS ? 0x80000000u : 0xFFFFFFFFu; }
 
 // Candidate formation for one element slot across the wave: ballot, one LDS atomic
 // per wave for the base slot, prefix count for each lane's slot, histogram update
-// and the tau0 count. Every active lane of the wave must reach it.
+// and this lane's tau0 count. Every active lane of the wave must reach it.
 template <bool POS>
 __device__ __forceinline__ void admit_one(bool valid, uint32_t u, uint32_t e, const PassCtx c,
-                                          uint32_t& c0w) {
+                                          uint32_t& c0l) {
   Smem& s = g_s;
   const bool pred = valid && admits<POS>(u, c.thr);
   const uint64_t m = __ballot(pred);
@@ -563,25 +540,77 @@ __device__ __forceinline__ void admit_one(bool valid, uint32_t u, uint32_t e, co
   uint32_t b = 0;
   if ((int)lane_id() == leader) b = atomicAdd(&s.cnt, (uint32_t)__popcll(m));
   const uint32_t pos = __shfl(b, leader) + mbcnt64(m);
-  const uint32_t k = key_of_bits(u);
   if (pred) {
+    const uint32_t k = key_of_bits(u);
     if (pos < (uint32_t)CAP) {
       s.buf[pos] = e;
       s.buf[CAP + pos] = k;
     }
     const uint32_t d = (k - c.t1key) >> c.sh;
     atomicAdd(&s.hist[d < (uint32_t)(NB - 1) ? d : (uint32_t)(NB - 1)], 1u);
+    c0l += k >= c.t0key ? 1u : 0u;
   }
-  c0w += (uint32_t)__popcll(__ballot(pred && k >= c.t0key));
+}
+
+// Candidate formation for NQ quads per lane (element e[q] + i holds v[q][i]; values
+// that must not be admitted are masked to never_admitted beforehand). Each lane counts
+// its admitted elements; the wave's prefix counts come from the ballots of the count's
+// bits, so one LDS atomic per wave reserves the slots of the whole batch and each lane
+// then writes its candidates to consecutive slots. Every active lane of the wave must
+// reach it.
+template <bool POS, int NQ>
+__device__ __forceinline__ void admit_batch(const u32x4 (&v)[NQ], const uint32_t (&e)[NQ], const PassCtx c,
+                                            uint32_t& c0l) {
+  Smem& s = g_s;
+  constexpr int NBITS = 32 - __builtin_clz(4u * NQ);  // bits of a count in [0, 4 NQ]
+  uint32_t n = 0;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    n += admits<POS>(v[q].x, c.thr) ? 1u : 0u;
+    n += admits<POS>(v[q].y, c.thr) ? 1u : 0u;
+    n += admits<POS>(v[q].z, c.thr) ? 1u : 0u;
+    n += admits<POS>(v[q].w, c.thr) ? 1u : 0u;
+  }
+  uint32_t total = 0, before = 0;
+#pragma unroll
+  for (int bit = 0; bit < NBITS; ++bit) {
+    const uint64_t m = __ballot((n >> bit) & 1u);
+    total += (uint32_t)__popcll(m) << bit;
+    before += mbcnt64(m) << bit;
+  }
+  if (total == 0) return;
+  const int leader = __builtin_ctzll(__ballot(true));
+  uint32_t b = 0;
+  if ((int)lane_id() == leader) b = atomicAdd(&s.cnt, total);
+  uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane(b) + before;
+  if (n == 0) return;
+  auto one = [&](uint32_t u, uint32_t idx) {
+    if (admits<POS>(u, c.thr)) {
+      const uint32_t k = key_of_bits(u);
+      if (pos < (uint32_t)CAP) {
+        s.buf[pos] = idx;
+        s.buf[CAP + pos] = k;
+      }
+      const uint32_t d = (k - c.t1key) >> c.sh;
+      atomicAdd(&s.hist[d < (uint32_t)(NB - 1) ? d : (uint32_t)(NB - 1)], 1u);
+      c0l += k >= c.t0key ? 1u : 0u;
+      ++pos;
+    }
+  };
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    one(v[q].x, e[q]);
+    one(v[q].y, e[q] + 1u);
+    one(v[q].z, e[q] + 2u);
+    one(v[q].w, e[q] + 3u);
+  }
 }
 
 template <bool POS>
-__device__ __forceinline__ void admit_quad(const u32x4& v, uint32_t e, const PassCtx c, uint32_t& c0w) {
-  if (__ballot(quad_admits<POS>(v, c.thr)) == 0) return;
-  admit_one<POS>(true, v.x, e, c, c0w);
-  admit_one<POS>(true, v.y, e + 1, c, c0w);
-  admit_one<POS>(true, v.z, e + 2, c, c0w);
-  admit_one<POS>(true, v.w, e + 3, c, c0w);
+__device__ __forceinline__ void admit_quad(const u32x4& v, uint32_t e, const PassCtx c, uint32_t& c0l) {
+  const u32x4 vv[1] = {v};
+  const uint32_t ee[1] = {e};
+  admit_batch<POS, 1>(vv, ee, c, c0l);
 }
 
 // The mandatory full-row pass when the sampled lines are not skipped: certification
@@ -592,20 +621,19 @@ template <bool POS>
 __device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, const PassCtx c) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
-  uint32_t c0w = 0;
+  uint32_t c0l = 0;
   uint32_t head = (uint32_t)((4u - ((uint32_t)((uintptr_t)x >> 2) & 3u)) & 3u);
   if (head > L) head = L;
-  if (t < head) admit_one<POS>(true, x[t], t, c, c0w);
+  if (t < head) admit_one<POS>(true, x[t], t, c, c0l);
   const uint32_t nv = (L - head) >> 2;
   grow_t body = x + head;
   const uint32_t per = BLOCK * UNROLL;
   const uint32_t nfull = nv / per;
   auto examine = [&](const u32x4 (&v)[UNROLL], uint32_t it) {
-    if (__ballot(batch_admits<POS>(v, c.thr)) != 0) {
+    uint32_t e[UNROLL];
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u)
-        admit_quad<POS>(v[u], head + 4u * (it * per + u * BLOCK + t), c, c0w);
-    }
+    for (int u = 0; u < UNROLL; ++u) e[u] = head + 4u * (it * per + u * BLOCK + t);
+    admit_batch<POS, UNROLL>(v, e, c, c0l);
   };
   if (nfull > 0) {
     // The prefetch is unconditional inside the loop (the last batch is peeled) so
@@ -625,10 +653,10 @@ __device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, const PassCtx c
     }
     examine(a, it);
   }
-  for (uint32_t q = nfull * per + t; q < nv; q += BLOCK) admit_quad<POS>(load4_stream(body + 4u * q), head + 4u * q, c, c0w);
+  for (uint32_t q = nfull * per + t; q < nv; q += BLOCK) admit_quad<POS>(load4_stream(body + 4u * q), head + 4u * q, c, c0l);
   const uint32_t tail0 = head + 4u * nv;
-  if (t < L - tail0) admit_one<POS>(true, x[tail0 + t], tail0 + t, c, c0w);
-  if (lane_id() == 0 && c0w != 0) atomicAdd(&s.cnt0, c0w);
+  if (t < L - tail0) admit_one<POS>(true, x[tail0 + t], tail0 + t, c, c0l);
+  if (c0l != 0) atomicAdd(&s.cnt0, c0l);
 }
 
 // ------------------------------------------------ line-granular sampling
@@ -738,48 +766,85 @@ __device__ __forceinline__ void sample_lines(grow_t x, uint32_t L, uint32_t n_s,
   block_minmax(mn, mx);
 }
 
+// Position of the n-th (from 0) set bit of m; requires n < popcount(m).
+__device__ __forceinline__ uint32_t nth_set_bit(uint64_t m, uint32_t n) {
+  uint32_t w = (uint32_t)m, pos = 0;
+  uint32_t c = (uint32_t)__popc(w);
+  if (n >= c) {
+    n -= c;
+    pos = 32;
+    w = (uint32_t)(m >> 32);
+  }
+#pragma unroll
+  for (uint32_t half = 16; half >= 1; half >>= 1) {
+    c = (uint32_t)__popc(w & ((1u << half) - 1u));
+    if (n >= c) {
+      n -= c;
+      pos += half;
+      w >>= half;
+    }
+  }
+  return pos;
+}
+
 // Re-reads the sampled lines whose maximum reaches tau1 and admits their elements.
-// Bit m of hot_mask is set when line j0 + t + m*BLOCK is hot.
+// Bit m of hot_mask is set when line j0 + t + m*BLOCK is hot. Eight lanes read one
+// hot line (one 16-byte chunk each): for every slot m the wave's ballot names the
+// threads that own a hot line, and the n-th of them goes to lane group n % 8 in round
+// n / 8. Slots are taken HOT_SLOTS at a time with every load of a round in flight
+// together, so a row costs a few memory latencies rather than one per slot.
 template <bool POS>
 __device__ __forceinline__ void hot_lines(grow_t x, uint32_t L, uint32_t j0, uint32_t hot_mask, const PassCtx c) {
   Smem& s = g_s;
-  const uint32_t t = threadIdx.x;
-  uint32_t c0w = 0;
+  constexpr int HOT_SLOTS = 8;
+  static_assert(LM_PER_THREAD % HOT_SLOTS == 0, "slot groups must tile the slots");
+  const uint32_t t = threadIdx.x, lane = lane_id();
+  const uint32_t wbase = t - lane;          // first thread of this wave
+  const uint32_t grp = lane >> 3, ch = lane & 7u;
+  constexpr uint32_t NA = never_admitted<POS>();
+  uint32_t c0l = 0;
   const uint32_t off4 = (uint32_t)((uintptr_t)x & 127u) >> 2;
   grow_t base = x - off4;
   const uint32_t lo = off4, hi = off4 + L;
   const uint32_t gfirst = off4 & ~3u, glast = (hi - 1u) & ~3u;
 #pragma unroll 1
-  for (int m = 0; m < LM_PER_THREAD; ++m) {
-    const uint32_t j = j0 + t + (uint32_t)m * BLOCK;
-    const bool hot = (hot_mask >> m) & 1u;
-    if (__ballot(hot) == 0) continue;
+  for (int mb = 0; mb < LM_PER_THREAD; mb += HOT_SLOTS) {
+    uint64_t b[HOT_SLOTS];
+    uint32_t nb[HOT_SLOTS];
+    uint32_t rounds = 0;
+#pragma unroll
+    for (int u = 0; u < HOT_SLOTS; ++u) {
+      b[u] = __ballot((hot_mask >> (mb + u)) & 1u);
+      nb[u] = (uint32_t)__popcll(b[u]);
+      rounds = max(rounds, (nb[u] + 7u) >> 3);
+    }
 #pragma unroll 1
-    for (int half = 0; half < 2; ++half) {
-      u32x4 v[4] = {splat4(0u), splat4(0u), splat4(0u), splat4(0u)};
-      if (hot) {
+    for (uint32_t r = 0; r < rounds; ++r) {
+      u32x4 v[HOT_SLOTS];
+      uint32_t e[HOT_SLOTS];
+      const uint32_t n = 8u * r + grp;
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          const uint32_t g = 128u * j + 16u * half + 4u * cc;
-          v[cc] = load4(base + (g < gfirst ? gfirst : (g < glast ? g : glast)));
-        }
+      for (int u = 0; u < HOT_SLOTS; ++u) {
+        const bool ok = n < nb[u];
+        const uint32_t owner = ok ? nth_set_bit(b[u], n) : 0u;
+        const uint32_t j = j0 + wbase + owner + (uint32_t)(mb + u) * BLOCK;
+        const uint32_t g = 128u * j + 4u * ch;
+        // Lanes without a line, and chunks outside the row, read an in-bounds chunk of
+        // the row instead; their elements are masked out below.
+        const uint32_t ga = !ok ? gfirst : (g < gfirst ? gfirst : (g < glast ? g : glast));
+        u32x4 w = load4(base + ga);
+        w.x = (ok && g + 0 >= lo && g + 0 < hi) ? w.x : NA;
+        w.y = (ok && g + 1 >= lo && g + 1 < hi) ? w.y : NA;
+        w.z = (ok && g + 2 >= lo && g + 2 < hi) ? w.z : NA;
+        w.w = (ok && g + 3 >= lo && g + 3 < hi) ? w.w : NA;
+        v[u] = w;
+        e[u] = g - off4;
       }
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        const uint32_t g = 128u * j + 16u * half + 4u * cc;
-        admit_one<POS>(hot && g + 0 >= lo && g + 0 < hi, v[cc].x, g + 0 - off4, c, c0w);
-        admit_one<POS>(hot && g + 1 >= lo && g + 1 < hi, v[cc].y, g + 1 - off4, c, c0w);
-        admit_one<POS>(hot && g + 2 >= lo && g + 2 < hi, v[cc].z, g + 2 - off4, c, c0w);
-        admit_one<POS>(hot && g + 3 >= lo && g + 3 < hi, v[cc].w, g + 3 - off4, c, c0w);
-      }
+      admit_batch<POS, HOT_SLOTS>(v, e, c, c0l);
     }
   }
-  if (lane_id() == 0 && c0w != 0) atomicAdd(&s.cnt0, c0w);
+  if (c0l != 0) atomicAdd(&s.cnt0, c0l);
 }
-
-// A value that never passes admits<POS> (tau1 key != 0 is required for NEG).
-template <bool POS>
-constexpr uint32_t never_admitted() { return POS ? 0x80000000u : 0xFFFFFFFFu; }
 
 // Offset of chunk k of the non-sampled lines: period k / 24, line 1 + (k % 24) / 8,
 // chunk k % 8.
@@ -816,7 +881,7 @@ __device__ __forceinline__ void fused_pass_lines(grow_t x, uint32_t L, uint32_t 
                                                  bool tail, const PassCtx c) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
-  uint32_t c0w = 0;
+  uint32_t c0l = 0;
   const uint32_t off4 = (uint32_t)((uintptr_t)x & 127u) >> 2;
   grow_t base = x - off4;
   const uint32_t hi = off4 + L;
@@ -826,16 +891,14 @@ __device__ __forceinline__ void fused_pass_lines(grow_t x, uint32_t L, uint32_t 
   const uint32_t nfull = nk / per;
   auto examine = [&](const u32x4 (&raw)[UNROLL], uint32_t it) {
     u32x4 v[UNROLL];
-    uint32_t g[UNROLL];
+    uint32_t e[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      g[u] = unsampled_offset(k0 + it * per + u * BLOCK + t);
-      v[u] = mask_tail<POS>(raw[u], g[u], hi);
+      const uint32_t g = unsampled_offset(k0 + it * per + u * BLOCK + t);
+      v[u] = mask_tail<POS>(raw[u], g, hi);
+      e[u] = g - off4;
     }
-    if (__ballot(batch_admits<POS>(v, c.thr)) != 0) {
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) admit_quad<POS>(v[u], g[u] - off4, c, c0w);
-    }
+    admit_batch<POS, UNROLL>(v, e, c, c0l);
   };
   auto fetch = [&](u32x4 (&v)[UNROLL], uint32_t it) {
 #pragma unroll
@@ -867,14 +930,14 @@ __device__ __forceinline__ void fused_pass_lines(grow_t x, uint32_t L, uint32_t 
   }
   for (uint32_t k = k0 + nfull * per + t; k < k1; k += BLOCK) {
     const uint32_t g = unsampled_offset(k);
-    admit_quad<POS>(mask_tail<POS>(load_chunk(base, g, glast), g, hi), g - off4, c, c0w);
+    admit_quad<POS>(mask_tail<POS>(load_chunk(base, g, glast), g, hi), g - off4, c, c0l);
   }
   // The first line of period n_s, if the row reaches into it (never sampled).
   if (tail && t < 8) {
     const uint32_t g = 128u * n_s + 4u * t;
-    if (g < hi) admit_quad<POS>(mask_tail<POS>(load_chunk(base, g, glast), g, hi), g - off4, c, c0w);
+    if (g < hi) admit_quad<POS>(mask_tail<POS>(load_chunk(base, g, glast), g, hi), g - off4, c, c0l);
   }
-  if (lane_id() == 0 && c0w != 0) atomicAdd(&s.cnt0, c0w);
+  if (c0l != 0) atomicAdd(&s.cnt0, c0l);
 }
 
 // Boundary refinement and commit of an LDS list of n keys whose first histogram,
@@ -1100,7 +1163,10 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
   } else {
     uint32_t mn = KEY_MAX, mx = 0;
 #pragma unroll 8
-    for (uint32_t j = t; j < n_s; j += BLOCK) {
+    for (uint32_t jr = t; jr < n_s; jr += BLOCK) {
+      // Last sample first: the lines read last are the ones the pass, which runs
+      // from the row's start, meets first, while they are still cached.
+      const uint32_t j = n_s - 1u - jr;
       const uint32_t k = key_of_bits(x[(size_t)j * p.stride]);
       s.buf[j] = k;
       mn = min(mn, k);
@@ -1993,13 +2059,14 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
   const int64_t resident = (int64_t)st->occ * st->n_cu;
   const int ex = g_exec.load();
   // Line sampling reads the sampled lines whole and skips them in the full pass; a
-  // sampled line is read again when its maximum reaches tau1 ("hot"). Measured on
-  // MI355X with the synthetic windows, it pays only on the longest rows (τ deep in
-  // the tail, so few hot lines) when workgroups run several rows each: 8192 x 1M
-  // 5.85 -> 5.58 ms with it, but 4096 x 512K 1.53 -> 1.66 ms and 512 x 1M (one row per
-  // workgroup, sampling in lockstep) 0.445 -> 0.471 ms, 512 x 128K +12% and 64K rows
-  // +13%. A forced sampled path keeps it wherever it applies.
-  p.line_min = (p.mode == TOPK_PATH_SAMPLED) ? 0u : ((M >= 2 * resident) ? 6144u : 0xFFFFFFFFu);
+  // sampled line is read again when its maximum reaches tau1 ("hot"). With about T1
+  // admitted elements in a row of L, a 32-element line is hot with probability of
+  // roughly 32 T1 / L, and the saving (a quarter of the row) shrinks with that
+  // re-read share while the skipping pass reads slightly slower per byte. Auto
+  // dispatch therefore uses it where at most about one sampled line in eight is
+  // expected hot: L >= 256 T1, i.e. n_s >= 2 T1 sample lines. A forced sampled path
+  // keeps it wherever it applies.
+  p.line_min = (p.mode == TOPK_PATH_SAMPLED) ? 0u : 2u * p.T1;
   bool split = M <= (int64_t)RS_MAX_ROWS &&
                (ex == TOPK_EXEC_ROWSPLIT || p.mode == TOPK_PATH_ROWSPLIT ||
                 (ex == TOPK_EXEC_AUTO && 4 * M <= resident && N_alloc >= ROWSPLIT_MIN_N));
