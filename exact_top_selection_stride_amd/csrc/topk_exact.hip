@@ -613,12 +613,21 @@ __device__ __forceinline__ void admit_quad(const u32x4& v, uint32_t e, const Pas
   admit_batch<POS, 1>(vv, ee, c, c0l);
 }
 
-// The mandatory full-row pass when the sampled lines are not skipped: certification
-// counts, candidate compaction and the first histogram, fused. The next batch of
-// loads is issued before the current one is examined so that each thread keeps
-// 2 x UNROLL 128-bit loads in flight.
-template <bool POS>
-__device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, const PassCtx c) {
+// The mandatory full-row pass: certification counts, candidate compaction and the
+// first histogram, fused. The next batch of loads is issued before the current one
+// is examined so that each thread keeps 2 x UNROLL 128-bit loads in flight.
+//
+// With SKIP, the row's sampled lines were read whole by the line sampler, and bit P
+// of the LDS bitmap s.fl_idx says whether the sampled line of period P (offsets
+// [128 P, 128 P + 32) from the 128-byte line below x, P < n_s) holds a key >= tau1.
+// Chunks of the other sampled lines are not loaded: none of their elements can be
+// admitted, so skipping them changes no result. The access pattern stays that of the
+// whole-row pass, with those lanes idle. The loads go through a buffer resource over
+// the row's body: a skipped chunk is given an offset past the resource's end, which
+// the hardware answers with zeros and no memory access. The loads stay unconditional
+// in the control flow, so the compiler can still wait for one batch at a time.
+template <bool POS, bool SKIP>
+__device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, uint32_t n_s, const PassCtx c) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   uint32_t c0l = 0;
@@ -627,33 +636,67 @@ __device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, const PassCtx c
   if (t < head) admit_one<POS>(true, x[t], t, c, c0l);
   const uint32_t nv = (L - head) >> 2;
   grow_t body = x + head;
+  const uint32_t gb = ((uint32_t)((uintptr_t)x & 127u) >> 2) + head;  // body offset from the line below x
   const uint32_t per = BLOCK * UNROLL;
   const uint32_t nfull = nv / per;
-  auto examine = [&](const u32x4 (&v)[UNROLL], uint32_t it) {
+  // Raw buffer over the body (16 nv bytes; rows on this path are at most a few MB).
+  // Word 3 is the gfx9-family buffer format word; the load's cache policy 2 is "nt".
+  const __amdgpu_buffer_rsrc_t rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)body, (short)0, (int)(16u * nv), 0x00020000);
+  // Loads chunk q; `inert` receives the value to OR into it before it is examined
+  // (never_admitted for a skipped chunk, which reads as zeros, else 0). Applying it
+  // at examination rather than here keeps the compiler from waiting for the
+  // prefetched batch, and keeps the load itself unconditional (no branch around it).
+  auto fetch = [&](uint32_t q, uint32_t& inert) -> u32x4 {
+    if (SKIP) {
+      const uint32_t g = gb + 4u * q;
+      const uint32_t P = g >> 7;
+      const uint32_t w = s.fl_idx[(P >> 5) & (uint32_t)(FL_CAP - 1)];
+      const bool cold = ((g >> 5) & 3u) == 0u && P < n_s && ((w >> (P & 31u)) & 1u) == 0u;
+      inert = cold ? never_admitted<POS>() : 0u;
+      return __builtin_amdgcn_raw_buffer_load_b128(rsrc, cold ? 0xFFFFFFF0u : 16u * q, 0, 2);
+    }
+    inert = 0u;
+    return load4_stream(body + 4u * q);
+  };
+  auto examine = [&](const u32x4 (&raw)[UNROLL], const uint32_t (&inert)[UNROLL], uint32_t it) {
+    u32x4 v[UNROLL];
     uint32_t e[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) e[u] = head + 4u * (it * per + u * BLOCK + t);
+    for (int u = 0; u < UNROLL; ++u) {
+      v[u] = SKIP ? (raw[u] | splat4(inert[u])) : raw[u];
+      e[u] = head + 4u * (it * per + u * BLOCK + t);
+    }
     admit_batch<POS, UNROLL>(v, e, c, c0l);
   };
   if (nfull > 0) {
     // The prefetch is unconditional inside the loop (the last batch is peeled) so
     // the compiler waits only for the batch being examined, not for the next one.
     u32x4 a[UNROLL];
+    uint32_t am[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) a[u] = load4_stream(body + 4u * (u * BLOCK + t));
+    for (int u = 0; u < UNROLL; ++u) a[u] = fetch(u * BLOCK + t, am[u]);
     uint32_t it = 0;
     for (; it + 1 < nfull; ++it) {
       u32x4 nx[UNROLL];
+      uint32_t nm[UNROLL];
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u) nx[u] = load4_stream(body + 4u * ((it + 1) * per + u * BLOCK + t));
+      for (int u = 0; u < UNROLL; ++u) nx[u] = fetch((it + 1) * per + u * BLOCK + t, nm[u]);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the examination
-      examine(a, it);
+      examine(a, am, it);
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u) a[u] = nx[u];
+      for (int u = 0; u < UNROLL; ++u) {
+        a[u] = nx[u];
+        am[u] = nm[u];
+      }
     }
-    examine(a, it);
+    examine(a, am, it);
   }
-  for (uint32_t q = nfull * per + t; q < nv; q += BLOCK) admit_quad<POS>(load4_stream(body + 4u * q), head + 4u * q, c, c0l);
+  for (uint32_t q = nfull * per + t; q < nv; q += BLOCK) {
+    uint32_t inert;
+    const u32x4 v = fetch(q, inert);
+    admit_quad<POS>(v | splat4(inert), head + 4u * q, c, c0l);
+  }
   const uint32_t tail0 = head + 4u * nv;
   if (t < L - tail0) admit_one<POS>(true, x[tail0 + t], tail0 + t, c, c0l);
   if (c0l != 0) atomicAdd(&s.cnt0, c0l);
@@ -680,6 +723,8 @@ __device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, const PassCtx c
 
 constexpr uint32_t LINE_SAMPLE_MAX = 8192;              // n_s limit of line sampling
 constexpr int LM_PER_THREAD = LINE_SAMPLE_MAX / BLOCK;  // lines per thread in the hot step
+static_assert(LINE_SAMPLE_MAX / 32 <= FL_CAP, "the hot-line bitmap lives in the frontier index list");
+static_assert(BLOCK % 64 == 0 && LINE_SAMPLE_MAX % BLOCK == 0, "bitmap words are written per wave");
 constexpr int SAMPLE_UNROLL = 6;
 
 // Reads the sampled lines j0 <= j < j1 whole. skey[j] = key(x[j*128]); lmax[j] = max
@@ -687,7 +732,7 @@ constexpr int SAMPLE_UNROLL = 6;
 // Eight lanes read one line (one 16-byte chunk each); batches of SAMPLE_UNROLL
 // loads per lane are double-buffered so the next batch is in flight while the
 // current one is reduced. P is an LDS or a global pointer type.
-template <class P>
+template <bool STREAM = false, class P>
 __device__ __forceinline__ void sample_lines_range(grow_t x, uint32_t L, uint32_t j0, uint32_t j1, P skey,
                                                    P lmax, uint32_t& mn, uint32_t& mx) {
   const uint32_t t = threadIdx.x;
@@ -708,7 +753,8 @@ __device__ __forceinline__ void sample_lines_range(grow_t x, uint32_t L, uint32_
     for (int u = 0; u < SAMPLE_UNROLL; ++u) {
       const uint32_t j = j0 + step * STEP + u * LINES_PER_STEP + (t >> 3);
       const uint32_t g = 128u * j + 4u * c;
-      v[u] = load4(base + (g < gfirst ? gfirst : (g < glast ? g : glast)));
+      const grow_t a = base + (g < gfirst ? gfirst : (g < glast ? g : glast));
+      v[u] = STREAM ? load4_stream(a) : load4(a);
     }
   };
   auto reduce = [&](const u32x4 (&v)[SAMPLE_UNROLL], uint32_t step) {
@@ -760,9 +806,10 @@ __device__ __forceinline__ void sample_lines_range(grow_t x, uint32_t L, uint32_
 }
 
 // The whole row's sample into LDS, with the min/max sample key in s.mn/s.mx.
+template <bool STREAM>
 __device__ __forceinline__ void sample_lines(grow_t x, uint32_t L, uint32_t n_s, uint32_t* skey, uint32_t* lmax) {
   uint32_t mn = KEY_MAX, mx = 0;
-  sample_lines_range(x, L, 0u, n_s, skey, lmax, mn, mx);
+  sample_lines_range<STREAM>(x, L, 0u, n_s, skey, lmax, mn, mx);
   block_minmax(mn, mx);
 }
 
@@ -1142,6 +1189,7 @@ __device__ __forceinline__ uint32_t sample_rank(uint32_t target, uint32_t n_s, u
   return (uint32_t)r;
 }
 
+template <bool STREAM_SAMPLE>
 __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_t x, uint32_t L, gout_t out) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
@@ -1159,7 +1207,7 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
   // full pass reads the whole row.
   const bool by_lines = p.stride == STRIDE && n_s <= LINE_SAMPLE_MAX && n_s >= p.line_min;
   if (by_lines) {
-    sample_lines(x, L, n_s, &s.buf[0], &s.buf[CAP]);
+    sample_lines<STREAM_SAMPLE>(x, L, n_s, &s.buf[0], &s.buf[CAP]);
   } else {
     uint32_t mn = KEY_MAX, mx = 0;
 #pragma unroll 8
@@ -1189,27 +1237,27 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
   // Skipping sampled lines needs a value that is never admitted, which exists
   // unless tau1 is the lowest possible key.
   const bool skip = by_lines && t1key != 0u;
-  uint32_t hot_mask = 0;
   if (skip) {
+    // Bitmap of the hot sampled lines (maximum >= tau1) in s.fl_idx, which the
+    // frontier uses only after the pass.
 #pragma unroll
     for (int m = 0; m < LM_PER_THREAD; ++m) {
       const uint32_t j = t + (uint32_t)m * BLOCK;
-      if (j < n_s && s.buf[CAP + j] >= t1key) hot_mask |= 1u << m;
+      const uint64_t hb = __ballot(j < n_s && s.buf[CAP + j] >= t1key);
+      if (lane_id() == 0) {
+        s.fl_idx[j >> 5] = (uint32_t)hb;
+        s.fl_idx[(j >> 5) + 1] = (uint32_t)(hb >> 32);
+      }
     }
   }
   reset_row_state();  // its barrier also ends every read of the line maxima in LDS
   if (skip) {
-    if (pos) {
-      hot_lines<true>(x, L, 0u, hot_mask, c);
-      fused_pass_lines<true>(x, L, n_s, 0u, 24u * n_s, true, c);
-    } else {
-      hot_lines<false>(x, L, 0u, hot_mask, c);
-      fused_pass_lines<false>(x, L, n_s, 0u, 24u * n_s, true, c);
-    }
+    if (pos) fused_pass<true, true>(x, L, n_s, c);
+    else fused_pass<false, true>(x, L, n_s, c);
   } else if (pos) {
-    fused_pass<true>(x, L, c);
+    fused_pass<true, false>(x, L, n_s, c);
   } else {
-    fused_pass<false>(x, L, c);
+    fused_pass<false, false>(x, L, n_s, c);
   }
   __syncthreads();
   const uint32_t c1 = s.cnt, c0 = s.cnt0;
@@ -1230,6 +1278,7 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
 // One row, start to commit. Everything on the row's path is inlined: an out-of-line
 // call per row would save and restore its callee-saved registers through scratch
 // memory for every row.
+template <bool STREAM_SAMPLE = false>
 __device__ __forceinline__ void process_row(const Params& p, uint32_t row) {
   const uint32_t t = threadIdx.x;
   const int32_t len = p.row_len[row];
@@ -1253,7 +1302,7 @@ __device__ __forceinline__ void process_row(const Params& p, uint32_t row) {
     if (t == 0) stat_add(p.ctl, TOPK_STAT_FORCED_RECOVERY);
     recover_row(p, row, x, L, 0u, KEY_MAX, out);
   } else {
-    sampled_row(p, row, x, L, out);
+    sampled_row<STREAM_SAMPLE>(p, row, x, L, out);
   }
 }
 
@@ -1266,8 +1315,13 @@ void topk_rows_kernel(Params p) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   if (!PERSISTENT) {
+    // All rows of the call start together, so their line samples are read in one
+    // streaming phase: non-temporal loads read it fastest (512 rows of 1M: 0.398 ->
+    // 0.383 ms per call). With persistent execution the rows are staggered and plain
+    // loads let the hot sampled lines come back from cache (8192 rows of 1M were 1%
+    // slower with non-temporal sample loads).
     if (t == 0) s.row = (int32_t)blockIdx.x;
-    process_row(p, blockIdx.x);
+    process_row<true>(p, blockIdx.x);
     return;
   }
   for (;;) {
