@@ -82,7 +82,7 @@ constexpr int KEYS_CAP = 2 * CAP;     // keys-only capacity of the same region
 constexpr int FL_CAP = 512;           // frontier (index, key) pairs
 constexpr uint32_t FL_RANK_MAX = 64;  // frontiers up to this size are resolved by rank counting
 constexpr uint32_t STRIDE = 128;      // sample stride s
-constexpr int UNROLL = 3;             // 128-bit loads per thread per batch
+constexpr int UNROLL = 4;             // 128-bit loads per thread per batch
 constexpr uint32_t DIRECT_MAX_DEFAULT = 16384;
 constexpr uint32_t QMAX = 256;        // rows queued for cooperative recovery per call
 constexpr uint32_t REC_SEG = 16384;   // elements per recovery work item
@@ -2116,11 +2116,11 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
   // sampled line is read again when its maximum reaches tau1 ("hot"). With about T1
   // admitted elements in a row of L, a 32-element line is hot with probability of
   // roughly 32 T1 / L, and the saving (a quarter of the row) shrinks with that
-  // re-read share while the skipping pass reads slightly slower per byte. Auto
-  // dispatch therefore uses it where at most about one sampled line in eight is
-  // expected hot: L >= 256 T1, i.e. n_s >= 2 T1 sample lines. A forced sampled path
-  // keeps it wherever it applies.
-  p.line_min = (p.mode == TOPK_PATH_SAMPLED) ? 0u : 2u * p.T1;
+  // re-read share. Auto dispatch uses it where at most about one sampled line in four
+  // is expected hot: L >= 128 T1, i.e. n_s >= T1 sample lines (measured: 4096 x 512K
+  // 1.507 -> 1.485 ms; 512 x 128K and 64K rows, where most lines are hot, lose with
+  // it). A forced sampled path keeps it wherever it applies.
+  p.line_min = (p.mode == TOPK_PATH_SAMPLED) ? 0u : p.T1;
   bool split = M <= (int64_t)RS_MAX_ROWS &&
                (ex == TOPK_EXEC_ROWSPLIT || p.mode == TOPK_PATH_ROWSPLIT ||
                 (ex == TOPK_EXEC_AUTO && 4 * M <= resident && N_alloc >= ROWSPLIT_MIN_N));
