@@ -202,6 +202,32 @@ __device__ __forceinline__ uint32_t wave_reserve(bool pred, uint32_t* counter) {
   return base + mbcnt64(m);
 }
 
+// Reserves cnt consecutive slots of an LDS counter for every lane (cnt < 2^NBITS) with
+// one atomic per wave: the wave's prefix counts come from the ballots of the count's
+// bits. Returns this lane's first slot. Every active lane of the wave must reach it.
+template <int NBITS>
+__device__ __forceinline__ uint32_t wave_reserve_n(uint32_t cnt, uint32_t* counter) {
+  uint32_t total = 0, before = 0;
+#pragma unroll
+  for (int bit = 0; bit < NBITS; ++bit) {
+    const uint64_t m = __ballot((cnt >> bit) & 1u);
+    total += (uint32_t)__popcll(m) << bit;
+    before += mbcnt64(m) << bit;
+  }
+  uint32_t b = 0;
+  if (total != 0) {
+    const int leader = __builtin_ctzll(__ballot(true));
+    if ((int)lane_id() == leader) b = atomicAdd(counter, total);
+    b = (uint32_t)__builtin_amdgcn_readfirstlane(b);
+  }
+  return b + before;
+}
+
+// Per-thread item counts of LDS lists walked as i = t, t + BLOCK, ...: at most 32 for
+// lists of up to 16384 entries.
+constexpr int LIST_BITS = 6;
+static_assert((KEYS_CAP + BLOCK - 1) / BLOCK < (1 << LIST_BITS), "per-thread list counts fit LIST_BITS");
+
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   for (int o = WAVE / 2; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor(v, o));
   return v;
@@ -397,15 +423,25 @@ __device__ __forceinline__ void commit_list(const uint32_t* keys, const uint32_t
                                             uint32_t T, uint32_t gt_total, uint32_t K, gout_t out) {
   Smem& s = g_s;
   const uint32_t ties = K - gt_total;
+  // Count this thread's keys of each kind, reserve their slots once per wave, then write.
+  uint32_t ng = 0, ne = 0;
   for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
     const uint32_t k = keys[i];
-    const uint32_t id = idx ? idx[i] : i;
-    const bool g = k > T;
-    const uint32_t p = wave_reserve(g, &s.out_gt);
-    if (g && p < K) out[p] = (int32_t)id;
-    const bool e = k == T;
-    const uint32_t q = wave_reserve(e, &s.out_tie);
-    if (e && q < ties && gt_total + q < K) out[gt_total + q] = (int32_t)id;
+    ng += k > T ? 1u : 0u;
+    ne += k == T ? 1u : 0u;
+  }
+  uint32_t p = wave_reserve_n<LIST_BITS>(ng, &s.out_gt);
+  uint32_t q = wave_reserve_n<LIST_BITS>(ne, &s.out_tie);
+  if (ng + ne == 0) return;
+  for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
+    const uint32_t k = keys[i];
+    if (k > T) {
+      if (p < K) out[p] = (int32_t)(idx ? idx[i] : i);
+      ++p;
+    } else if (k == T) {
+      if (q < ties && gt_total + q < K) out[gt_total + q] = (int32_t)(idx ? idx[i] : i);
+      ++q;
+    }
   }
 }
 
@@ -571,18 +607,7 @@ __device__ __forceinline__ void admit_batch(const u32x4 (&v)[NQ], const uint32_t
     n += admits<POS>(v[q].z, c.thr) ? 1u : 0u;
     n += admits<POS>(v[q].w, c.thr) ? 1u : 0u;
   }
-  uint32_t total = 0, before = 0;
-#pragma unroll
-  for (int bit = 0; bit < NBITS; ++bit) {
-    const uint64_t m = __ballot((n >> bit) & 1u);
-    total += (uint32_t)__popcll(m) << bit;
-    before += mbcnt64(m) << bit;
-  }
-  if (total == 0) return;
-  const int leader = __builtin_ctzll(__ballot(true));
-  uint32_t b = 0;
-  if ((int)lane_id() == leader) b = atomicAdd(&s.cnt, total);
-  uint32_t pos = (uint32_t)__builtin_amdgcn_readfirstlane(b) + before;
+  uint32_t pos = wave_reserve_n<NBITS>(n, &s.cnt);
   if (n == 0) return;
   auto one = [&](uint32_t u, uint32_t idx) {
     if (admits<POS>(u, c.thr)) {
@@ -1015,24 +1040,36 @@ __device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t bas
   const bool fits = cb <= (uint32_t)FL_CAP;
   // Commit the resolved bins above b; move bin b to the frontier buffer, or, when it
   // is too wide for it, note the extremes of its keys.
-  uint32_t bmn = KEY_MAX, bmx = 0;
+  // Two sweeps over the list: count this thread's keys above the bin and in it (and
+  // note the bin's extremes), reserve their slots once per wave, then write them.
+  uint32_t bmn = KEY_MAX, bmx = 0, ng = 0, nin = 0;
   for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
     const uint32_t k = key_at(i);
-    const uint32_t id = id_at(i);
-    const bool g = k > bhi;
-    const uint32_t p = wave_reserve(g, &s.out_gt);
-    if (g && p < K) out[p] = (int32_t)id;
     const bool in = k >= blo && k <= bhi;
-    if (fits) {
-      const uint32_t f = wave_reserve(in, &s.fl_cnt);
-      if (in && f < (uint32_t)FL_CAP) {
-        s.fl_idx[f] = id;
-        s.fl_key[f] = k;
-      }
-    }
+    ng += k > bhi ? 1u : 0u;
+    nin += in ? 1u : 0u;
     if (in) {
       bmn = min(bmn, k);
       bmx = max(bmx, k);
+    }
+  }
+  {
+    uint32_t p = wave_reserve_n<LIST_BITS>(ng, &s.out_gt);
+    uint32_t f = fits ? wave_reserve_n<LIST_BITS>(nin, &s.fl_cnt) : 0u;
+    if (ng + (fits ? nin : 0u) != 0) {
+      for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
+        const uint32_t k = key_at(i);
+        if (k > bhi) {
+          if (p < K) out[p] = (int32_t)id_at(i);
+          ++p;
+        } else if (fits && k >= blo) {
+          if (f < (uint32_t)FL_CAP) {
+            s.fl_idx[f] = id_at(i);
+            s.fl_key[f] = k;
+          }
+          ++f;
+        }
+      }
     }
   }
   bmn = wave_min_u32(bmn);
@@ -1089,15 +1126,25 @@ __device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t bas
     }
     const uint32_t gt_total = above + gt2;
     const uint32_t ties = K - gt_total;
+    uint32_t ng = 0, ne = 0;
     for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
       const uint32_t k = key_at(i);
-      const uint32_t id = id_at(i);
-      const bool g = k > T && k <= bhi;
-      const uint32_t p = wave_reserve(g, &s.out_gt);
-      if (g && p < K) out[p] = (int32_t)id;
-      const bool e = k == T;
-      const uint32_t q = wave_reserve(e, &s.out_tie);
-      if (e && q < ties && gt_total + q < K) out[gt_total + q] = (int32_t)id;
+      ng += (k > T && k <= bhi) ? 1u : 0u;
+      ne += k == T ? 1u : 0u;
+    }
+    uint32_t p = wave_reserve_n<LIST_BITS>(ng, &s.out_gt);
+    uint32_t q = wave_reserve_n<LIST_BITS>(ne, &s.out_tie);
+    if (ng + ne != 0) {
+      for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
+        const uint32_t k = key_at(i);
+        if (k > T && k <= bhi) {
+          if (p < K) out[p] = (int32_t)id_at(i);
+          ++p;
+        } else if (k == T) {
+          if (q < ties && gt_total + q < K) out[gt_total + q] = (int32_t)id_at(i);
+          ++q;
+        }
+      }
     }
   }
 }
@@ -1157,11 +1204,17 @@ __device__ __forceinline__ void select_taus(uint32_t n_s, uint32_t r0, uint32_t 
   const uint32_t m = s.sel_above + s.hist[b];  // sample keys in bin b and above
   const uint32_t blo = mn + (b << sh);
   if (m <= (uint32_t)FL_CAP) {
-    for (uint32_t i = t; i < n_s; i += BLOCK) {
-      const uint32_t k = s.buf[i];
-      const bool in = k >= blo;
-      const uint32_t f = wave_reserve(in, &s.fl_cnt);
-      if (in && f < (uint32_t)FL_CAP) s.fl_key[f] = k;
+    uint32_t nin = 0;
+    for (uint32_t i = t; i < n_s; i += BLOCK) nin += s.buf[i] >= blo ? 1u : 0u;
+    uint32_t f = wave_reserve_n<LIST_BITS>(nin, &s.fl_cnt);
+    if (nin != 0) {
+      for (uint32_t i = t; i < n_s; i += BLOCK) {
+        const uint32_t k = s.buf[i];
+        if (k >= blo) {
+          if (f < (uint32_t)FL_CAP) s.fl_key[f] = k;
+          ++f;
+        }
+      }
     }
     __syncthreads();
     const uint32_t rk = rank_in_list(s.fl_key, m);
