@@ -651,14 +651,18 @@ __device__ __forceinline__ void admit_quad(const u32x4& v, uint32_t e, const Pas
 // the row's body: a skipped chunk is given an offset past the resource's end, which
 // the hardware answers with zeros and no memory access. The loads stay unconditional
 // in the control flow, so the compiler can still wait for one batch at a time.
+// x[0, L) may be a segment of a row whose element 0 is row element ebase (candidates
+// record row indices); with SKIP the segment must start on a sampled line, and P
+// counts periods from there.
 template <bool POS, bool SKIP>
-__device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, uint32_t n_s, const PassCtx c) {
+__device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, uint32_t n_s, const PassCtx c,
+                                           uint32_t ebase = 0u) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   uint32_t c0l = 0;
   uint32_t head = (uint32_t)((4u - ((uint32_t)((uintptr_t)x >> 2) & 3u)) & 3u);
   if (head > L) head = L;
-  if (t < head) admit_one<POS>(true, x[t], t, c, c0l);
+  if (t < head) admit_one<POS>(true, x[t], ebase + t, c, c0l);
   const uint32_t nv = (L - head) >> 2;
   grow_t body = x + head;
   const uint32_t gb = ((uint32_t)((uintptr_t)x & 127u) >> 2) + head;  // body offset from the line below x
@@ -690,7 +694,7 @@ __device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, uint32_t n_s, c
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
       v[u] = SKIP ? (raw[u] | splat4(inert[u])) : raw[u];
-      e[u] = head + 4u * (it * per + u * BLOCK + t);
+      e[u] = ebase + head + 4u * (it * per + u * BLOCK + t);
     }
     admit_batch<POS, UNROLL>(v, e, c, c0l);
   };
@@ -720,10 +724,10 @@ __device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, uint32_t n_s, c
   for (uint32_t q = nfull * per + t; q < nv; q += BLOCK) {
     uint32_t inert;
     const u32x4 v = fetch(q, inert);
-    admit_quad<POS>(v | splat4(inert), head + 4u * q, c, c0l);
+    admit_quad<POS>(v | splat4(inert), ebase + head + 4u * q, c, c0l);
   }
   const uint32_t tail0 = head + 4u * nv;
-  if (t < L - tail0) admit_one<POS>(true, x[tail0 + t], tail0 + t, c, c0l);
+  if (t < L - tail0) admit_one<POS>(true, x[tail0 + t], ebase + tail0 + t, c, c0l);
   if (c0l != 0) atomicAdd(&s.cnt0, c0l);
 }
 
@@ -733,11 +737,9 @@ __device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, uint32_t n_s, c
 // (a quarter of the row's bytes at stride 128). The sampler therefore reads each
 // sampled line whole: the element at j*128 is still the sample key (the proposal
 // is unchanged), and the line's maximum key is kept alongside it. The full-row pass
-// then reads only the other three lines of every 512-byte period, and a sampled
-// line is read again only if its maximum reaches tau1 (a "hot" line), since no
-// other sampled line can hold an admitted element. Every element is examined
-// exactly once, by the pass or by the hot-line step. It pays where few sampled lines
-// are hot (tau1 deep in the tail of long rows); the host enables it by shape.
+// then skips every sampled line whose maximum is below tau1 (no element of it can be
+// admitted) and reads the "hot" ones again. It pays where few sampled lines are hot
+// (tau1 deep in the tail of long rows); the host enables it by shape.
 //
 // Geometry: offsets are counted in floats from base = x rounded down to a 128-byte
 // line, so element index = offset - off4 with off4 = (x & 127) / 4. The line of
@@ -747,7 +749,7 @@ __device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, uint32_t n_s, c
 // only into the first line of period n_s, which is not sampled.
 
 constexpr uint32_t LINE_SAMPLE_MAX = 8192;              // n_s limit of line sampling
-constexpr int LM_PER_THREAD = LINE_SAMPLE_MAX / BLOCK;  // lines per thread in the hot step
+constexpr int LM_PER_THREAD = LINE_SAMPLE_MAX / BLOCK;  // sampled lines per thread
 static_assert(LINE_SAMPLE_MAX / 32 <= FL_CAP, "the hot-line bitmap lives in the frontier index list");
 static_assert(BLOCK % 64 == 0 && LINE_SAMPLE_MAX % BLOCK == 0, "bitmap words are written per wave");
 constexpr int SAMPLE_UNROLL = 6;
@@ -836,180 +838,6 @@ __device__ __forceinline__ void sample_lines(grow_t x, uint32_t L, uint32_t n_s,
   uint32_t mn = KEY_MAX, mx = 0;
   sample_lines_range<STREAM>(x, L, 0u, n_s, skey, lmax, mn, mx);
   block_minmax(mn, mx);
-}
-
-// Position of the n-th (from 0) set bit of m; requires n < popcount(m).
-__device__ __forceinline__ uint32_t nth_set_bit(uint64_t m, uint32_t n) {
-  uint32_t w = (uint32_t)m, pos = 0;
-  uint32_t c = (uint32_t)__popc(w);
-  if (n >= c) {
-    n -= c;
-    pos = 32;
-    w = (uint32_t)(m >> 32);
-  }
-#pragma unroll
-  for (uint32_t half = 16; half >= 1; half >>= 1) {
-    c = (uint32_t)__popc(w & ((1u << half) - 1u));
-    if (n >= c) {
-      n -= c;
-      pos += half;
-      w >>= half;
-    }
-  }
-  return pos;
-}
-
-// Re-reads the sampled lines whose maximum reaches tau1 and admits their elements.
-// Bit m of hot_mask is set when line j0 + t + m*BLOCK is hot. Eight lanes read one
-// hot line (one 16-byte chunk each): for every slot m the wave's ballot names the
-// threads that own a hot line, and the n-th of them goes to lane group n % 8 in round
-// n / 8. Slots are taken HOT_SLOTS at a time with every load of a round in flight
-// together, so a row costs a few memory latencies rather than one per slot.
-template <bool POS>
-__device__ __forceinline__ void hot_lines(grow_t x, uint32_t L, uint32_t j0, uint32_t hot_mask, const PassCtx c) {
-  Smem& s = g_s;
-  constexpr int HOT_SLOTS = 8;
-  static_assert(LM_PER_THREAD % HOT_SLOTS == 0, "slot groups must tile the slots");
-  const uint32_t t = threadIdx.x, lane = lane_id();
-  const uint32_t wbase = t - lane;          // first thread of this wave
-  const uint32_t grp = lane >> 3, ch = lane & 7u;
-  constexpr uint32_t NA = never_admitted<POS>();
-  uint32_t c0l = 0;
-  const uint32_t off4 = (uint32_t)((uintptr_t)x & 127u) >> 2;
-  grow_t base = x - off4;
-  const uint32_t lo = off4, hi = off4 + L;
-  const uint32_t gfirst = off4 & ~3u, glast = (hi - 1u) & ~3u;
-#pragma unroll 1
-  for (int mb = 0; mb < LM_PER_THREAD; mb += HOT_SLOTS) {
-    uint64_t b[HOT_SLOTS];
-    uint32_t nb[HOT_SLOTS];
-    uint32_t rounds = 0;
-#pragma unroll
-    for (int u = 0; u < HOT_SLOTS; ++u) {
-      b[u] = __ballot((hot_mask >> (mb + u)) & 1u);
-      nb[u] = (uint32_t)__popcll(b[u]);
-      rounds = max(rounds, (nb[u] + 7u) >> 3);
-    }
-#pragma unroll 1
-    for (uint32_t r = 0; r < rounds; ++r) {
-      u32x4 v[HOT_SLOTS];
-      uint32_t e[HOT_SLOTS];
-      const uint32_t n = 8u * r + grp;
-#pragma unroll
-      for (int u = 0; u < HOT_SLOTS; ++u) {
-        const bool ok = n < nb[u];
-        const uint32_t owner = ok ? nth_set_bit(b[u], n) : 0u;
-        const uint32_t j = j0 + wbase + owner + (uint32_t)(mb + u) * BLOCK;
-        const uint32_t g = 128u * j + 4u * ch;
-        // Lanes without a line, and chunks outside the row, read an in-bounds chunk of
-        // the row instead; their elements are masked out below.
-        const uint32_t ga = !ok ? gfirst : (g < gfirst ? gfirst : (g < glast ? g : glast));
-        u32x4 w = load4(base + ga);
-        w.x = (ok && g + 0 >= lo && g + 0 < hi) ? w.x : NA;
-        w.y = (ok && g + 1 >= lo && g + 1 < hi) ? w.y : NA;
-        w.z = (ok && g + 2 >= lo && g + 2 < hi) ? w.z : NA;
-        w.w = (ok && g + 3 >= lo && g + 3 < hi) ? w.w : NA;
-        v[u] = w;
-        e[u] = g - off4;
-      }
-      admit_batch<POS, HOT_SLOTS>(v, e, c, c0l);
-    }
-  }
-  if (c0l != 0) atomicAdd(&s.cnt0, c0l);
-}
-
-// Offset of chunk k of the non-sampled lines: period k / 24, line 1 + (k % 24) / 8,
-// chunk k % 8.
-__device__ __forceinline__ uint32_t unsampled_offset(uint32_t k) {
-  const uint32_t p = k / 24u;
-  const uint32_t r = k - 24u * p;
-  return 128u * p + 32u * (1u + (r >> 3)) + 4u * (r & 7u);
-}
-
-// Loads the chunk at offset g, or the row's last chunk when g lies past the row, so
-// the load is unconditional and always in bounds (the loads of a batch then stay
-// back to back). Elements at or past the row end are masked when examined.
-__device__ __forceinline__ u32x4 load_chunk(grow_t base, uint32_t g, uint32_t glast) {
-  return load4_stream(base + (g < glast ? g : glast));
-}
-
-// Replaces every element of the chunk at offset g that lies at or past the row end
-// hi with a value that is never admitted.
-template <bool POS>
-__device__ __forceinline__ u32x4 mask_tail(u32x4 v, uint32_t g, uint32_t hi) {
-  constexpr uint32_t NA = never_admitted<POS>();
-  v.x = (g + 0 >= hi) ? NA : v.x;
-  v.y = (g + 1 >= hi) ? NA : v.y;
-  v.z = (g + 2 >= hi) ? NA : v.z;
-  v.w = (g + 3 >= hi) ? NA : v.w;
-  return v;
-}
-
-// The full-row pass over the non-sampled lines (see the geometry note above).
-// Chunks k0 <= k < k1 of the non-sampled lines; with tail set, also the first line of
-// period n_s (which the row may reach into and which is never sampled).
-template <bool POS>
-__device__ __forceinline__ void fused_pass_lines(grow_t x, uint32_t L, uint32_t n_s, uint32_t k0, uint32_t k1,
-                                                 bool tail, const PassCtx c) {
-  Smem& s = g_s;
-  const uint32_t t = threadIdx.x;
-  uint32_t c0l = 0;
-  const uint32_t off4 = (uint32_t)((uintptr_t)x & 127u) >> 2;
-  grow_t base = x - off4;
-  const uint32_t hi = off4 + L;
-  const uint32_t glast = (hi - 1u) & ~3u;  // chunk holding the row's last element
-  const uint32_t nk = k1 - k0;
-  const uint32_t per = BLOCK * UNROLL;
-  const uint32_t nfull = nk / per;
-  auto examine = [&](const u32x4 (&raw)[UNROLL], uint32_t it) {
-    u32x4 v[UNROLL];
-    uint32_t e[UNROLL];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const uint32_t g = unsampled_offset(k0 + it * per + u * BLOCK + t);
-      v[u] = mask_tail<POS>(raw[u], g, hi);
-      e[u] = g - off4;
-    }
-    admit_batch<POS, UNROLL>(v, e, c, c0l);
-  };
-  auto fetch = [&](u32x4 (&v)[UNROLL], uint32_t it) {
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) v[u] = load_chunk(base, unsampled_offset(k0 + it * per + u * BLOCK + t), glast);
-  };
-  if (nfull > 0) {
-    // Two batch buffers in ping-pong: while one batch is examined the next one is in
-    // flight, with no register copies between iterations (a copy would force the
-    // compiler to wait for the prefetch).
-    u32x4 a[UNROLL], b[UNROLL];
-    fetch(a, 0);
-    uint32_t it = 0;
-    for (; it + 2 < nfull; it += 2) {
-      fetch(b, it + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      examine(a, it);
-      fetch(a, it + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      examine(b, it + 1);
-    }
-    if (it + 1 < nfull) {
-      fetch(b, it + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      examine(a, it);
-      examine(b, it + 1);
-    } else {
-      examine(a, it);
-    }
-  }
-  for (uint32_t k = k0 + nfull * per + t; k < k1; k += BLOCK) {
-    const uint32_t g = unsampled_offset(k);
-    admit_quad<POS>(mask_tail<POS>(load_chunk(base, g, glast), g, hi), g - off4, c, c0l);
-  }
-  // The first line of period n_s, if the row reaches into it (never sampled).
-  if (tail && t < 8) {
-    const uint32_t g = 128u * n_s + 4u * t;
-    if (g < hi) admit_quad<POS>(mask_tail<POS>(load_chunk(base, g, glast), g, hi), g - off4, c, c0l);
-  }
-  if (c0l != 0) atomicAdd(&s.cnt0, c0l);
 }
 
 // Boundary refinement and commit of an LDS list of n keys whose first histogram,
@@ -1850,22 +1678,28 @@ void split_pass_kernel(Params p) {
   }
   const PassCtx c = pass_ctx(t1key, rs->t0key, rs->mx);
   grow_t x = (grow_t)(p.scores) + (size_t)row * p.N;
+  // This part covers the sample periods [q0, q1): row elements [e0, e1), where period
+  // P starts at offset 128 P from the 128-byte line below x (the last part runs to the
+  // row's end, which may reach one element line past its last sampled period).
   const uint32_t q0 = (uint32_t)((uint64_t)part * n_s / p.pp);
   const uint32_t q1 = (uint32_t)((uint64_t)(part + 1) * n_s / p.pp);
-  uint32_t hot_mask = 0;
+  const uint32_t off4 = (uint32_t)((uintptr_t)x & 127u) >> 2;
+  const uint32_t e0 = q0 == 0u ? 0u : 128u * q0 - off4;
+  const uint32_t e1 = part == p.pp - 1 ? L : (q1 == 0u ? 0u : 128u * q1 - off4);
+  // Bitmap of this part's hot sampled lines (bit P - q0), as in the one-workgroup pass.
 #pragma unroll
   for (int m = 0; m < LM_PER_THREAD; ++m) {
-    const uint32_t j = q0 + t + (uint32_t)m * BLOCK;
-    if (j < q1 && rs->lmax[j] >= t1key) hot_mask |= 1u << m;
+    const uint32_t j = t + (uint32_t)m * BLOCK;
+    const uint64_t hb = __ballot(q0 + j < q1 && rs->lmax[q0 + j] >= t1key);
+    if (lane_id() == 0) {
+      s.fl_idx[j >> 5] = (uint32_t)hb;
+      s.fl_idx[(j >> 5) + 1] = (uint32_t)(hb >> 32);
+    }
   }
   reset_row_state();
-  const bool tail = part == p.pp - 1;
-  if (t1key >= 0x80000000u) {
-    hot_lines<true>(x, L, q0, hot_mask, c);
-    fused_pass_lines<true>(x, L, n_s, 24u * q0, 24u * q1, tail, c);
-  } else {
-    hot_lines<false>(x, L, q0, hot_mask, c);
-    fused_pass_lines<false>(x, L, n_s, 24u * q0, 24u * q1, tail, c);
+  if (e1 > e0) {
+    if (t1key >= 0x80000000u) fused_pass<true, true>(x + e0, e1 - e0, q1 - q0, c, e0);
+    else fused_pass<false, true>(x + e0, e1 - e0, q1 - q0, c, e0);
   }
   __syncthreads();
   // Merge into the row: one atomic reserves this workgroup's candidate range.
