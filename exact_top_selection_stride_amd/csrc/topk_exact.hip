@@ -1988,12 +1988,15 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
   p.rs = nullptr;
   p.ps = 1;
   p.pp = 1;
-  // Execution by shape. Row-split when rows are few (at most a quarter of the
-  // resident workgroup slots) and long: their scan and sampling are divided among
-  // several workgroups. Measured on MI355X (512 resident slots), row-split is 4x
-  // faster for 1-32 rows of 1M and 1.1-1.6x at 128 rows, even at 256 rows and
-  // slower at 512, where one workgroup per row already fills the chip and the extra
-  // kernel boundaries and merges cost more than they save. Persistent execution
+  // Execution by shape. Row-split when rows are few and long: their scan and
+  // sampling are divided among several workgroups. Measured on MI355X (512 resident
+  // slots, graph replays): for rows of 1M, row-split takes 44-62 us for 1-32 rows
+  // against 224-241 us, 146 against 240 us at 128 rows, about even at 256 and slower
+  // at 512, where one workgroup per row already fills the chip and the extra kernel
+  // boundaries and merges cost more than they save; for rows of 128K it wins up to
+  // 64 rows (44 against 52 us) and loses from 128 (60 against 55 us). So: at most a
+  // quarter of the resident slots for rows of 256K and more, an eighth for rows of
+  // 64K-256K. Persistent execution
   // for many long rows per resident workgroup. One workgroup per row otherwise
   // (equal to persistent on 0.5-1M-wide rows, faster on short rows, where the
   // per-row loop overhead is not amortised).
@@ -2010,7 +2013,8 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
   p.line_min = (p.mode == TOPK_PATH_SAMPLED) ? 0u : p.T1;
   bool split = M <= (int64_t)RS_MAX_ROWS &&
                (ex == TOPK_EXEC_ROWSPLIT || p.mode == TOPK_PATH_ROWSPLIT ||
-                (ex == TOPK_EXEC_AUTO && 4 * M <= resident && N_alloc >= ROWSPLIT_MIN_N));
+                (ex == TOPK_EXEC_AUTO && N_alloc >= ROWSPLIT_MIN_N &&
+                 (N_alloc >= 4 * ROWSPLIT_MIN_N ? 4 * M <= resident : 8 * M <= resident)));
   if (split && !st->rs) {
     if (capturing) {
       split = false;  // no state and no allocation under capture: run unsplit (same result)

@@ -127,8 +127,8 @@ int topk_exact_reset_stats(hipStream_t stream);
 int topk_exact_set_path_override(int mode);
 
 /* Selects how rows map to workgroups for later calls (TOPK_EXEC_*). Auto uses
- * row-split when M is at most a quarter of the resident workgroup count and
- * N_alloc >= 65536,
+ * row-split when N_alloc >= 65536 and M is at most a quarter (N_alloc >= 262144) or an
+ * eighth (shorter rows) of the resident workgroup count,
  * persistent execution when M is at least four times the resident workgroup count
  * and N_alloc >= 262144, and one workgroup per row otherwise. Every mode gives a
  * result satisfying the same contract; a captured graph keeps the mode set when it
