@@ -144,7 +144,7 @@ struct Params {
   uint32_t pp;          // row-split: workgroups per row passing
 };
 
-struct Smem {
+struct alignas(16) Smem {
   uint32_t buf[2 * CAP];       // candidates: idx in [0,CAP), key in [CAP,2CAP); or keys only
   uint32_t hist[NB];
   uint32_t fl_idx[FL_CAP];
@@ -355,15 +355,20 @@ __device__ void select_rank(ForKeys&& for_keys, uint32_t r, uint32_t lo, uint32_
 
 // For a short key list in LDS (m <= BLOCK): thread i < m returns the number of keys
 // ahead of keys[i] in the strict order (key descending, position ascending).
+// keys must be 16-byte aligned: they are read four at a time, several reads in flight.
 __device__ __forceinline__ uint32_t rank_in_list(const uint32_t* keys, uint32_t m) {
   const uint32_t i = threadIdx.x;
   if (i >= m) return KEY_MAX;
   const uint32_t ki = keys[i];
-  uint32_t r = 0;
-  for (uint32_t j = 0; j < m; ++j) {
-    const uint32_t kj = keys[j];
-    r += (kj > ki || (kj == ki && j < i)) ? 1u : 0u;
+  auto ahead = [&](uint32_t kj, uint32_t j) -> uint32_t { return (kj > ki || (kj == ki && j < i)) ? 1u : 0u; };
+  uint32_t r = 0, j = 0;
+  const uint32_t m4 = m & ~3u;
+#pragma unroll 4
+  for (; j < m4; j += 4) {
+    const u32x4 k4 = *reinterpret_cast<const u32x4*>(keys + j);
+    r += ahead(k4.x, j) + ahead(k4.y, j + 1) + ahead(k4.z, j + 2) + ahead(k4.w, j + 3);
   }
+  for (; j < m; ++j) r += ahead(keys[j], j);
   return r;
 }
 
