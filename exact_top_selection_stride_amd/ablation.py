@@ -1,7 +1,7 @@
 """Ablation harness for the proposal mechanism on MI355X.
 
 Sweeps the sample stride s and the primary target rho0 (secondary rho1 = rho0 + 0.25)
-of the sampled path, and the direct exact proposal, over the short-row widths where
+of the sampled path, the direct exact proposal and the default dispatch, over the short-row widths where
 the pages place the crossover between sampled and exact proposals (page
 "几何平均快 1.55 倍，但短行采样会输：腾讯怎么测精确 Top-K", section
 "采样不是处处都该开": stride and target ablations, sampled against exact proposal at
@@ -72,10 +72,15 @@ def main(argv=None):
                   for g in range(w.groups)]
         outs = [torch.empty((w.M, K), dtype=torch.int32, device=dev) for _ in groups]
         tk.reserve(w.M, w.n_alloc, K)
-        settings = [("direct", 128, 1.5, 1.75)]
+        # "auto" is the library's own choice at the method's stride and targets: direct
+        # up to 16K, above that the sampled path with element-wise sampling (line
+        # sampling, which the forced sampled path uses at stride 128, is reserved for
+        # the longest rows).
+        settings = [("direct", 128, 1.5, 1.75), ("auto", 128, 1.5, 1.75)]
         settings += [("sampled", s, r, r + 0.25) for s in args.strides for r in args.rho0]
+        paths = {"direct": tk.PATH_DIRECT, "auto": tk.PATH_AUTO, "sampled": tk.PATH_SAMPLED}
         for mode, stride, rho0, rho1 in settings:
-            path = tk.PATH_DIRECT if mode == "direct" else tk.PATH_SAMPLED
+            path = paths[mode]
             with tk.path_override(path), tk.proposal(stride, rho0, rho1):
                 tk.reset_stats()
                 for g, (s, l) in enumerate(groups):
