@@ -49,11 +49,37 @@ def parse():
     return ap.parse_args()
 
 
+def _code_tokens(text: str) -> str:
+    """C/C++ source with comments removed and whitespace collapsed (string literals kept)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"' or c == "'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_digest() -> str:
+    """Digest of the selector's code (comments and layout ignored): counter summaries taken
+    on one digest describe exactly the kernels of any source with the same digest."""
     h = hashlib.sha256()
     for rel in ("exact_top_selection_stride_amd/csrc/topk_exact.hip", "include/topk_exact.h"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -17,21 +17,23 @@
 //      a. the fixed-stride view x[j*128] proposes tau0 (target 1.5K
 //         candidates) and the nested, wider tau1 (target 1.75K) as ranks of
 //         the sample ([Cx] section "采样不是处处都该开"; [PD] question 2). On
-//         the longest rows the sampled 128-byte lines are read whole and
-//         skipped by the full pass (line sampling, below);
+//         the long rows the sampled 128-byte lines are read whole, and the
+//         full pass skips those whose maximum is below tau1 (line sampling,
+//         below);
 //      b. one mandatory full-row pass reads the row with 128-bit non-temporal
-//         loads, admits keys >= tau1 into an LDS candidate buffer by wave
-//         ballot and prefix count, counts C(tau0) and C(tau1), and builds the
-//         first radix histogram of the admitted keys ([PD] question 2, Fig. 4
-//         stage 2; [AX]);
+//         loads, admits keys >= tau1 into an LDS candidate buffer (per-lane
+//         counts, one slot reservation per wave and batch), counts C(tau0)
+//         and C(tau1), and builds the first radix histogram of the admitted
+//         keys ([PD] question 2, Fig. 4 stage 2; [AX]);
 //      c. certification: C(tau0) >= K, else C(tau1) >= K (the nested set is
 //         already in LDS, so this fallback rereads nothing), else exact
 //         full-row recovery; a candidate overflow also goes to recovery.
 //         Nothing is written before this decision ([PD] question 2; [AX]);
 //      d. refinement on the unresolved boundary only: bins above the bin that
 //         holds rank K are committed at once, that bin's candidates move to a
-//         small frontier buffer and radix digits narrow it until the K-th key
-//         is exact ([PD] question 2, Fig. 4 stage 3).
+//         small frontier buffer, where the K-th key is found exactly (rank
+//         counting, or radix digits narrowing the bin) ([PD] question 2, Fig. 4
+//         stage 3).
 //   4. Exact full-row recovery is a radix select over the whole row, run after
 //      the selector by three small kernels that spread the queued rows over the
 //      GPU: a histogram pass, a pass that commits every key above the boundary
