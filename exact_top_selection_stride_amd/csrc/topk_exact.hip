@@ -1797,30 +1797,33 @@ __global__ void zero_stats_kernel(Control* ctl) {
 }
 
 // Plain streaming read for the measured-ceiling report: workgroup b reads the
-// contiguous span [b*span, (b+1)*span) of 16-byte chunks with non-temporal loads (as
-// the full-row pass does), eight independent loads per lane per step, and folds the
-// bits so the loads cannot be elided.
+// contiguous chunk [b*PROBE_CHUNK, (b+1)*PROBE_CHUNK) of 16-byte elements (4 MiB, a
+// 1M-float row) with non-temporal loads, as the full-row pass does, four loads per lane
+// in flight, and folds the bits so the loads cannot be elided. Workgroups are
+// dispatched in address order, so the chunks read at any time are neighbours, as the
+// rows of a selector call are. (A grid of a few hundred workgroups each streaming one
+// far-apart span measured 8% slower on a 32 GiB buffer: 6.48 against 7.02 TB/s.)
+constexpr uint64_t PROBE_CHUNK = 1ull << 18;
 __global__ __launch_bounds__(BLOCK) void stream_read_probe_kernel(const float* __restrict__ x, uint64_t n,
                                                                   float* __restrict__ sink) {
   const u32x4* p4 = reinterpret_cast<const u32x4*>(x);
   const uint64_t nv = n >> 2;
-  const uint64_t span = (nv + gridDim.x - 1) / gridDim.x;
-  const uint64_t beg = (uint64_t)blockIdx.x * span;
-  const uint64_t end = beg + span < nv ? beg + span : nv;
+  const uint64_t beg = (uint64_t)blockIdx.x * PROBE_CHUNK;
+  const uint64_t end = beg + PROBE_CHUNK < nv ? beg + PROBE_CHUNK : nv;
   uint32_t acc = 0;
   uint64_t q = beg + threadIdx.x;
-  for (; q + 7 * BLOCK < end; q += 8 * BLOCK) {
-    u32x4 v[8];
+  for (; q + 3 * BLOCK < end; q += 4 * BLOCK) {
+    u32x4 v[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(&p4[q + (uint64_t)u * BLOCK]);
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(&p4[q + (uint64_t)u * BLOCK]);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   for (; q < end; q += BLOCK) {
-    const u32x4 a = p4[q];
+    const u32x4 a = __builtin_nontemporal_load(&p4[q]);
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
-  if (blockIdx.x == 0) {
+  if (blockIdx.x == gridDim.x - 1) {
     const uint32_t* xu = reinterpret_cast<const uint32_t*>(x);
     for (uint64_t i = 4 * nv + threadIdx.x; i < n; i += BLOCK) acc ^= xu[i];
   }
@@ -1831,7 +1834,7 @@ __global__ __launch_bounds__(BLOCK) void stream_read_probe_kernel(const float* _
   if (threadIdx.x == 0) {
     uint32_t v = 0;
     for (int i = 0; i < NWAVES; ++i) v ^= w[i];
-    sink[blockIdx.x] = __uint_as_float(v);
+    sink[blockIdx.x & 4095u] = __uint_as_float(v);
   }
 }
 
@@ -2195,11 +2198,10 @@ int topk_stream_read_probe(const float* x, int64_t n, float* sink, hipStream_t s
   DevState* st = nullptr;
   rc = get_state(capturing, &st);
   if (rc != TOPK_OK) return rc;
-  // Two workgroups per CU (the selector's residency), fewer for small inputs.
-  int64_t want = (n / 4 + BLOCK * 8 - 1) / (BLOCK * 8);
-  int64_t cap = (int64_t)st->n_cu * 2;
-  if (cap > 4096) cap = 4096;
-  const unsigned grid = (unsigned)(want < 1 ? 1 : (want < cap ? want : cap));
+  // One workgroup per 4 MiB chunk (at least one, for the tail elements).
+  const int64_t chunks = (n / 4 + (int64_t)PROBE_CHUNK - 1) / (int64_t)PROBE_CHUNK;
+  if (chunks > (int64_t)INT32_MAX) return fail(TOPK_ERR_BAD_SHAPE, "n = %lld is too large", (long long)n);
+  const unsigned grid = (unsigned)(chunks < 1 ? 1 : chunks);
   hipLaunchKernelGGL(stream_read_probe_kernel, dim3(grid), dim3(BLOCK), 0, stream, x, (uint64_t)n, sink);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch stream_read_probe_kernel");

@@ -162,9 +162,10 @@ int topk_exact_time_next_call(hipEvent_t start, hipEvent_t stop);
 const char* topk_exact_last_error(void);
 
 /* Bandwidth probe (measurement only, not part of the selection): reads n floats from
- * `x` (device) with the same 128-bit non-temporal loads as the selector's full-row pass and
- * writes one float per workgroup into `sink` (device, >= 4096 floats) so the reads
- * cannot be elided. Used to report a measured HBM read ceiling next to the peak. */
+ * `x` (device, 16-byte aligned) with the same 128-bit non-temporal loads as the selector's
+ * full-row pass, one workgroup per consecutive 4 MiB chunk, and writes one float per
+ * workgroup into `sink` (device, >= 4096 floats; workgroup b writes slot b mod 4096) so the
+ * reads cannot be elided. Used to report a measured HBM read ceiling next to the peak. */
 int topk_stream_read_probe(const float* x, int64_t n, float* sink, hipStream_t stream);
 
 #ifdef __cplusplus

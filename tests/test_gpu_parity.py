@@ -345,6 +345,16 @@ def test_consecutive_calls_reuse_the_ticket():
             _check(s[:M], l[:M], out, label=f"M={M}")
 
 
+def test_stream_read_probe_sizes():
+    # The measurement probe (one workgroup per 4 MiB chunk) on sizes below one chunk, with
+    # a ragged tail, and over several chunks; it only has to run cleanly.
+    sink = torch.zeros(4096, device=DEV)
+    for n in (1, 3, 4, 1000, (1 << 20) + 5, 12 * (1 << 20) + 7):
+        x = torch.randn(n, device=DEV)
+        tk.stream_read_probe(x, sink)
+        torch.cuda.synchronize()
+
+
 def test_selector_timing_hook():
     # The hook's events bracket the selector kernels inside the call's own events.
     s, l = _window_rows("c1", [(0, 64)])
