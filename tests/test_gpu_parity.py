@@ -335,6 +335,46 @@ def test_wide_boundary_bin_of_ties(two_keys):
                 assert st["frontier_wide"] == 4
 
 
+def _random_case(seed):
+    """A seeded random shape: width, rows, K, lengths (0, <= K, near the width) and one of
+    several value families (continuous, bf16-rounded, few distinct values, signed)."""
+    rng = np.random.default_rng(seed)
+    n_alloc = int(rng.choice([3000, 8192, 20001, 65536, 131073, 300007]))
+    M = int(rng.integers(1, 9))
+    Kr = int(rng.choice([1, 64, 2048, 3000]))
+    lens = rng.integers(0, n_alloc + 1, size=M)
+    lens[rng.random(M) < 0.25] = n_alloc
+    lens[rng.random(M) < 0.15] = min(Kr, n_alloc)
+    family = seed % 4
+    if family == 0:
+        x = rng.normal(30.0, 2.5, size=(M, n_alloc)).astype(np.float32)
+        tail = rng.random((M, n_alloc)) < 0.01
+        x[tail] = (45.0 + rng.exponential(3.0, size=int(tail.sum()))).astype(np.float32)
+    elif family == 1:
+        x = torch.from_numpy(rng.normal(30.0, 2.5, size=(M, n_alloc)).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    elif family == 2:
+        x = rng.integers(0, 5, size=(M, n_alloc)).astype(np.float32)
+    else:
+        x = rng.standard_normal((M, n_alloc)).astype(np.float32) * np.float32(1e-3)
+        x[:, ::7] = -x[:, ::7]
+    cols = np.arange(n_alloc)[None, :]
+    x[cols >= lens[:, None]] = -np.inf
+    return (torch.from_numpy(x).to(DEV), torch.from_numpy(lens.astype(np.int32)).to(DEV), Kr, n_alloc)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_every_mode(seed):
+    # Seeded random widths, row counts, K, lengths and value families, in every forced
+    # path and every execution mode; each result is checked against the oracle.
+    s, l, Kr, n_alloc = _random_case(seed)
+    for execution in (tk.EXEC_AUTO, tk.EXEC_PERSISTENT, tk.EXEC_ROW_PER_WG, tk.EXEC_ROWSPLIT):
+        for mode in (tk.PATH_AUTO, tk.PATH_SAMPLED, tk.PATH_DIRECT, tk.PATH_RECOVERY):
+            with tk.execution(execution):
+                out, st = _run(s, l, K=Kr, mode=mode)
+            _check(s, l, out, K=Kr, label=f"seed {seed} n_alloc {n_alloc} M {s.shape[0]} K {Kr} exec {execution} mode {mode}")
+            assert st["rows"] == s.shape[0]
+
+
 def test_consecutive_calls_reuse_the_ticket():
     # Row tickets rewind after every call: calls of different M back to back.
     s, l = _window_rows("c1", [(0, 40)])
