@@ -230,23 +230,50 @@ __device__ __forceinline__ uint32_t wave_reserve_n(uint32_t cnt, uint32_t* count
 constexpr int LIST_BITS = 6;
 static_assert((KEYS_CAP + BLOCK - 1) / BLOCK < (1 << LIST_BITS), "per-thread list counts fit LIST_BITS");
 
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-  for (int o = WAVE / 2; o >= 1; o >>= 1) v = min(v, (uint32_t)__shfl_xor(v, o));
+// Cross-lane steps through DPP (GFX9 family controls): row_shr:n moves each lane's value
+// n lanes up within its row of 16; row_bcast:15 / row_bcast:31 pass lane 15 / 31 on to
+// the following row(s), which the row mask selects. Lanes that receive nothing keep
+// `old`. Each step is one VALU instruction, where a shuffle is an LDS round trip.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+constexpr int DPP_ROW_SHR = 0x110;      // + n, n in 1..15
+constexpr int DPP_ROW_BCAST15 = 0x142;
+constexpr int DPP_ROW_BCAST31 = 0x143;
+
+// Inclusive scan over the 64 lanes of a wave (every lane active): a within-row
+// Kogge-Stone scan, then row totals carried into rows 1, 3 and 2, 3.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += dpp<DPP_ROW_SHR + 1>(0u, v);
+  v += dpp<DPP_ROW_SHR + 2>(0u, v);
+  v += dpp<DPP_ROW_SHR + 4>(0u, v);
+  v += dpp<DPP_ROW_SHR + 8>(0u, v);
+  v += dpp<DPP_ROW_BCAST15, 0xa>(0u, v);
+  v += dpp<DPP_ROW_BCAST31, 0xc>(0u, v);
   return v;
+}
+
+// Minimum / maximum over the wave (every lane active), returned to every lane: the
+// same scan structure leaves the result in lane 63.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp<DPP_ROW_SHR + 1>(KEY_MAX, v));
+  v = min(v, dpp<DPP_ROW_SHR + 2>(KEY_MAX, v));
+  v = min(v, dpp<DPP_ROW_SHR + 4>(KEY_MAX, v));
+  v = min(v, dpp<DPP_ROW_SHR + 8>(KEY_MAX, v));
+  v = min(v, dpp<DPP_ROW_BCAST15, 0xa>(KEY_MAX, v));
+  v = min(v, dpp<DPP_ROW_BCAST31, 0xc>(KEY_MAX, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, WAVE - 1);
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  for (int o = WAVE / 2; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor(v, o));
-  return v;
-}
-
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const uint32_t l = lane_id();
-  for (int o = 1; o < WAVE; o <<= 1) {
-    const uint32_t n = __shfl_up(v, o);
-    if (l >= (uint32_t)o) v += n;
-  }
-  return v;
+  v = max(v, dpp<DPP_ROW_SHR + 1>(0u, v));
+  v = max(v, dpp<DPP_ROW_SHR + 2>(0u, v));
+  v = max(v, dpp<DPP_ROW_SHR + 4>(0u, v));
+  v = max(v, dpp<DPP_ROW_SHR + 8>(0u, v));
+  v = max(v, dpp<DPP_ROW_BCAST15, 0xa>(0u, v));
+  v = max(v, dpp<DPP_ROW_BCAST31, 0xc>(0u, v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, WAVE - 1);
 }
 
 // Smallest shift such that span >> shift fits in NB bins (at most 21).
