@@ -199,7 +199,7 @@ __device__ __forceinline__ uint32_t wave_reserve(bool pred, uint32_t* counter) {
     const int leader = __builtin_ctzll(m);
     uint32_t b = 0;
     if ((int)lane_id() == leader) b = atomicAdd(counter, (uint32_t)__popcll(m));
-    base = __shfl(b, leader);
+    base = (uint32_t)__builtin_amdgcn_readlane((int)b, leader);
   }
   return base + mbcnt64(m);
 }
@@ -234,10 +234,13 @@ static_assert((KEYS_CAP + BLOCK - 1) / BLOCK < (1 << LIST_BITS), "per-thread lis
 // n lanes up within its row of 16; row_bcast:15 / row_bcast:31 pass lane 15 / 31 on to
 // the following row(s), which the row mask selects. Lanes that receive nothing keep
 // `old`. Each step is one VALU instruction, where a shuffle is an LDS round trip.
-template <int CTRL, int ROW_MASK = 0xf>
+template <int CTRL, int ROW_MASK = 0xf, int BANK_MASK = 0xf>
 __device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xf, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, BANK_MASK, false);
 }
+constexpr int DPP_QUAD_SWAP1 = 0xB1;    // quad_perm [1, 0, 3, 2]
+constexpr int DPP_QUAD_SWAP2 = 0x4E;    // quad_perm [2, 3, 0, 1]
+constexpr int DPP_ROW_SHL = 0x100;      // + n, n in 1..15
 constexpr int DPP_ROW_SHR = 0x110;      // + n, n in 1..15
 constexpr int DPP_ROW_BCAST15 = 0x142;
 constexpr int DPP_ROW_BCAST31 = 0x143;
@@ -609,7 +612,7 @@ __device__ __forceinline__ void admit_one(bool valid, uint32_t u, uint32_t e, co
   const int leader = __builtin_ctzll(m);
   uint32_t b = 0;
   if ((int)lane_id() == leader) b = atomicAdd(&s.cnt, (uint32_t)__popcll(m));
-  const uint32_t pos = __shfl(b, leader) + mbcnt64(m);
+  const uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)b, leader) + mbcnt64(m);
   if (pred) {
     const uint32_t k = key_of_bits(u);
     if (pos < (uint32_t)CAP) {
@@ -828,9 +831,12 @@ __device__ __forceinline__ void sample_lines_range(grow_t x, uint32_t L, uint32_
       if (j < j1 && g + 1 >= lo && g + 1 < hi) m = max(m, key_of_bits(v[u].y));
       if (j < j1 && g + 2 >= lo && g + 2 < hi) m = max(m, key_of_bits(v[u].z));
       if (j < j1 && g + 3 >= lo && g + 3 < hi) m = max(m, key_of_bits(v[u].w));
-      m = max(m, (uint32_t)__shfl_xor(m, 1));
-      m = max(m, (uint32_t)__shfl_xor(m, 2));
-      m = max(m, (uint32_t)__shfl_xor(m, 4));
+      // Maximum over the line's eight lanes: within each quad, then the two quads of
+      // the eight-lane group exchange through row shifts by 4 limited to their banks.
+      m = max(m, dpp<DPP_QUAD_SWAP1>(0u, m));
+      m = max(m, dpp<DPP_QUAD_SWAP2>(0u, m));
+      m = max(m, dpp<DPP_ROW_SHR + 4, 0xf, 0xa>(0u, m));
+      m = max(m, dpp<DPP_ROW_SHL + 4, 0xf, 0x5>(0u, m));
       if (j < j1) {
         if (c == 0) lmax[j] = m;
         if (c == cs) {
