@@ -158,3 +158,93 @@ def valid_score_bytes(lengths: torch.Tensor, K: int) -> int:
     """Bytes of valid FP32 scores a selector must read: 4 * sum of L over rows with L > K."""
     L = lengths.to(torch.int64)
     return int(4 * L[L > K].sum().item())
+
+
+# ---------------------------------------------------------------------------
+# Indexer inputs for the score + select chain.
+#
+# The selector's scores come from a DSA-style indexer (page "LiteTopK: Exploiting
+# the Curse of Dimensionality for a Fused Indexer-TopK Kernel ...", section
+# 核心公式, Eq. (1)) computed by an FP8 multi-query score kernel (page
+# "几何平均快 1.55 倍，但短行采样会输：腾讯怎么测精确 Top-K", section "框架轨迹").
+# Neither the model nor its weights are available, so q, k and w are drawn here.
+# Recipe, in this draw order from one generator:
+#   g  ~ Normal(0, 1)^D                         one shared "topic" direction
+#   q[t, h, :] = 0.25 * g + Normal(0, 1)^D      rounded to FP8 E4M3
+#   hot[s]     = Uniform(0, 1) < hot_p          (1% of keys)
+#   k[s, :]    = Normal(0, 1)^D + hot[s] * g    rounded to FP8 E4M3
+#   w[t, h]    ~ (0.5 + 0.5 * Normal(0, 1)) / sqrt(H)   float32, mostly positive
+# Hot keys align with every query's shared component and form the upper tail of
+# each score row; the cold keys form a dense body (the concentration the LiteTopK
+# review reports for real indexer scores). Lengths are the causal window
+# lengths of the selector workloads. Only the input draw lives here; the score
+# arithmetic is the HIP kernel's (product path) and the oracle's (tests).
+# ---------------------------------------------------------------------------
+
+INDEXER_HEADS = 64
+INDEXER_DIM = 128
+
+
+@dataclass(frozen=True)
+class ChainWorkload:
+    name: str
+    n_alloc: int        # keys S (= the selector's N_alloc)
+    M: int              # query rows per call
+    heads: int = INDEXER_HEADS
+    dim: int = INDEXER_DIM
+    hot_p: float = 0.01
+    seed: int = BASE_SEED + 7
+
+
+CHAINS = {
+    "chain_c1": ChainWorkload("chain_c1", 131072, 512),
+    "chain_n512k_m1024": ChainWorkload("chain_n512k_m1024", 524288, 1024),
+}
+
+
+def get_chain(name: str) -> ChainWorkload:
+    try:
+        return CHAINS[name]
+    except KeyError:
+        raise KeyError(f"unknown chain workload {name!r}; known: {sorted(CHAINS)}") from None
+
+
+def to_e4m3_codes(x: torch.Tensor) -> torch.Tensor:
+    """Rounds float32 values to OCP FP8 E4M3 (torch's float8_e4m3fn, saturating at
+    +-448 first) and returns the raw bytes as uint8."""
+    return x.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def make_indexer_inputs(T: int, S: int, H: int = INDEXER_HEADS, D: int = INDEXER_DIM,
+                        row_len=None, hot_p: float = 0.01, seed: int = BASE_SEED + 7,
+                        device="cpu", row_start: int = 0):
+    """Returns (q [T, H, D] uint8, k [S, D] uint8, w [T, H] float32, row_len [T] int32).
+
+    row_len defaults to the causal window lengths of rows row_start.. (S - 8192 + r + 1)."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    g = torch.randn((D,), generator=gen, device=device, dtype=torch.float32)
+    q = torch.randn((T, H, D), generator=gen, device=device, dtype=torch.float32)
+    q.add_(0.25 * g)
+    hot = torch.rand((S, 1), generator=gen, device=device, dtype=torch.float32) < hot_p
+    k = torch.randn((S, D), generator=gen, device=device, dtype=torch.float32)
+    k.add_(hot.to(torch.float32) * g)
+    w = torch.randn((T, H), generator=gen, device=device, dtype=torch.float32)
+    w.mul_(0.5).add_(0.5).div_(H ** 0.5)
+    if row_len is None:
+        rows = torch.arange(row_start, row_start + T, device=device, dtype=torch.int64)
+        row_len = causal_lengths(S, rows)
+    else:
+        row_len = torch.as_tensor(row_len, dtype=torch.int32, device=device).reshape(T)
+    return to_e4m3_codes(q).contiguous(), to_e4m3_codes(k).contiguous(), w.contiguous(), row_len
+
+
+def make_chain(c: ChainWorkload, device="cpu", row_start: int = None, n_rows: int = None):
+    """Indexer inputs of a chain workload: the last M rows of the causal window by default."""
+    if n_rows is None:
+        n_rows = c.M
+    if row_start is None:
+        row_start = WINDOW - c.M
+    return make_indexer_inputs(n_rows, c.n_alloc, c.heads, c.dim, hot_p=c.hot_p, seed=c.seed,
+                               device=device, row_start=row_start)
