@@ -2,9 +2,11 @@
 
     python -m exact_top_selection_stride_amd.build
 
-Produces exact_top_selection_stride_amd/libtopk_exact.so from csrc/*.hip with
-hipcc. Packed FP32 instructions are disabled (the path does no float math, and
-the flag keeps the compiler from emitting them anywhere).
+Produces exact_top_selection_stride_amd/libtopk_exact.so from csrc/topk_exact.hip
+(the selector) and csrc/indexer_scores.hip (the FP8 indexer score producer) with
+hipcc. Packed FP32 instructions are disabled: the selector does no float math,
+and the flag keeps the compiler from emitting them in the score kernel's
+ReLU / weighting code.
 """
 import os
 import subprocess
@@ -12,7 +14,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "topk_exact.hip")
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("topk_exact.hip", "indexer_scores.hip")]
 INC = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtopk_exact.so")
 ARCH = os.environ.get("TOPK_OFFLOAD_ARCH", "gfx950")
@@ -28,7 +30,7 @@ def command(out: str, extra=()):
     return [hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
             "-Wall", "-Wno-unused-function",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", INC, SRC, "-o", out, *extra]
+            "-I", INC, *SRCS, "-o", out, *extra]
 
 
 def build(verbose: bool = False, extra=()) -> str:

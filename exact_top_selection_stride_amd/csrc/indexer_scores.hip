@@ -1,0 +1,178 @@
+// indexer_scores.hip -- FP8 indexer score producer for the exact Top-K selector (gfx950).
+//
+// Computes, for query row t and key s, the DSA-style indexer score of page "LiteTopK:
+// Exploiting the Curse of Dimensionality for a Fused Indexer-TopK Kernel ..." (section
+// 核心公式, Eq. (1)):
+//
+//     I[t, s] = sum_h w[t, h] * ReLU(q[t, h, :] . k[s, :])        for s <  L_t
+//     I[t, s] = -inf                                               for s >= L_t
+//
+// with q and k in FP8 (OCP E4M3) and w in FP32. This is the score matrix the selector
+// consumes: ragged rows with a -inf suffix. The pages chain the selector behind an FP8
+// multi-query score kernel in one graph (page "几何平均快 1.55 倍，但短行采样会输：腾讯怎么测精确
+// Top-K", section "框架轨迹"); this kernel plays that part.
+//
+// Design (CDNA4, wave64). The q.k products are a dense contraction over the head
+// dimension D = 128, so they run on the matrix cores: one v_mfma_f32_16x16x128_f8f6f4 gives
+// the dot products of 16 heads of one query with 16 keys. Each wave keeps the A operands
+// (its queries' heads, 32 B per lane per 16-head group) in registers for the whole key
+// range and streams 16-key B operands from L2; the ReLU, the weighting by w and the sum
+// over heads are VALU work on the accumulators:
+//   * lane (g = lane / 16, c = lane % 16) of an MFMA output holds heads 4g..4g+3 of the
+//     16-head group for key c; it folds its 4 heads of every group into one partial sum;
+//   * four 16-key steps (64 keys) are then combined across the four lane groups by a
+//     two-step butterfly (lane ^ 32, lane ^ 16) that leaves lane l with the total for
+//     key 64-block base + l, so every wave writes 256 contiguous bytes per query.
+// The A and B operands hold the same 32-byte slice of D in the same lane positions, so the
+// contraction is correct whatever order the instruction walks D in internally.
+// Products of two E4M3 values are exact in FP32; the sums round in FP32.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "topk_exact.h"
+
+int topk_record_error(int code, const char* text);  // defined with the selector (error text)
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int WAVES = 4;                  // waves per workgroup
+constexpr int QPW = 2;                    // queries per wave
+constexpr int QPB = WAVES * QPW;          // queries per workgroup
+constexpr int DIM = 128;                  // head dimension (one MFMA K step)
+constexpr int KEYS_PER_BLOCK = 64;        // keys per wave iteration (4 MFMA column tiles)
+constexpr int KEYS_PER_WG = 4096;         // key range of one workgroup
+
+__device__ __forceinline__ v8i load32(const uint8_t* p) {
+  const int4* v = reinterpret_cast<const int4*>(p);
+  int4 a = v[0], b = v[1];
+  v8i r = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  return r;
+}
+
+// One 16-key step of one query: the HG MFMAs of its head groups and the lane's partial
+// sum over its 4 heads of each group.
+template <int HG>
+__device__ __forceinline__ float head_partial(const v8i (&a)[HG], const v8i& b, const float (&wl)[HG][4]) {
+  float p = 0.f;
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) {
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[hg], b, acc, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p = fmaf(wl[hg][r], fmaxf(acc[r], 0.f), p);
+  }
+  return p;
+}
+
+// Lane l of the wave holds p[j] = its partial for key base + 16 j + (l % 16) from lane group
+// g = l / 16. Returns the sum over the four lane groups for key base + l.
+__device__ __forceinline__ float reduce_scatter4(const float (&p)[4], int lane) {
+  const bool hi2 = (lane >> 5) & 1;  // g >> 1
+  const bool hi1 = (lane >> 4) & 1;  // g & 1
+  float send_a = hi2 ? p[0] : p[2], send_b = hi2 ? p[1] : p[3];
+  float keep_a = hi2 ? p[2] : p[0], keep_b = hi2 ? p[3] : p[1];
+  float q0 = keep_a + __shfl_xor(send_a, 32);
+  float q1 = keep_b + __shfl_xor(send_b, 32);
+  float send = hi1 ? q0 : q1, keep = hi1 ? q1 : q0;
+  return keep + __shfl_xor(send, 16);
+}
+
+template <int HG>
+__global__ __launch_bounds__(WAVES * 64) void indexer_scores_kernel(
+    const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const float* __restrict__ w,
+    const int32_t* __restrict__ row_len, int T, int S, int n_qgroups, float* __restrict__ out) {
+  constexpr int H = HG * 16;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int qg = blockIdx.x % n_qgroups;
+  const int kc = blockIdx.x / n_qgroups;
+  const int s_begin = kc * KEYS_PER_WG;
+  const int s_end = min(S, s_begin + KEYS_PER_WG);
+
+  // Queries of this wave, their lengths and operands.
+  int t[QPW], L[QPW];
+  v8i a[QPW][HG];
+  float wl[QPW][HG][4];
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+    t[i] = qg * QPB + wave * QPW + i;
+    const bool live = t[i] < T;
+    const int tt = live ? t[i] : 0;
+    // The length is the same for every lane; readfirstlane makes the branches on it uniform.
+    L[i] = __builtin_amdgcn_readfirstlane(live ? min(max(row_len[tt], 0), S) : 0);
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) {
+      a[i][hg] = load32(q + ((size_t)tt * H + hg * 16 + c) * DIM + g * 32);
+      const float4 wv = *reinterpret_cast<const float4*>(w + (size_t)tt * H + hg * 16 + 4 * g);
+      wl[i][hg][0] = wv.x; wl[i][hg][1] = wv.y; wl[i][hg][2] = wv.z; wl[i][hg][3] = wv.w;
+    }
+  }
+  const int Lmax = max(L[0], L[1]);
+  const float ninf = -__builtin_inff();
+
+  for (int s0 = s_begin; s0 < s_end; s0 += KEYS_PER_BLOCK) {
+    float res[QPW];
+    if (s0 < Lmax) {
+      v8i b[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int s = min(s0 + 16 * j + c, S - 1);  // rows past S are loaded in bounds and masked
+        b[j] = load32(k + (size_t)s * DIM + g * 32);
+      }
+#pragma unroll
+      for (int i = 0; i < QPW; ++i) {
+        float p[4] = {0.f, 0.f, 0.f, 0.f};
+        if (s0 < L[i]) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) p[j] = head_partial<HG>(a[i], b[j], wl[i]);
+        }
+        res[i] = reduce_scatter4(p, lane);
+      }
+    } else {
+      res[0] = res[1] = 0.f;
+    }
+    const int s = s0 + lane;
+    if (s < s_end) {
+#pragma unroll
+      for (int i = 0; i < QPW; ++i)
+        if (t[i] < T) out[(size_t)t[i] * S + s] = (s < L[i]) ? res[i] : ninf;
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" int topk_indexer_scores(const uint8_t* q, const uint8_t* k, const float* w,
+                                   const int32_t* row_len, int64_t T, int64_t S, int32_t H,
+                                   int32_t D, float* out, hipStream_t stream) {
+  if (T < 0) return topk_record_error(TOPK_ERR_BAD_SHAPE, "indexer: T is negative");
+  if (S < 1 || S > INT32_MAX) return topk_record_error(TOPK_ERR_BAD_SHAPE, "indexer: S outside [1, INT32_MAX]");
+  if (T > INT32_MAX || (T > 0 && S > INT64_MAX / 4 / T))
+    return topk_record_error(TOPK_ERR_BAD_SHAPE, "indexer: T outside [0, INT32_MAX] or T * S overflows");
+  if (D != DIM) return topk_record_error(TOPK_ERR_BAD_ARG, "indexer: D must be 128");
+  if (H != 16 && H != 32 && H != 48 && H != 64)
+    return topk_record_error(TOPK_ERR_BAD_ARG, "indexer: H must be 16, 32, 48 or 64");
+  if (T == 0) return TOPK_OK;
+  if (!q || !k || !w || !row_len || !out)
+    return topk_record_error(TOPK_ERR_NULL_POINTER, "indexer: null pointer argument");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)w) & 15)
+    return topk_record_error(TOPK_ERR_BAD_ARG, "indexer: q, k and w must be 16-byte aligned");
+  const int n_qgroups = (int)((T + QPB - 1) / QPB);
+  const int64_t n_kchunks = (S + KEYS_PER_WG - 1) / KEYS_PER_WG;
+  const int64_t blocks = n_kchunks * n_qgroups;
+  if (blocks > INT32_MAX) return topk_record_error(TOPK_ERR_BAD_SHAPE, "indexer: grid too large");
+  dim3 grid((unsigned)blocks), block(WAVES * 64);
+  switch (H) {
+    case 16: indexer_scores_kernel<1><<<grid, block, 0, stream>>>(q, k, w, row_len, (int)T, (int)S, n_qgroups, out); break;
+    case 32: indexer_scores_kernel<2><<<grid, block, 0, stream>>>(q, k, w, row_len, (int)T, (int)S, n_qgroups, out); break;
+    case 48: indexer_scores_kernel<3><<<grid, block, 0, stream>>>(q, k, w, row_len, (int)T, (int)S, n_qgroups, out); break;
+    default: indexer_scores_kernel<4><<<grid, block, 0, stream>>>(q, k, w, row_len, (int)T, (int)S, n_qgroups, out); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return topk_record_error(TOPK_ERR_HIP, hipGetErrorString(e));
+  return TOPK_OK;
+}

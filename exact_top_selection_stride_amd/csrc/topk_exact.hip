@@ -1985,6 +1985,12 @@ int stream_capturing(hipStream_t stream, bool* capturing) {
 
 }  // namespace
 
+// Records an error text for topk_exact_last_error() on behalf of the library's other
+// translation units (the indexer score producer).
+__attribute__((visibility("hidden"))) int topk_record_error(int code, const char* text) {
+  return fail(code, "%s", text);
+}
+
 extern "C" {
 
 int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc, int32_t K,

@@ -168,6 +168,32 @@ const char* topk_exact_last_error(void);
  * reads cannot be elided. Used to report a measured HBM read ceiling next to the peak. */
 int topk_stream_read_probe(const float* x, int64_t n, float* sink, hipStream_t stream);
 
+/* FP8 indexer score producer: the score matrix the selector consumes, made on the GPU so
+ * that scoring and selection can be chained on one stream and captured into one graph
+ * (page "几何平均快 1.55 倍，但短行采样会输：腾讯怎么测精确 Top-K", section "框架轨迹": the
+ * selector runs behind an FP8 multi-query attention score kernel in one graph). For every
+ * query row t and key s it writes the DSA indexer score of page "LiteTopK: Exploiting the
+ * Curse of Dimensionality for a Fused Indexer-TopK Kernel ..." (section 核心公式, Eq. (1)):
+ *     out[t][s] = sum_{h < H} w[t][h] * max(0, sum_{d < D} q[t][h][d] * k[s][d])   for s < L_t
+ *     out[t][s] = -inf                                                            for s >= L_t
+ * with L_t = clamp(row_len[t], 0, S).
+ *   q        device, [T][H][D] bytes, OCP FP8 E4M3 codes (row-major), 16-byte aligned.
+ *   k        device, [S][D] bytes, OCP FP8 E4M3 codes (row-major), 16-byte aligned.
+ *   w        device, [T][H] float32 head weights, 16-byte aligned.
+ *   row_len  device, [T] int32 valid lengths (the selector's row_len).
+ *   T, S     T >= 0 query rows, 1 <= S <= INT32_MAX keys (the selector's N_alloc).
+ *   H, D     H in {16, 32, 48, 64} heads, D = 128 (head dimension).
+ *   out      device, row-major [T][S] float32; every element is written.
+ *   stream   the kernel is enqueued here; no allocation or synchronization (capturable).
+ * Products of E4M3 values are exact in float32; the sums over D and over H round in
+ * float32 in an unspecified order, so each element is within (D + H + 2) * 2^-24 *
+ * sum_h |w[t][h]| * sum_d |q[t][h][d] * k[s][d]| of the exact value. NaN codes (S.1111.111)
+ * are outside the contract (the result is unspecified). Returns TOPK_OK (T == 0 is a no-op), TOPK_ERR_BAD_SHAPE,
+ * TOPK_ERR_BAD_ARG (H, D or alignment), TOPK_ERR_NULL_POINTER or TOPK_ERR_HIP, before
+ * anything is enqueued except for TOPK_ERR_HIP. */
+int topk_indexer_scores(const uint8_t* q, const uint8_t* k, const float* w, const int32_t* row_len,
+                        int64_t T, int64_t S, int32_t H, int32_t D, float* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -68,6 +68,18 @@ def test_argument_validation_without_gpu():
     assert L.topk_exact_time_next_call(fake, None) == B.TOPK_ERR_NULL_POINTER
     assert L.topk_exact_time_next_call(None, fake) == B.TOPK_ERR_NULL_POINTER
     assert L.topk_exact_time_next_call(None, None) == B.TOPK_OK
+    # Indexer score producer: shape, head count, head dimension, alignment, null pointers.
+    assert L.topk_indexer_scores(fake, fake, fake, fake, -1, 10, 64, 128, fake, None) == B.TOPK_ERR_BAD_SHAPE
+    assert L.topk_indexer_scores(fake, fake, fake, fake, 2, 0, 64, 128, fake, None) == B.TOPK_ERR_BAD_SHAPE
+    assert L.topk_indexer_scores(fake, fake, fake, fake, 2, 2**31, 64, 128, fake, None) == B.TOPK_ERR_BAD_SHAPE
+    assert L.topk_indexer_scores(fake, fake, fake, fake, 2, 10, 64, 64, fake, None) == B.TOPK_ERR_BAD_ARG
+    assert L.topk_indexer_scores(fake, fake, fake, fake, 2, 10, 8, 128, fake, None) == B.TOPK_ERR_BAD_ARG
+    assert L.topk_indexer_scores(fake, fake, fake, fake, 2, 10, 80, 128, fake, None) == B.TOPK_ERR_BAD_ARG
+    assert L.topk_indexer_scores(fake + 4, fake, fake, fake, 2, 10, 64, 128, fake, None) == B.TOPK_ERR_BAD_ARG
+    assert "aligned" in tk.last_error()
+    assert L.topk_indexer_scores(None, fake, fake, fake, 2, 10, 64, 128, fake, None) == B.TOPK_ERR_NULL_POINTER
+    assert L.topk_indexer_scores(fake, fake, fake, fake, 2, 10, 64, 128, None, None) == B.TOPK_ERR_NULL_POINTER
+    assert L.topk_indexer_scores(None, None, None, None, 0, 10, 64, 128, None, None) == B.TOPK_OK
 
 
 def test_execution_mode_roundtrip():

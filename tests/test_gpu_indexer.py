@@ -1,0 +1,255 @@
+"""GPU parity of the FP8 indexer score producer and the score + select chain.
+
+Scores: the HIP kernel against the float64 oracle of Eq. (1) of page "LiteTopK:
+Exploiting the Curse of Dimensionality for a Fused Indexer-TopK Kernel ..."
+(section 核心公式), element by element. The -inf suffix must match exactly; every
+finite score must lie within the bound of the kernel's arithmetic:
+  * the matrix core forms each q.k dot product from groups of 8 adjacent products;
+    inside a group every product is truncated toward zero to a multiple of
+    2^(E - 13), E = floor(log2) of the group's largest product (measured on gfx950,
+    pinned by test_matrix_core_group_truncation), so a product p loses at most
+    |p| mod 2^(E - 13) (nothing when it lies within 2^6 of the group's largest);
+  * the group sums, the MFMA accumulator and the weighted ReLU sum over heads round
+    in float32: at most (D / 8 + H + 4) * 2^-24 * sum_h |w| * sum_d |q k|.
+
+Chain: the selector runs on the GPU's own float32 scores, so its result is checked
+bit-exactly under the set contract against the oracle's selection of those same
+scores (the floating-point decision is taken once, in the kernel's float32).
+
+All calls go through the C ABI via the ctypes binding.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import indexer_scores as O
+import exact_top_selection_stride_amd as tk
+from exact_top_selection_stride_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+K = 2048
+
+
+GROUP = 8                 # adjacent products summed together by the matrix core
+GROUP_BITS = 13           # products below 2^(E - 13) of the group's largest 2^E are dropped
+
+
+def _kernel_tolerance(qh, kh, wh, Lh):
+    """Absolute bound on |kernel - exact| per element (see the module docstring).
+
+    Truncation term: in a group whose largest |product| is M, a product p loses
+    |p| mod 2^(floor(log2 M) - 13) at most (zero when p is a multiple of that quantum,
+    as every product within 2^6 of M is). Rounding term: float32 sums."""
+    q = np.abs(O.decode_e4m3(qh))
+    k = np.abs(O.decode_e4m3(kh))
+    T, H, D = q.shape
+    S = k.shape[0]
+    wa = np.abs(wh.astype(np.float64))
+    Lc = np.clip(Lh.astype(np.int64), 0, S)
+    trunc = np.zeros((T, S))
+    for t in range(T):
+        n = int(Lc[t])
+        for s0 in range(0, n, 512):
+            s1 = min(n, s0 + 512)
+            prod = (q[t][:, None, :] * k[None, s0:s1, :]).reshape(H, s1 - s0, D // GROUP, GROUP)
+            top = prod.max(axis=3, keepdims=True)
+            quantum = np.exp2(np.floor(np.log2(np.where(top > 0, top, 1.0))) - GROUP_BITS)
+            loss = np.fmod(prod, quantum).sum(axis=(2, 3))                   # [H, keys]
+            trunc[t, s0:s1] = wa[t] @ loss
+    return trunc + (D // GROUP + H + 4) * 2.0 ** -24 * O.abs_magnitude(qh, kh, wh, Lh)
+
+
+def _check_scores(q, k, w, L, got, rows=None, cols=None, label=""):
+    """rows: optional list of query rows; cols: optional key window (a, n), checked as the
+    scores of keys a .. a+n-1 (the oracle on k[a:a+n] with lengths clamp(L - a, 0, n))."""
+    qh, kh, wh, Lh = q.cpu().numpy(), k.cpu().numpy(), w.cpu().numpy(), L.cpu().numpy()
+    g = got.detach().cpu().numpy().astype(np.float64) if cols is None else \
+        got[:, cols[0]:cols[0] + cols[1]].detach().cpu().numpy().astype(np.float64)
+    if cols is not None:
+        a, n = cols
+        kh = kh[a:a + n]
+        Lh = np.clip(Lh.astype(np.int64) - a, 0, n).astype(np.int32)
+    if rows is not None:
+        qh, wh, Lh, g = qh[rows], wh[rows], Lh[rows], g[rows]
+    ref = O.indexer_scores(qh, kh, wh, Lh)
+    tol = _kernel_tolerance(qh, kh, wh, Lh)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isneginf(g), ~fin), f"{label}: -inf suffix differs"
+    err = np.abs(g[fin] - ref[fin])
+    bad = err > tol[fin]
+    assert not bad.any(), (f"{label}: {int(bad.sum())} scores outside the kernel's bound; "
+                           f"worst excess {float((err - tol[fin]).max()):.3e}")
+    return ref
+
+
+def _raw_codes(shape, gen, max_code=0x7E):
+    """Uniform finite E4M3 codes of both signs (subnormals and +-448 included, no NaN)."""
+    mag = torch.randint(0, max_code + 1, shape, generator=gen, dtype=torch.int32)
+    sign = torch.randint(0, 2, shape, generator=gen, dtype=torch.int32) << 7
+    return (mag | sign).to(torch.uint8)
+
+
+@pytest.mark.parametrize("T,S,H", [(1, 1, 64), (3, 15, 16), (8, 64, 32), (13, 100, 48), (9, 4097, 64),
+                                   (17, 5000, 64), (2, 8192, 16)])
+def test_scores_small_shapes_recipe(T, S, H):
+    q, k, w, _ = W.make_indexer_inputs(T, S, H=H, seed=100 + T + S + H)
+    gen = torch.Generator().manual_seed(T * 7 + S)
+    L = torch.randint(-2, S + 3, (T,), generator=gen, dtype=torch.int32)
+    L[0] = S
+    out = tk.indexer_scores(q.to(DEV), k.to(DEV), w.to(DEV), L.to(DEV))
+    torch.cuda.synchronize()
+    _check_scores(q, k, w, L, out, label=f"T={T} S={S} H={H}")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_scores_raw_codes_full_range(seed):
+    # Every finite code: subnormals, +-0, +-448, mixed signs; weights of both signs.
+    gen = torch.Generator().manual_seed(seed)
+    T, S, H = 11, 1000 + 37 * seed, (16, 32, 48, 64)[seed]
+    q = _raw_codes((T, H, 128), gen)
+    k = _raw_codes((S, 128), gen)
+    w = torch.randn((T, H), generator=gen) * 3
+    L = torch.randint(0, S + 1, (T,), generator=gen, dtype=torch.int32)
+    out = tk.indexer_scores(q.to(DEV), k.to(DEV), w.to(DEV), L.to(DEV))
+    torch.cuda.synchronize()
+    _check_scores(q, k, w, L, out, label=f"raw codes seed {seed}")
+
+
+def _code(e):
+    """E4M3 code of 2^e, -9 <= e <= 8 (subnormal below 2^-6)."""
+    return (e + 7) << 3 if e >= -6 else 1 << (e + 9)
+
+
+def _single_dot(pairs):
+    """Score of one query (head 0 weighted 1, the other 15 heads weighted 0) against key 0
+    whose dot product is sum over (d, q code, k code) of the listed products."""
+    q = torch.zeros((1, 16, 128), dtype=torch.uint8)
+    k = torch.zeros((16, 128), dtype=torch.uint8)
+    for d, qc, kc in pairs:
+        q[0, 0, d] = qc
+        k[0, d] = kc
+    w = torch.zeros((1, 16))
+    w[0, 0] = 1.0
+    L = torch.full((1,), 16, dtype=torch.int32)
+    out = tk.indexer_scores(q.to(DEV), k.to(DEV), w.to(DEV), L.to(DEV)).cpu().numpy()
+    exact = O.indexer_scores(q.numpy(), k.numpy(), w.numpy(), L.numpy())
+    return float(out[0, 0]), float(exact[0, 0])
+
+
+def test_matrix_core_group_truncation():
+    # Pins the accumulation behaviour the tolerance relies on: a product 2^14 times smaller
+    # than the largest product of its 8-element group is dropped, while the same product
+    # in another group, or 2^13 times smaller in the same group, is kept exactly.
+    big = (0, _code(8), _code(8))                                   # 2^16
+    got, exact = _single_dot([big, (1, _code(2), 0x38)])            # + 2^2, same group
+    assert (got, exact) == (65536.0, 65540.0)
+    got, exact = _single_dot([big, (8, _code(2), 0x38)])            # + 2^2, next group
+    assert got == exact == 65540.0
+    got, exact = _single_dot([big, (7, _code(3), 0x38)])            # + 2^3, same group
+    assert got == exact == 65544.0
+    got, exact = _single_dot([big, (3, _code(2) | 0x80, 0x38)])     # - 2^2: toward zero
+    assert (got, exact) == (65536.0, 65532.0)
+    # the loss stays inside the per-group bound 7 * 2^-13 * 2^16 = 56
+    pairs = [big] + [(d, _code(2), 0x3F) for d in range(1, 8)]      # 7 x 7.5
+    got, exact = _single_dot(pairs)
+    assert 0 < exact - got <= 7 * 2.0 ** -13 * 65536
+
+
+def test_scores_one_hot_exact():
+    # q[t, h] = e_{(h + t) % 128}, k[s] = 2^(s % 5 - 2) e_{s % 128}: every dot is 0 or a power
+    # of two, each output sums at most one weight times that power, so float32 is exact.
+    T, S, H = 8, 300, 64
+    q = torch.zeros((T, H, 128), dtype=torch.uint8)
+    for t in range(T):
+        for h in range(H):
+            q[t, h, (h + t) % 128] = 0x38
+    k = torch.zeros((S, 128), dtype=torch.uint8)
+    for s in range(S):
+        k[s, s % 128] = 0x38 + ((s % 5) - 2) * 8
+    w = torch.arange(T * H, dtype=torch.float32).reshape(T, H) - 100
+    L = torch.full((T,), S, dtype=torch.int32)
+    out = tk.indexer_scores(q.to(DEV), k.to(DEV), w.to(DEV), L.to(DEV)).cpu().numpy()
+    ref = O.indexer_scores(q.numpy(), k.numpy(), w.numpy(), L.numpy())
+    assert np.array_equal(out.astype(np.float64), ref)
+
+
+def test_scores_write_every_element():
+    T, S = 5, 5000
+    q, k, w, _ = W.make_indexer_inputs(T, S, seed=3)
+    L = torch.tensor([0, 1, 63, 4096, 5000], dtype=torch.int32)
+    out = torch.full((T, S), 123.0, device=DEV)
+    tk.indexer_scores(q.to(DEV), k.to(DEV), w.to(DEV), L.to(DEV), out=out)
+    torch.cuda.synchronize()
+    assert not (out == 123.0).any()
+    _check_scores(q, k, w, L, out, label="every element")
+
+
+def test_chain_small_every_row():
+    # 64 causal rows of a 16K-key window: the selector takes its direct path on these rows.
+    T, S = 64, 16384
+    q, k, w, L = W.make_indexer_inputs(T, S, seed=11)
+    qd, kd, wd, Ld = q.to(DEV), k.to(DEV), w.to(DEV), L.to(DEV)
+    scores, idx = tk.indexer_topk(qd, kd, wd, Ld, K=K)
+    torch.cuda.synchronize()
+    _check_scores(q, k, w, L, scores, rows=[0, 31, 63], label="chain scores")
+    sh, oh = scores.cpu().numpy(), idx.cpu().numpy()
+    Lh = L.numpy()
+    ref = oracle.topk(sh, Lh, K, -1)
+    n_bad, _ = oracle.check_contract(sh, Lh, K, -1, oh, ref)
+    assert n_bad == 0
+
+
+def test_chain_full_size_c1_sampled_rows():
+    # The 512 x 131072 chain workload in the launch configuration the benchmark times;
+    # scores of a few rows checked against the oracle, selections of more rows checked
+    # under the contract on the GPU's scores.
+    c = W.get_chain("chain_c1")
+    q, k, w, L = W.make_chain(c, DEV)
+    tk.reset_stats()
+    scores, idx = tk.indexer_topk(q, k, w, L, K=K)
+    torch.cuda.synchronize()
+    st = tk.get_stats()
+    assert st["rows"] == c.M and st["sampled"] == c.M
+    for a in (0, 61440, 122880):  # key windows at the start, middle and ragged end
+        _check_scores(q, k, w, L, scores, rows=[0, 257, 511], cols=(a, 8192),
+                      label=f"chain_c1 scores, keys {a}..{a + 8191}")
+    rows = torch.tensor([0, 1, 100, 255, 256, 400, 510, 511], device=DEV)
+    sh = scores[rows].cpu().numpy()
+    Lh = L[rows].cpu().numpy()
+    oh = idx[rows].cpu().numpy()
+    ref = oracle.topk(sh, Lh, K, -1)
+    n_bad, _ = oracle.check_contract(sh, Lh, K, -1, oh, ref)
+    assert n_bad == 0
+
+
+def test_chain_graph_replay():
+    T, S = 24, 131072
+    q, k, w, L = W.make_indexer_inputs(T, S, seed=21, device=DEV)
+    tk.reserve(T, S, K)
+    scores = torch.empty((T, S), device=DEV)
+    idx = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        tk.indexer_topk(q, k, w, L, K=K, scores=scores, out=idx)  # warm-up outside capture
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            tk.indexer_topk(q, k, w, L, K=K, scores=scores, out=idx)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    eager = scores.clone()
+    Lh = L.cpu().numpy()
+    ref = oracle.topk(eager.cpu().numpy(), Lh, K, -1)
+    for rep in range(5):
+        scores.fill_(7.0)
+        idx.fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(scores, eager), f"replay {rep}: scores differ from the eager call"
+        n_bad, _ = oracle.check_contract(eager.cpu().numpy(), Lh, K, -1, idx.cpu().numpy(), ref)
+        assert n_bad == 0, f"replay {rep}"
+        tk.indexer_scores(q[:2], k, w[:2], L[:2].contiguous())  # eager work between replays
+        torch.cuda.synchronize()
