@@ -12,6 +12,18 @@ configuration gated on a passing contract check.
 
 Prints one JSON line. Default workload: 8192 rows x 1,048,576 columns, causal
 ragged lengths (the 1M-width persistent-path configuration).
+
+--workload chain_c1 (or chain_n512k_m1024) times the score + select chain instead:
+the FP8 indexer score kernel (Eq. (1) of page "LiteTopK: Exploiting the Curse of
+Dimensionality for a Fused Indexer-TopK Kernel ...") feeding the selector, both
+captured in one graph, as the pages chain the selector behind an FP8 score
+kernel (page "几何平均快 1.55 倍，但短行采样会输：腾讯怎么测精确 Top-K", section
+"框架轨迹"). Its roofline is the score kernel's, against the dense FP8 matrix peak.
+
+--summarize-counters FETCH_DIR WRITE_DIR does no GPU work: it turns two
+rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, both with
+--copy-calibration) into profiles/hbm_traffic_<workload>.json, scaling each
+counter by what it reads for the plain 1 GiB device copy.
 """
 import argparse
 import hashlib
@@ -28,6 +40,7 @@ METRIC = "Top-K rows/s and achieved HBM GB/s (frac of peak), K=2048, FP32 ragged
 HBM_PEAK_GBPS = 8000.0
 K_DEFAULT = 2048
 EXECUTIONS = {"auto": 0, "persistent": 1, "row": 2, "rowsplit": 3}  # TOPK_EXEC_* values
+CHAIN_NAMES = ("chain_c1", "chain_n512k_m1024")  # score + select workloads (workloads.CHAINS)
 
 
 def parse():
@@ -46,6 +59,9 @@ def parse():
                     help="row-to-workgroup mapping (auto: the library's shape-based choice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy first (known bytes, for counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "script with --copy-calibration into profiles/hbm_traffic_<workload>.json")
     return ap.parse_args()
 
 
@@ -73,11 +89,18 @@ def _code_tokens(text: str) -> str:
     return " ".join("".join(out).split())
 
 
-def kernel_source_digest() -> str:
-    """Digest of the selector's code (comments and layout ignored): counter summaries taken
-    on one digest describe exactly the kernels of any source with the same digest."""
+SOURCES = {
+    "selector": ("exact_top_selection_stride_amd/csrc/topk_exact.hip", "include/topk_exact.h"),
+    "indexer": ("exact_top_selection_stride_amd/csrc/indexer_scores.hip", "include/topk_exact.h",
+                "exact_top_selection_stride_amd/build.py"),
+}
+
+
+def kernel_source_digest(part: str = "selector") -> str:
+    """Digest of one kernel family's code (comments and layout ignored): counter summaries
+    taken on one digest describe exactly the kernels of any source with the same digest."""
     h = hashlib.sha256()
-    for rel in ("exact_top_selection_stride_amd/csrc/topk_exact.hip", "include/topk_exact.h"):
+    for rel in SOURCES[part]:
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
             h.update(_code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
@@ -136,13 +159,232 @@ def cpu_baseline(scores, lengths, K, sentinel, target_s, max_rows=1024):
                       f"{reps} times on host copies, {spent:.1f} s of selection"}
 
 
+def _counter_rows(d):
+    """(kernel name, dispatch id, counter value) rows of a rocprofv3 --pmc csv output dir."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                rows.append((r["Kernel_Name"], int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    return rows
+
+
+def summarize_counters(args):
+    """Writes profiles/hbm_traffic_<workload>.json from a FETCH_SIZE and a WRITE_SIZE run."""
+    import re
+    chain = args.workload in CHAIN_NAMES
+    kernel_re = re.compile(r"indexer_scores_kernel" if chain else r"topk_rows_kernel|split_[a-z]+_kernel")
+    out = {"workload": args.workload,
+           "kernel_source_digest": kernel_source_digest("indexer" if chain else "selector"),
+           "calibration": "plain device copy of 2^28 floats (1 GiB read, 1 GiB written)"}
+    total = 0.0
+    for counter, d, known_kib in (("FETCH_SIZE", args.summarize_counters[0], 1 << 20),
+                                  ("WRITE_SIZE", args.summarize_counters[1], 1 << 20)):
+        per = {}
+        names = set()
+        calib = {}
+        for name, disp, v in _counter_rows(d):
+            if "copyBuffer" in name:
+                calib[disp] = calib.get(disp, 0.0) + v
+            elif kernel_re.search(name):
+                per[disp] = per.get(disp, 0.0) + v
+                names.add(kernel_re.search(name).group(0) + ("<true>" if "<true>" in name else
+                                                             "<false>" if "<false>" in name else ""))
+        # The calibration copies are the script's first three device copies (1 GiB each).
+        first = [calib[k] for k in sorted(calib)[:3]]
+        if len(first) < 3 or not per or max(first) > 1.01 * min(first):
+            raise SystemExit(f"{counter}: calibration copies or kernel dispatches missing in {d}")
+        cal = sum(first) / len(first)
+        scale = known_kib / cal
+        mean = sum(per.values()) / len(per)
+        key = counter.split("_")[0].lower()
+        out["kernel"] = " + ".join(sorted(names))
+        out[f"{key}_raw_kib_mean"] = mean
+        out[f"{key}_calibration_kib"] = cal
+        out[f"{key}_scale"] = scale
+        out[f"{key}_bytes"] = mean * scale * 1024
+        out[f"{key}_dispatches"] = len(per)
+        total += mean * scale * 1024
+    out["bytes_per_launch"] = total
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{args.workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def _traffic(workload, part):
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.json")
+    if os.path.exists(path):
+        with open(path) as f:
+            prof = json.load(f)
+        if prof.get("kernel_source_digest") == kernel_source_digest(part):
+            return prof.get("bytes_per_launch")
+    return None
+
+
+def cpu_baseline_chain(q, k, w, lengths, K, sentinel, target_s):
+    """Times the CPU oracles (indexer scores, then selection) on whole rows of the call
+    until about target_s seconds have been spent."""
+    import numpy as np
+    import oracle
+    from oracle import indexer_scores as O
+    threads = oracle.default_threads()
+    qh, kh, wh = q.cpu().numpy(), k.cpu().numpy(), w.cpu().numpy()
+    lh = lengths.cpu().numpy().astype(np.int32)
+    done, spent, r = 0, 0.0, 0
+    while spent < target_s and done < lh.shape[0]:
+        t0 = time.perf_counter()
+        sc = O.indexer_scores(qh[r:r + 1], kh, wh[r:r + 1], lh[r:r + 1])
+        oracle.topk(sc.astype(np.float32), lh[r:r + 1], K, sentinel, n_threads=threads)
+        spent += time.perf_counter() - t0
+        done += 1
+        r += 1
+    return {"value": done / spent, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {done} rows of the call scored (float64 numpy) and selected on host "
+                      f"copies, {spent:.1f} s"}
+
+
+def run_chain(args):
+    """Score + select chain: the FP8 indexer score kernel and the selector in one graph."""
+    import torch
+    import exact_top_selection_stride_amd as tk
+    from exact_top_selection_stride_amd import workloads as W
+
+    K, sentinel = K_DEFAULT, -1
+    c = W.get_chain(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    q, k, w, L = W.make_chain(c, dev)
+    scores = torch.empty((c.M, c.n_alloc), dtype=torch.float32, device=dev)
+    idx = torch.empty((c.M, K), dtype=torch.int32, device=dev)
+    tk.reserve(c.M, c.n_alloc, K)
+
+    tk.reset_stats()
+    tk.indexer_topk(q, k, w, L, K=K, sentinel=sentinel, scores=scores, out=idx)
+    torch.cuda.synchronize()
+    stats = tk.get_stats()
+    rows = sorted(set([0, c.M - 1] + [int(i) for i in torch.linspace(0, c.M - 1, min(args.check_rows, c.M)).round().tolist()]))
+    violations = gate_rows(scores, L, idx, K, sentinel, rows)
+    if violations:
+        print(json.dumps({"error": "contract violations before timing", "violations": violations}), flush=True)
+        return 1
+
+    stream = torch.cuda.Stream(device=dev)
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = None
+    if not args.eager:
+        with torch.cuda.stream(stream):
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                tk.indexer_topk(q, k, w, L, K=K, sentinel=sentinel, scores=scores, out=idx)
+        torch.cuda.synchronize()
+
+    def launch():
+        if graph is not None:
+            graph.replay()
+        else:
+            tk.indexer_topk(q, k, w, L, K=K, sentinel=sentinel, scores=scores, out=idx, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup + args.condition):
+            launch()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            starts[i].record(stream)
+            launch()
+            ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = [starts[i].elapsed_time(ends[i]) for i in range(args.steps)]
+
+    # Kernel times: the score kernel between events on the bench stream (one kernel), the
+    # selector kernels through the library's timing hook.
+    s0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    s1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    k0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    k1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    with torch.cuda.stream(stream):
+        for e in k0 + k1:
+            e.record(stream)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            s0[i].record(stream)
+            tk.indexer_scores(q, k, w, L, out=scores, stream=stream)
+            s1[i].record(stream)
+            tk.time_next_call(k0[i], k1[i])
+            tk.topk_exact(scores, L, K=K, sentinel=sentinel, out=idx, stream=stream)
+    torch.cuda.synchronize()
+    score_ms = sum(s0[i].elapsed_time(s1[i]) for i in range(args.steps)) / args.steps
+    select_ms = sum(k0[i].elapsed_time(k1[i]) for i in range(args.steps)) / args.steps
+    post_bad = gate_rows(scores, L, idx, K, sentinel, [0, c.M // 2, c.M - 1])
+
+    Lsum = int(L.to(torch.int64).sum())
+    flops = 2.0 * c.heads * c.dim * Lsum          # q.k products of the valid (t, s) pairs
+    achieved = flops / (score_ms / 1e3) / 1e12
+    sel_bytes = 4 * Lsum + 4 * int(((L.to(torch.int64) + 127) // 128).sum()) + 4 * c.M * K + 4 * c.M
+    result = {
+        "metric": "Score + select chain rows/s (FP8 indexer scores, then exact Top-K K=2048 of the "
+                  "ragged FP32 rows, one hipGraph)",
+        "value": c.M * args.steps / wall,
+        "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8e4m3 (scores), u32 (selection)", "data": "synthetic",
+        "config": {"workload": c.name, "M": c.M, "N_alloc": c.n_alloc, "K": K, "heads": c.heads,
+                   "head_dim": c.dim, "lengths": "causal", "hot_p": c.hot_p,
+                   "launch": "eager" if graph is None else "hipGraph replay (scores + select)"},
+        "median_call_ms": statistics.median(per_call_ms),
+        "p10_call_ms": sorted(per_call_ms)[int(0.1 * (len(per_call_ms) - 1))],
+        "p90_call_ms": sorted(per_call_ms)[int(0.9 * (len(per_call_ms) - 1))],
+        "roofline": {"bound": "mfma", "kernel": "indexer_scores_kernel", "achieved": achieved,
+                     "peak": 5000.0, "unit": "TFLOP/s", "frac": achieved / 5000.0,
+                     "traffic": _traffic(c.name, "indexer"), "mean_launch_ms": score_ms,
+                     "timing": f"HIP events around the score kernel, {args.steps} direct launches on the bench stream",
+                     "algorithmic_flops_per_launch": flops,
+                     "peak_note": "MI355X dense FP8 matrix peak"},
+        "selector": {"mean_launch_ms": select_ms, "algorithmic_bytes_per_launch": sel_bytes,
+                     "achieved_gbps": sel_bytes / (select_ms / 1e3) / 1e9,
+                     "frac_of_8tbps": sel_bytes / (select_ms / 1e3) / 1e9 / HBM_PEAK_GBPS},
+        "parity": {"rows_checked": len(rows), "violations": violations, "post_timing_violations": post_bad,
+                   "gate": "torch contract check of the selection on the GPU's scores"},
+        "path_stats_first_call": stats,
+        "kernel_source_digest": kernel_source_digest("indexer"),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_chain(q, k, w, L, K, sentinel, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0 if post_bad == 0 else 1
+
+
 def main():
     args = parse()
+    if args.summarize_counters:
+        return summarize_counters(args)
     if args.gpus != 1:
         print(json.dumps({"error": "this selector build runs on one GPU only; "
                                    "the multi-GPU row sharding is a design note, not built",
                           "n_gpus_requested": args.gpus}), flush=True)
         return 2
+    if args.workload in CHAIN_NAMES:
+        return run_chain(args)
     import torch
     import exact_top_selection_stride_amd as tk
     from exact_top_selection_stride_amd import workloads as W
@@ -260,14 +502,8 @@ def main():
     kernel_total_s = sum(kernel_ms) / 1e3
     achieved = alg_steps / kernel_total_s / 1e9
 
-    traffic = None
-    prof_path = os.path.join(ROOT, "profiles", f"hbm_traffic_{w.name}.json")
-    digest = kernel_source_digest()
-    if os.path.exists(prof_path):
-        with open(prof_path) as f:
-            prof = json.load(f)
-        if prof.get("kernel_source_digest") == digest:
-            traffic = prof.get("bytes_per_launch")
+    traffic = _traffic(w.name, "selector")
+    digest = kernel_source_digest("selector")
 
     result = {
         "metric": METRIC,

@@ -30,6 +30,9 @@ def command(out: str, extra=()):
     return [hipcc(), "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
             "-Wall", "-Wno-unused-function",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results in VGPRs: the score kernel reads every accumulator with VALU
+            # ops, which cannot take accumulator registers (each would need a copy).
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-I", INC, *SRCS, "-o", out, *extra]
 
 

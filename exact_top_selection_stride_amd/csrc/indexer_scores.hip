@@ -16,8 +16,11 @@
 // dimension D = 128, so they run on the matrix cores: one v_mfma_f32_16x16x128_f8f6f4 gives
 // the dot products of 16 heads of one query with 16 keys. Each wave keeps the A operands
 // (its queries' heads, 32 B per lane per 16-head group) in registers for the whole key
-// range and streams 16-key B operands from L2; the ReLU, the weighting by w and the sum
-// over heads are VALU work on the accumulators:
+// range; the workgroup streams its 4096-key range through LDS in 64-key blocks, and the
+// waves take their 16-key B operands from there. The ReLU, the weighting by w and the sum
+// over heads are VALU work on the accumulators (two VALU ops per head and key, about as
+// many cycles as the MFMA that produced them; the library is built with the MFMA results
+// in ordinary VGPRs so that no accumulator-register copies are added):
 //   * lane (g = lane / 16, c = lane % 16) of an MFMA output holds heads 4g..4g+3 of the
 //     16-head group for key c; it folds its 4 heads of every group into one partial sum;
 //   * four 16-key steps (64 keys) are then combined across the four lane groups by a
@@ -52,6 +55,11 @@ __device__ __forceinline__ v8i load32(const uint8_t* p) {
   return r;
 }
 
+// ReLU on the bit pattern: a float with its sign bit set is a negative int32 and becomes
+// +0 under a signed max, every other value is kept. One VALU op, where fmaxf(x, 0) costs
+// two (the IEEE-mode max first canonicalizes its input).
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // One 16-key step of one query: the HG MFMAs of its head groups and the lane's partial
 // sum over its 4 heads of each group.
 template <int HG>
@@ -62,7 +70,7 @@ __device__ __forceinline__ float head_partial(const v8i (&a)[HG], const v8i& b, 
     v4f acc = {0.f, 0.f, 0.f, 0.f};
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[hg], b, acc, 0, 0, 0, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p = fmaf(wl[hg][r], fmaxf(acc[r], 0.f), p);
+    for (int r = 0; r < 4; ++r) p = fmaf(wl[hg][r], relu(acc[r]), p);
   }
   return p;
 }
@@ -80,13 +88,22 @@ __device__ __forceinline__ float reduce_scatter4(const float (&p)[4], int lane) 
   return keep + __shfl_xor(send, 16);
 }
 
+// Shared-memory staging of the key stream: every wave of a workgroup needs the same 16-key
+// B operands, so the workgroup copies each 64-key block (8 KB) into LDS once, one block
+// ahead of its use (double buffer), and the waves read their operands from there. Rows
+// are padded from 128 to 144 bytes so that the 16 lanes reading one 16-byte slice of 16
+// different keys hit 16 disjoint groups of 4 banks.
+constexpr int PITCH = 144;
+
 template <int HG>
 __global__ __launch_bounds__(WAVES * 64) void indexer_scores_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const float* __restrict__ w,
     const int32_t* __restrict__ row_len, int T, int S, int n_qgroups, float* __restrict__ out) {
   constexpr int H = HG * 16;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][KEYS_PER_BLOCK * PITCH];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int qg = blockIdx.x % n_qgroups;
   const int kc = blockIdx.x / n_qgroups;
@@ -111,36 +128,56 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_scores_kernel(
       wl[i][hg][0] = wv.x; wl[i][hg][1] = wv.y; wl[i][hg][2] = wv.z; wl[i][hg][3] = wv.w;
     }
   }
-  const int Lmax = max(L[0], L[1]);
   const float ninf = -__builtin_inff();
 
+  // Staging: thread tid copies bytes [part * 32, part * 32 + 32) of key (tid / 4) of a block.
+  // Keys past S are read from row S - 1 (in bounds) and their scores are never stored.
+  const int skey = tid >> 2, part = tid & 3;
+  const int soff = skey * PITCH + part * 32;
+  {
+    const int4* src = reinterpret_cast<const int4*>(k + (size_t)min(s_begin + skey, S - 1) * DIM + part * 32);
+    const int4 r0 = src[0], r1 = src[1];
+    *reinterpret_cast<int4*>(&kbuf[0][soff]) = r0;
+    *reinterpret_cast<int4*>(&kbuf[0][soff + 16]) = r1;
+  }
+  __syncthreads();
+
+  int buf = 0;
   for (int s0 = s_begin; s0 < s_end; s0 += KEYS_PER_BLOCK) {
-    float res[QPW];
-    if (s0 < Lmax) {
-      v8i b[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s = min(s0 + 16 * j + c, S - 1);  // rows past S are loaded in bounds and masked
-        b[j] = load32(k + (size_t)s * DIM + g * 32);
-      }
-#pragma unroll
-      for (int i = 0; i < QPW; ++i) {
-        float p[4] = {0.f, 0.f, 0.f, 0.f};
-        if (s0 < L[i]) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) p[j] = head_partial<HG>(a[i], b[j], wl[i]);
-        }
-        res[i] = reduce_scatter4(p, lane);
-      }
-    } else {
-      res[0] = res[1] = 0.f;
+    // Fetch the next block into registers now; it goes to the other buffer after this
+    // block's work, so its latency overlaps the matrix and vector work below.
+    const int nxt = s0 + KEYS_PER_BLOCK;
+    const bool more = nxt < s_end;
+    int4 r0 = {0, 0, 0, 0}, r1 = {0, 0, 0, 0};
+    if (more) {
+      const int4* src = reinterpret_cast<const int4*>(k + (size_t)min(nxt + skey, S - 1) * DIM + part * 32);
+      r0 = src[0];
+      r1 = src[1];
     }
-    const int s = s0 + lane;
-    if (s < s_end) {
+    float p[QPW][4];
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) p[i][0] = p[i][1] = p[i][2] = p[i][3] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint8_t* bp = &kbuf[buf][(16 * j + c) * PITCH + g * 32];
+      const int4 x0 = *reinterpret_cast<const int4*>(bp), x1 = *reinterpret_cast<const int4*>(bp + 16);
+      const v8i b = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
       for (int i = 0; i < QPW; ++i)
-        if (t[i] < T) out[(size_t)t[i] * S + s] = (s < L[i]) ? res[i] : ninf;
+        if (s0 < L[i]) p[i][j] = head_partial<HG>(a[i], b, wl[i]);
     }
+    const int s = s0 + lane;
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+      const float res = reduce_scatter4(p[i], lane);
+      if (s < s_end && t[i] < T) out[(size_t)t[i] * S + s] = (s < L[i]) ? res : ninf;
+    }
+    if (more) {
+      *reinterpret_cast<int4*>(&kbuf[buf ^ 1][soff]) = r0;
+      *reinterpret_cast<int4*>(&kbuf[buf ^ 1][soff + 16]) = r1;
+    }
+    __syncthreads();
+    buf ^= 1;
   }
 }
 
