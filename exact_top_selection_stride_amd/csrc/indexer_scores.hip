@@ -60,18 +60,15 @@ __device__ __forceinline__ v8i load32(const uint8_t* p) {
 // two (the IEEE-mode max first canonicalizes its input).
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-// One 16-key step of one query: the HG MFMAs of its head groups and the lane's partial
-// sum over its 4 heads of each group.
+// The lane's partial sum over its 4 heads of each 16-head group for one 16-key step of one
+// query, from that step's HG MFMA accumulators.
 template <int HG>
-__device__ __forceinline__ float head_partial(const v8i (&a)[HG], const v8i& b, const float (&wl)[HG][4]) {
+__device__ __forceinline__ float weighted_relu_sum(const v4f (&acc)[HG], const float (&wl)[HG][4]) {
   float p = 0.f;
 #pragma unroll
-  for (int hg = 0; hg < HG; ++hg) {
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[hg], b, acc, 0, 0, 0, 0, 0, 0);
+  for (int hg = 0; hg < HG; ++hg)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p = fmaf(wl[hg][r], relu(acc[r]), p);
-  }
+    for (int r = 0; r < 4; ++r) p = fmaf(wl[hg][r], relu(acc[hg][r]), p);
   return p;
 }
 
@@ -128,6 +125,7 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_scores_kernel(
       wl[i][hg][0] = wv.x; wl[i][hg][1] = wv.y; wl[i][hg][2] = wv.z; wl[i][hg][3] = wv.w;
     }
   }
+  const int Lmax = max(L[0], L[1]);
   const float ninf = -__builtin_inff();
 
   // Staging: thread tid copies bytes [part * 32, part * 32 + 32) of key (tid / 4) of a block.
@@ -157,14 +155,30 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_scores_kernel(
     float p[QPW][4];
 #pragma unroll
     for (int i = 0; i < QPW; ++i) p[i][0] = p[i][1] = p[i][2] = p[i][3] = 0.f;
+    if (s0 < Lmax) {
+      // All 4 x QPW x HG products of the block first, then the epilogue: the matrix work of
+      // later products overlaps the ReLU / weighting of earlier ones.
+      v4f acc[4][QPW][HG];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint8_t* bp = &kbuf[buf][(16 * j + c) * PITCH + g * 32];
-      const int4 x0 = *reinterpret_cast<const int4*>(bp), x1 = *reinterpret_cast<const int4*>(bp + 16);
-      const v8i b = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      for (int j = 0; j < 4; ++j) {
+        const uint8_t* bp = &kbuf[buf][(16 * j + c) * PITCH + g * 32];
+        const int4 x0 = *reinterpret_cast<const int4*>(bp), x1 = *reinterpret_cast<const int4*>(bp + 16);
+        const v8i b = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-      for (int i = 0; i < QPW; ++i)
-        if (s0 < L[i]) p[i][j] = head_partial<HG>(a[i], b, wl[i]);
+        for (int i = 0; i < QPW; ++i)
+#pragma unroll
+          for (int hg = 0; hg < HG; ++hg) {
+            const v4f zero = {0.f, 0.f, 0.f, 0.f};
+            acc[j][i][hg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i][hg], b, zero, 0, 0, 0, 0, 0, 0);
+          }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < QPW; ++i) p[i][j] = weighted_relu_sum<HG>(acc[j][i], wl[i]);
+#pragma unroll
+      for (int i = 0; i < QPW; ++i)  // a query whose row ends before this block
+        if (s0 >= L[i]) p[i][0] = p[i][1] = p[i][2] = p[i][3] = 0.f;
     }
     const int s = s0 + lane;
 #pragma unroll
