@@ -187,6 +187,19 @@ def test_scores_write_every_element():
     _check_scores(q, k, w, L, out, label="every element")
 
 
+def test_scores_guard_canaries():
+    # The score rows sit between guard regions; the kernel writes exactly [out, out + T * S).
+    T, S, G = 13, 4099, 8192
+    q, k, w, _ = W.make_indexer_inputs(T, S, seed=5)
+    L = torch.randint(0, S + 1, (T,), generator=torch.Generator().manual_seed(5), dtype=torch.int32)
+    buf = torch.full((T * S + 2 * G,), 12345.0, device=DEV)
+    out = buf[G:G + T * S].view(T, S)
+    tk.indexer_scores(q.to(DEV), k.to(DEV), w.to(DEV), L.to(DEV), out=out)
+    torch.cuda.synchronize()
+    assert bool((buf[:G] == 12345.0).all()) and bool((buf[G + T * S:] == 12345.0).all())
+    _check_scores(q, k, w, L, out, label="guarded")
+
+
 def test_chain_small_every_row():
     # 64 causal rows of a 16K-key window: the selector takes its direct path on these rows.
     T, S = 64, 16384

@@ -528,3 +528,74 @@ def test_full_size_few_long_rows_take_rowsplit():
     assert st["rows"] == 64 and st["rowsplit"] == 64
     idx = torch.tensor([0, 31, 63], device=DEV)
     _check(s[idx], l[idx], out[idx], label="1M x 64 rows, row-split")
+
+
+# ---------------------------------------------- memory safety and long replay runs
+
+GUARD = 4096          # int32 guard words on each side of an output buffer
+CANARY = 0x5A5A5A5A
+
+
+def _guarded_out(M, K):
+    buf = torch.full((M * K + 2 * GUARD,), CANARY, dtype=torch.int32, device=DEV)
+    return buf, buf[GUARD:GUARD + M * K].view(M, K)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_output_guard_canaries(seed):
+    # The output view sits between two guard regions of canary words; no path or execution
+    # mode may write outside [out, out + M * K).
+    s, l, Kr, n_alloc = _random_case(100 + seed)
+    M = s.shape[0]
+    for execution in (tk.EXEC_PERSISTENT, tk.EXEC_ROW_PER_WG, tk.EXEC_ROWSPLIT):
+        for mode in (tk.PATH_AUTO, tk.PATH_SAMPLED, tk.PATH_DIRECT, tk.PATH_RECOVERY):
+            buf, out = _guarded_out(M, Kr)
+            tk.set_path_override(mode)
+            try:
+                with tk.execution(execution):
+                    tk.topk_exact(s, l, K=Kr, out=out)
+                torch.cuda.synchronize()
+            finally:
+                tk.set_path_override(tk.PATH_AUTO)
+            assert bool((buf[:GUARD] == CANARY).all()) and bool((buf[GUARD + M * Kr:] == CANARY).all()), \
+                f"write outside the output: seed {seed} exec {execution} mode {mode}"
+            _check(s, l, out, K=Kr, label=f"guarded seed {seed} exec {execution} mode {mode}")
+
+
+def _sorted_selected_keys(scores, out):
+    """Per-row sorted order keys of the selected scores (rows with L > K), on the GPU."""
+    from bench import order_keys
+    idx = out.to(torch.int64).clamp(min=0)
+    keys = order_keys(torch.gather(scores, 1, idx))
+    return torch.sort(keys, dim=1).values
+
+
+def test_graph_replay_200():
+    # One captured call replayed 200 times: the self-rewinding tickets, queues and counters
+    # must give the same selected key multiset every time (compared on the GPU), and the
+    # first and last replays pass the full oracle check. Rows include recovery rows.
+    s, l = _window_rows("c1", [(0, 24)])
+    s[3, : l[3]] = 1.0                          # all-equal row: ties at the boundary
+    torch.manual_seed(0)
+    s[5, : l[5]] = torch.randint(0, 3, (int(l[5]),), device=DEV).float()  # three values
+    tk.reserve(24, s.shape[1], K)
+    out = torch.empty((24, K), dtype=torch.int32, device=DEV)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        tk.topk_exact(s, l, K=K, out=out)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            tk.topk_exact(s, l, K=K, out=out)
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    _check(s, l, out, label="replay warm-up")
+    ref = _sorted_selected_keys(s, out)
+    for rep in range(200):
+        out.fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = _sorted_selected_keys(s, out)
+        assert torch.equal(got, ref), f"replay {rep}: selected key multiset changed"
+        assert int(torch.unique(out, dim=None).numel()) > K  # not a constant fill
+    _check(s, l, out, label="replay 200")
