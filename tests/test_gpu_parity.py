@@ -599,3 +599,61 @@ def test_graph_replay_200():
         assert torch.equal(got, ref), f"replay {rep}: selected key multiset changed"
         assert int(torch.unique(out, dim=None).numel()) > K  # not a constant fill
     _check(s, l, out, label="replay 200")
+
+
+_FRESH_PROCESS = r"""
+import json, sys
+sys.path.insert(0, sys.argv[1])
+import numpy as np, torch
+import exact_top_selection_stride_amd as tk
+from exact_top_selection_stride_amd import workloads as W
+import oracle
+res = {}
+s, l = W.make_rows(2, 131072, [131072, 100000], device="cuda")
+out = torch.empty((2, 2048), dtype=torch.int32, device="cuda")
+stream = torch.cuda.Stream()
+# 1. No workspace yet: a call under capture must fail with TOPK_ERR_WORKSPACE, enqueue nothing.
+with torch.cuda.stream(stream):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        try:
+            tk.topk_exact(s, l, K=2048, out=out)
+            res["capture_without_workspace"] = "ok"
+        except tk.TopKError as e:
+            res["capture_without_workspace"] = e.code
+torch.cuda.synchronize()
+# 2. Workspace without row-split state (reserve for more than 1024 rows): a few long rows,
+# which auto dispatch would split, run unsplit under capture and stay exact.
+tk.reserve(4096, 1048576, 2048)
+s2, l2 = W.make_rows(2, 1048576, [1048576, 1000000], device="cuda")
+out2 = torch.empty((2, 2048), dtype=torch.int32, device="cuda")
+with torch.cuda.stream(stream):
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2, stream=stream):
+        tk.topk_exact(s2, l2, K=2048, out=out2)
+torch.cuda.synchronize()
+tk.reset_stats()
+g2.replay()
+torch.cuda.synchronize()
+res["stats"] = tk.get_stats()
+sh, lh, oh = s2.cpu().numpy(), l2.cpu().numpy().astype(np.int32), out2.cpu().numpy()
+res["violations"] = int(oracle.check_contract(sh, lh, 2048, -1, oh, oracle.topk(sh, lh, 2048, -1))[0])
+print(json.dumps(res))
+"""
+
+
+def test_capture_without_reserve_in_a_fresh_process():
+    # A fresh process has no workspace: capturing a call must return TOPK_ERR_WORKSPACE
+    # before enqueueing anything; with the workspace but no row-split state, long rows run
+    # unsplit under capture and stay exact.
+    import json
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _FRESH_PROCESS, root], capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    res = json.loads(r.stdout.strip().splitlines()[-1])
+    assert res["capture_without_workspace"] == 5  # TOPK_ERR_WORKSPACE
+    assert res["violations"] == 0
+    assert res["stats"]["rows"] == 2 and res["stats"]["rowsplit"] == 0
