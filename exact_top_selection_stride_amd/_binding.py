@@ -46,7 +46,7 @@ EXPORTED = (
     "topk_exact", "topk_exact_reserve", "topk_exact_get_stats", "topk_exact_reset_stats",
     "topk_exact_set_path_override", "topk_exact_last_error", "topk_stream_read_probe",
     "topk_exact_set_execution", "topk_exact_time_next_call", "topk_exact_set_proposal",
-    "topk_indexer_scores",
+    "topk_indexer_scores", "topk_indexer_topk",
 )
 
 
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.topk_stream_read_probe.argtypes = [vp, i64, vp, vp]
         L.topk_indexer_scores.restype = ctypes.c_int
         L.topk_indexer_scores.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, vp, vp]
+        L.topk_indexer_topk.restype = ctypes.c_int
+        L.topk_indexer_topk.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, vp, vp, i32, vp]
         _lib = L
     return _lib
 
@@ -229,15 +231,7 @@ def stream_read_probe(x: torch.Tensor, sink: torch.Tensor, stream=None):
                                             _stream_handle(x.device, stream)), "topk_stream_read_probe")
 
 
-def indexer_scores(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, row_len: torch.Tensor,
-                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """FP8 indexer scores I[t, s] = sum_h w[t, h] * ReLU(q[t, h] . k[s]), -inf for s >= row_len[t].
-
-    q: uint8 [T, H, D] holding OCP E4M3 codes (torch.float8_e4m3fn viewed as uint8 also
-    accepted), k: uint8 [S, D] likewise, w: float32 [T, H], row_len: int32 [T], all
-    contiguous on one GPU; H in {16, 32, 48, 64}, D = 128. Returns float32 [T, S]
-    (or fills `out`). Enqueued on `stream` (default: the current stream).
-    """
+def _indexer_args(q, k, w, row_len):
     if q.dtype == torch.float8_e4m3fn:
         q = q.view(torch.uint8)
     if k.dtype == torch.float8_e4m3fn:
@@ -248,16 +242,33 @@ def indexer_scores(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, row_len: t
     dev = q.device
     if k.dim() != 2 or k.dtype != torch.uint8 or k.device != dev or not k.is_contiguous() or k.shape[1] != D:
         raise ValueError("k must be a contiguous uint8 [S, D] tensor on q's device")
-    S = k.shape[0]
     if w.dtype != torch.float32 or w.device != dev or tuple(w.shape) != (T, H) or not w.is_contiguous():
         raise ValueError("w must be a contiguous float32 [T, H] tensor on q's device")
     if row_len.dtype != torch.int32 or row_len.device != dev or tuple(row_len.shape) != (T,) \
             or not row_len.is_contiguous():
         raise ValueError("row_len must be a contiguous int32 [T] tensor on q's device")
+    return q, k, T, H, D, k.shape[0], dev
+
+
+def _scores_buffer(out, T, S, dev):
     if out is None:
-        out = torch.empty((T, S), dtype=torch.float32, device=dev)
-    elif out.dtype != torch.float32 or out.device != dev or tuple(out.shape) != (T, S) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [T, S] tensor on q's device")
+        return torch.empty((T, S), dtype=torch.float32, device=dev)
+    if out.dtype != torch.float32 or out.device != dev or tuple(out.shape) != (T, S) or not out.is_contiguous():
+        raise ValueError("scores must be a contiguous float32 [T, S] tensor on q's device")
+    return out
+
+
+def indexer_scores(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, row_len: torch.Tensor,
+                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """FP8 indexer scores I[t, s] = sum_h w[t, h] * ReLU(q[t, h] . k[s]), -inf for s >= row_len[t].
+
+    q: uint8 [T, H, D] holding OCP E4M3 codes (torch.float8_e4m3fn viewed as uint8 also
+    accepted), k: uint8 [S, D] likewise, w: float32 [T, H], row_len: int32 [T], all
+    contiguous on one GPU; H in {16, 32, 48, 64}, D = 128. Returns float32 [T, S]
+    (or fills `out`). Enqueued on `stream` (default: the current stream).
+    """
+    q, k, T, H, D, S, dev = _indexer_args(q, k, w, row_len)
+    out = _scores_buffer(out, T, S, dev)
     with torch.cuda.device(dev):
         code = lib().topk_indexer_scores(q.data_ptr(), k.data_ptr(), w.data_ptr(), row_len.data_ptr(),
                                          T, S, H, D, out.data_ptr(), _stream_handle(dev, stream))
@@ -268,8 +279,18 @@ def indexer_scores(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, row_len: t
 def indexer_topk(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, row_len: torch.Tensor,
                  K: int = 2048, sentinel: int = -1, scores: Optional[torch.Tensor] = None,
                  out: Optional[torch.Tensor] = None, stream=None):
-    """The score + select chain: indexer scores, then exact top-K of each ragged row, both
-    enqueued on one stream (graph-capturable). Returns (scores [T, S] float32, idx [T, K] int32)."""
-    scores = indexer_scores(q, k, w, row_len, out=scores, stream=stream)
-    idx = topk_exact(scores, row_len, K=K, sentinel=sentinel, out=out, stream=stream)
-    return scores, idx
+    """The score + select chain (topk_indexer_topk): indexer scores, then the exact top-K of
+    each ragged row, both enqueued on one stream (graph-capturable).
+    Returns (scores [T, S] float32, idx [T, K] int32)."""
+    q, k, T, H, D, S, dev = _indexer_args(q, k, w, row_len)
+    scores = _scores_buffer(scores, T, S, dev)
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.int32, device=dev)
+    elif out.dtype != torch.int32 or out.device != dev or tuple(out.shape) != (T, K) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 [T, K] tensor on q's device")
+    with torch.cuda.device(dev):
+        code = lib().topk_indexer_topk(q.data_ptr(), k.data_ptr(), w.data_ptr(), row_len.data_ptr(),
+                                       T, S, H, D, K, scores.data_ptr(), out.data_ptr(), sentinel,
+                                       _stream_handle(dev, stream))
+    _check(code, "topk_indexer_topk")
+    return scores, out

@@ -200,9 +200,11 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_scores_kernel(
 
 }  // namespace
 
-extern "C" int topk_indexer_scores(const uint8_t* q, const uint8_t* k, const float* w,
-                                   const int32_t* row_len, int64_t T, int64_t S, int32_t H,
-                                   int32_t D, float* out, hipStream_t stream) {
+// Host-side checks of a score call (no launch); shared with the score + select chain.
+__attribute__((visibility("hidden"))) int topk_indexer_check(const uint8_t* q, const uint8_t* k,
+                                                            const float* w, const int32_t* row_len,
+                                                            int64_t T, int64_t S, int32_t H, int32_t D,
+                                                            const float* out) {
   if (T < 0) return topk_record_error(TOPK_ERR_BAD_SHAPE, "indexer: T is negative");
   if (S < 1 || S > INT32_MAX) return topk_record_error(TOPK_ERR_BAD_SHAPE, "indexer: S outside [1, INT32_MAX]");
   if (T > INT32_MAX || (T > 0 && S > INT64_MAX / 4 / T))
@@ -215,11 +217,20 @@ extern "C" int topk_indexer_scores(const uint8_t* q, const uint8_t* k, const flo
     return topk_record_error(TOPK_ERR_NULL_POINTER, "indexer: null pointer argument");
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)w) & 15)
     return topk_record_error(TOPK_ERR_BAD_ARG, "indexer: q, k and w must be 16-byte aligned");
+  const int64_t n_qgroups = (T + QPB - 1) / QPB;
+  const int64_t n_kchunks = (S + KEYS_PER_WG - 1) / KEYS_PER_WG;
+  if (n_kchunks * n_qgroups > INT32_MAX) return topk_record_error(TOPK_ERR_BAD_SHAPE, "indexer: grid too large");
+  return TOPK_OK;
+}
+
+// Enqueues the score kernel of a checked call (T > 0).
+__attribute__((visibility("hidden"))) int topk_indexer_launch(const uint8_t* q, const uint8_t* k,
+                                                             const float* w, const int32_t* row_len,
+                                                             int64_t T, int64_t S, int32_t H, float* out,
+                                                             hipStream_t stream) {
   const int n_qgroups = (int)((T + QPB - 1) / QPB);
   const int64_t n_kchunks = (S + KEYS_PER_WG - 1) / KEYS_PER_WG;
-  const int64_t blocks = n_kchunks * n_qgroups;
-  if (blocks > INT32_MAX) return topk_record_error(TOPK_ERR_BAD_SHAPE, "indexer: grid too large");
-  dim3 grid((unsigned)blocks), block(WAVES * 64);
+  dim3 grid((unsigned)(n_kchunks * n_qgroups)), block(WAVES * 64);
   switch (H) {
     case 16: indexer_scores_kernel<1><<<grid, block, 0, stream>>>(q, k, w, row_len, (int)T, (int)S, n_qgroups, out); break;
     case 32: indexer_scores_kernel<2><<<grid, block, 0, stream>>>(q, k, w, row_len, (int)T, (int)S, n_qgroups, out); break;
@@ -229,4 +240,13 @@ extern "C" int topk_indexer_scores(const uint8_t* q, const uint8_t* k, const flo
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return topk_record_error(TOPK_ERR_HIP, hipGetErrorString(e));
   return TOPK_OK;
+}
+
+extern "C" int topk_indexer_scores(const uint8_t* q, const uint8_t* k, const float* w,
+                                   const int32_t* row_len, int64_t T, int64_t S, int32_t H,
+                                   int32_t D, float* out, hipStream_t stream) {
+  topk_record_error(TOPK_OK, "");  // clears the error text
+  const int rc = topk_indexer_check(q, k, w, row_len, T, S, H, D, out);
+  if (rc != TOPK_OK || T == 0) return rc;
+  return topk_indexer_launch(q, k, w, row_len, T, S, H, out, stream);
 }

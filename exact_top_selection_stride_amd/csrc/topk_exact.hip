@@ -1985,17 +1985,28 @@ int stream_capturing(hipStream_t stream, bool* capturing) {
 
 }  // namespace
 
+// The indexer score producer's host-side checks and launch (indexer_scores.hip).
+int topk_indexer_check(const uint8_t* q, const uint8_t* k, const float* w, const int32_t* row_len,
+                       int64_t T, int64_t S, int32_t H, int32_t D, const float* out);
+int topk_indexer_launch(const uint8_t* q, const uint8_t* k, const float* w, const int32_t* row_len,
+                        int64_t T, int64_t S, int32_t H, float* out, hipStream_t stream);
+
 // Records an error text for topk_exact_last_error() on behalf of the library's other
 // translation units (the indexer score producer).
 __attribute__((visibility("hidden"))) int topk_record_error(int code, const char* text) {
   return fail(code, "%s", text);
 }
 
-extern "C" {
+namespace {
 
-int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc, int32_t K,
-               int32_t* out_idx, int32_t sentinel, hipStream_t stream) {
-  g_err[0] = '\0';
+// Host-side checks of a selector call and the device state it runs with. Returns an error
+// before anything is enqueued; on success *st_out is null when there is nothing to
+// launch (M == 0).
+int selector_check(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc, int32_t K,
+                   int32_t* out_idx, int32_t sentinel, hipStream_t stream, bool* capturing_out,
+                   DevState** st_out) {
+  *st_out = nullptr;
+  *capturing_out = false;
   if (M < 0) return fail(TOPK_ERR_BAD_SHAPE, "M = %lld is negative", (long long)M);
   if (N_alloc < 1 || N_alloc > INT32_MAX)
     return fail(TOPK_ERR_BAD_SHAPE, "N_alloc = %lld outside [1, INT32_MAX]", (long long)N_alloc);
@@ -2006,7 +2017,7 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
   if (sentinel >= 0 && (int64_t)sentinel < N_alloc)
     return fail(TOPK_ERR_BAD_SENTINEL, "sentinel %d lies inside [0, N_alloc = %lld)", sentinel,
                 (long long)N_alloc);
-  if (M == 0) return TOPK_OK;
+  if (M == 0) return TOPK_OK;  // *st_out stays null: nothing to launch
   if (!scores || !row_len || !out_idx) return fail(TOPK_ERR_NULL_POINTER, "null scores/row_len/out_idx");
   if ((reinterpret_cast<uintptr_t>(scores) & 3u) != 0)
     return fail(TOPK_ERR_BAD_ARG, "scores is not 4-byte aligned");
@@ -2017,7 +2028,17 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
   DevState* st = nullptr;
   rc = get_state(capturing, &st);
   if (rc != TOPK_OK) return rc;
+  *capturing_out = capturing;
+  *st_out = st;
+  return TOPK_OK;
+}
 
+
+// Enqueues the selector and recovery kernels of a checked call.
+int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc, int32_t K,
+                   int32_t* out_idx, int32_t sentinel, hipStream_t stream, bool capturing,
+                    DevState* st) {
+  int rc = TOPK_OK;
   Params p;
   p.scores = scores;
   p.row_len = row_len;
@@ -2132,6 +2153,36 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "launch recovery_finish_kernel");
   return TOPK_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc, int32_t K,
+               int32_t* out_idx, int32_t sentinel, hipStream_t stream) {
+  g_err[0] = '\0';
+  bool capturing = false;
+  DevState* st = nullptr;
+  const int rc = selector_check(scores, row_len, M, N_alloc, K, out_idx, sentinel, stream, &capturing, &st);
+  if (rc != TOPK_OK || st == nullptr) return rc;
+  return selector_launch(scores, row_len, M, N_alloc, K, out_idx, sentinel, stream, capturing, st);
+}
+
+int topk_indexer_topk(const uint8_t* q, const uint8_t* k, const float* w, const int32_t* row_len,
+                      int64_t T, int64_t S, int32_t H, int32_t D, int32_t K, float* scores,
+                      int32_t* out_idx, int32_t sentinel, hipStream_t stream) {
+  g_err[0] = '\0';
+  int rc = topk_indexer_check(q, k, w, row_len, T, S, H, D, scores);
+  if (rc != TOPK_OK) return rc;
+  bool capturing = false;
+  DevState* st = nullptr;
+  rc = selector_check(scores, row_len, T, S, K, out_idx, sentinel, stream, &capturing, &st);
+  if (rc != TOPK_OK || st == nullptr) return rc;
+  rc = topk_indexer_launch(q, k, w, row_len, T, S, H, scores, stream);
+  if (rc != TOPK_OK) return rc;
+  return selector_launch(scores, row_len, T, S, K, out_idx, sentinel, stream, capturing, st);
 }
 
 int topk_exact_reserve(int64_t M_max, int64_t N_alloc_max, int32_t K) {

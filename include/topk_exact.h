@@ -198,6 +198,17 @@ int topk_stream_read_probe(const float* x, int64_t n, float* sink, hipStream_t s
 int topk_indexer_scores(const uint8_t* q, const uint8_t* k, const float* w, const int32_t* row_len,
                         int64_t T, int64_t S, int32_t H, int32_t D, float* out, hipStream_t stream);
 
+/* The score + select chain in one call: topk_indexer_scores into `scores` (device,
+ * [T][S] float32, caller-owned), then topk_exact(scores, row_len, T, S, K, out_idx,
+ * sentinel) on the same stream, so one capture holds both (page "几何平均快 1.55 倍，但短行采样会输：
+ * 腾讯怎么测精确 Top-K", section "框架轨迹": the selector behind an FP8 score kernel in one
+ * graph). Arguments as in the two calls. Every host-side check of both (shapes, H, D, K,
+ * sentinel, pointers, alignment, the workspace under capture) runs before anything is
+ * enqueued; T == 0 is a no-op. */
+int topk_indexer_topk(const uint8_t* q, const uint8_t* k, const float* w, const int32_t* row_len,
+                      int64_t T, int64_t S, int32_t H, int32_t D, int32_t K, float* scores,
+                      int32_t* out_idx, int32_t sentinel, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
