@@ -173,8 +173,9 @@ def _counter_rows(d):
     return rows
 
 
-def summarize_counters(args):
-    """Writes profiles/hbm_traffic_<workload>.json from a FETCH_SIZE and a WRITE_SIZE run."""
+def summarize_counters(args, out_dir=None):
+    """Writes profiles/hbm_traffic_<workload>.json (or into out_dir) from a FETCH_SIZE and a
+    WRITE_SIZE run."""
     import re
     chain = args.workload in CHAIN_NAMES
     kernel_re = re.compile(r"indexer_scores_kernel" if chain else r"topk_rows_kernel|split_[a-z]+_kernel")
@@ -210,7 +211,7 @@ def summarize_counters(args):
         out[f"{key}_dispatches"] = len(per)
         total += mean * scale * 1024
     out["bytes_per_launch"] = total
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{args.workload}.json")
+    path = os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"hbm_traffic_{args.workload}.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out), flush=True)
