@@ -55,6 +55,10 @@ def lib():
         L.oracle_topk.restype = ctypes.c_int
         L.oracle_topk.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int]
+        L.oracle_topk_sorted.restype = ctypes.c_int
+        L.oracle_topk_sorted.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_int]
         L.oracle_check_contract.restype = ctypes.c_int64
         L.oracle_check_contract.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                             ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -90,6 +94,22 @@ def topk(scores, row_len, K: int, sentinel: int = -1, n_threads: int = None) -> 
     if rc != 0:
         raise ValueError(f"oracle_topk rejected its arguments (code {rc})")
     return out
+
+
+def topk_sorted(scores, row_len, K: int, sentinel: int = -1, n_threads: int = None):
+    """Sorted, value-returning Top-K: ([M, K] int32 indices, [M, K] float32 values). Every
+    valid index of a row (K of them, or all L when L <= K) in (key descending, index
+    ascending) order, then the sentinel; values are the scores, -inf in sentinel slots."""
+    s = _as_scores(scores)
+    M, N = s.shape
+    r = _as_lengths(row_len, M)
+    out = np.empty((M, K), dtype=np.int32)
+    val = np.empty((M, K), dtype=np.float32)
+    rc = lib().oracle_topk_sorted(s.ctypes.data, r.ctypes.data, M, N, K, sentinel, out.ctypes.data,
+                                  val.ctypes.data, n_threads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_topk_sorted rejected its arguments (code {rc})")
+    return out, val
 
 
 def check_contract(scores, row_len, K: int, sentinel: int, cand, ref=None, n_threads: int = None):

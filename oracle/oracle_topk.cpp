@@ -30,6 +30,9 @@
 //   * Row lengths outside [0, N_alloc] are clamped into it.
 //   * The oracle breaks ties by the lower index, so its set is deterministic;
 //     any tie choice satisfies the contract.
+//   * Sorted output (an option beyond the pages' unordered contract): every
+//     valid index in (key descending, index ascending) order, then the
+//     sentinel; values are the selected scores, -inf in sentinel slots.
 //
 // Method: the plain definition. Rows are independent; each row with L > K is
 // resolved by std::nth_element on an index array under the strict weak order
@@ -97,9 +100,47 @@ void select_row(const float* row, int64_t L, int32_t K, int32_t sentinel, int32_
   std::copy(idx.begin(), idx.begin() + K, out);
 }
 
+// The sorted, value-returning output: the same selection, then every valid index of the
+// row (the K selected ones, or all L when L <= K) in the order (key descending, index
+// ascending), followed by the sentinel; values are the selected scores and -inf in the
+// sentinel slots.
+void select_row_sorted(const float* row, int64_t L, int32_t K, int32_t sentinel, int32_t* out,
+                       float* val) {
+  const int64_t n = L < K ? L : K;
+  std::vector<int32_t> idx(static_cast<size_t>(L));
+  for (int64_t j = 0; j < L; ++j) idx[j] = static_cast<int32_t>(j);
+  auto before = [&](int32_t a, int32_t b) {
+    const uint32_t ka = order_key(row[a]), kb = order_key(row[b]);
+    return ka > kb || (ka == kb && a < b);
+  };
+  if (L > K) std::nth_element(idx.begin(), idx.begin() + K, idx.end(), before);
+  std::sort(idx.begin(), idx.begin() + n, before);
+  for (int64_t j = 0; j < n; ++j) {
+    out[j] = idx[j];
+    val[j] = row[idx[j]];
+  }
+  for (int64_t j = n; j < K; ++j) {
+    out[j] = sentinel;
+    val[j] = -__builtin_inff();
+  }
+}
+
 }  // namespace
 
 extern "C" {
+
+// Sorted variant: out [M][K] int32 and val [M][K] float (host). Returns as oracle_topk.
+int oracle_topk_sorted(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc,
+                       int32_t K, int32_t sentinel, int32_t* out, float* val, int n_threads) {
+  if (M < 0 || N_alloc < 1 || K < 1) return 1;
+  if (M == 0) return 0;
+  if (!scores || !row_len || !out || !val) return 2;
+  parallel_rows(M, n_threads, [&](int64_t r) {
+    select_row_sorted(scores + r * N_alloc, clamp_len(row_len[r], N_alloc), K, sentinel, out + r * K,
+                      val + r * K);
+  });
+  return 0;
+}
 
 // Returns 0 on success, nonzero on a bad argument.
 // scores: host, row-major [M][N_alloc]; row_len: host [M]; out: host [M][K].

@@ -211,3 +211,46 @@ def test_oracle_rows_are_sorted_descending():
     for r in range(4):
         v = x[r, out[r]]
         assert np.all(v[:-1] >= v[1:])
+
+
+# ---- sorted, value-returning output --------------------------------------------------------
+
+def _py_key(v):
+    u = int(np.asarray(v, dtype=np.float32).view(np.uint32))
+    return (~u & 0xFFFFFFFF) if u & 0x80000000 else (u | 0x80000000)
+
+
+def test_sorted_oracle_matches_python_sort_on_tiny_rows():
+    rng = random.Random(7)
+    pool = [0.0, -0.0, 1.0, -1.0, 2.5, float("inf"), float("-inf"), 1e-45, -1e-45, 3.0, 3.0]
+    for _ in range(400):
+        L = rng.randint(0, 24)
+        N = max(L, 1) + rng.randint(0, 3)
+        K = rng.randint(1, 30)
+        row = np.array([rng.choice(pool) for _ in range(N)], dtype=np.float32)
+        idx, val = oracle.topk_sorted(row[None, :], np.array([L], dtype=np.int32), K, -7)
+        want = sorted(range(L), key=lambda j: (-_py_key(row[j]), j))[:min(K, L)]
+        want_idx = want + [-7] * (K - len(want))
+        assert idx[0].tolist() == want_idx
+        want_val = np.array([row[j] for j in want] + [-np.inf] * (K - len(want)), dtype=np.float32)
+        assert np.array_equal(val[0].view(np.uint32), want_val.view(np.uint32))
+
+
+def test_sorted_oracle_closed_forms_and_agreement_with_topk():
+    # Position-valued rows: the sorted output is L-1, L-2, ... with values equal to the indices.
+    N, K = 100, 16
+    s = np.tile(np.arange(N, dtype=np.float32), (3, 1))
+    L = np.array([100, 40, 9], dtype=np.int32)
+    idx, val = oracle.topk_sorted(s, L, K, -1)
+    for r in range(3):
+        n = min(K, int(L[r]))
+        assert idx[r, :n].tolist() == list(range(int(L[r]) - 1, int(L[r]) - 1 - n, -1))
+        assert np.array_equal(val[r, :n], idx[r, :n].astype(np.float32))
+        assert (idx[r, n:] == -1).all() and np.isneginf(val[r, n:]).all()
+    # Rows longer than K: the plain oracle's rows are already in this order.
+    rng = np.random.default_rng(3)
+    s = rng.integers(0, 6, size=(20, 300)).astype(np.float32)
+    L = rng.integers(K + 1, 301, size=20).astype(np.int32)
+    idx, val = oracle.topk_sorted(s, L, K, -1)
+    assert np.array_equal(idx, oracle.topk(s, L, K, -1))
+    assert np.array_equal(val, np.take_along_axis(s, idx.astype(np.int64), axis=1))
