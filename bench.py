@@ -59,6 +59,8 @@ def parse():
                     help="row-to-workgroup mapping (auto: the library's shape-based choice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy first (known bytes, for counter calibration)")
+    ap.add_argument("--sorted", action="store_true",
+                    help="time topk_exact_sorted (indices by score descending plus their values) instead")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "script with --copy-calibration into profiles/hbm_traffic_<workload>.json")
@@ -409,14 +411,21 @@ def main():
     groups = [(window[g * w.M:(g + 1) * w.M], lengths[g * w.M:(g + 1) * w.M].contiguous())
               for g in range(w.groups)]
     outs = [torch.empty((w.M, K), dtype=torch.int32, device=dev) for _ in range(w.groups)]
+    vals = [torch.empty((w.M, K), dtype=torch.float32, device=dev) for _ in range(w.groups)] if args.sorted else None
     tk.reserve(w.M, w.n_alloc, K)
+
+    def select(g, s, l, stream=None):
+        if args.sorted:
+            tk.topk_exact_sorted(s, l, K=K, sentinel=sentinel, out=outs[g], out_values=vals[g], stream=stream)
+        else:
+            tk.topk_exact(s, l, K=K, sentinel=sentinel, out=outs[g], stream=stream)
     tk.set_execution(EXECUTIONS[args.execution])
 
     # Contract gate on every group before anything is timed.
     tk.reset_stats()
     violations, checked = 0, 0
     for g, (s, l) in enumerate(groups):
-        tk.topk_exact(s, l, K=K, sentinel=sentinel, out=outs[g])
+        select(g, s, l)
         torch.cuda.synchronize()
         n_chk = min(args.check_rows, w.M)
         rows = sorted(set([0, w.M - 1] + [int(i) for i in torch.linspace(0, w.M - 1, n_chk).round().tolist()]))
@@ -436,7 +445,7 @@ def main():
             for g, (s, l) in enumerate(groups):
                 gr = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(gr, stream=stream):
-                    tk.topk_exact(s, l, K=K, sentinel=sentinel, out=outs[g])
+                    select(g, s, l)
                 graphs.append(gr)
         torch.cuda.synchronize()
 
@@ -446,7 +455,7 @@ def main():
             graphs[g].replay()
         else:
             s, l = groups[g]
-            tk.topk_exact(s, l, K=K, sentinel=sentinel, out=outs[g], stream=stream)
+            select(g, s, l, stream=stream)
 
     with torch.cuda.stream(stream):
         for i in range(args.warmup + args.condition):
@@ -521,7 +530,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N_alloc": w.n_alloc, "K": K, "groups": w.groups,
                    "lengths": w.lengths, "tail_p": w.tail_p, "bf16_rounded": w.bf16,
-                   "launch": "eager" if args.eager else "hipGraph replay", "execution": args.execution},
+                   "launch": "eager" if args.eager else "hipGraph replay", "execution": args.execution,
+                   "output": "sorted indices + values" if args.sorted else "unordered indices"},
         "hbm_gbps": steps_bytes / wall / 1e9,
         "hbm_frac_of_peak": steps_bytes / wall / 1e9 / HBM_PEAK_GBPS,
         "median_call_ms": statistics.median(per_call_ms),

@@ -46,7 +46,7 @@ EXPORTED = (
     "topk_exact", "topk_exact_reserve", "topk_exact_get_stats", "topk_exact_reset_stats",
     "topk_exact_set_path_override", "topk_exact_last_error", "topk_stream_read_probe",
     "topk_exact_set_execution", "topk_exact_time_next_call", "topk_exact_set_proposal",
-    "topk_indexer_scores", "topk_indexer_topk",
+    "topk_indexer_scores", "topk_indexer_topk", "topk_exact_sorted",
 )
 
 
@@ -90,6 +90,8 @@ def lib() -> ctypes.CDLL:
         L.topk_stream_read_probe.argtypes = [vp, i64, vp, vp]
         L.topk_indexer_scores.restype = ctypes.c_int
         L.topk_indexer_scores.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, vp, vp]
+        L.topk_exact_sorted.restype = ctypes.c_int
+        L.topk_exact_sorted.argtypes = [vp, vp, i64, i64, i32, vp, vp, i32, vp]
         L.topk_indexer_topk.restype = ctypes.c_int
         L.topk_indexer_topk.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, vp, vp, i32, vp]
         _lib = L
@@ -140,6 +142,41 @@ def topk_exact(scores: torch.Tensor, row_len: torch.Tensor, K: int = 2048, senti
                                 sentinel, _stream_handle(scores.device, stream))
     _check(code, "topk_exact")
     return out
+
+
+def topk_exact_sorted(scores: torch.Tensor, row_len: torch.Tensor, K: int = 2048, sentinel: int = -1,
+                      values: bool = True, out: Optional[torch.Tensor] = None,
+                      out_values: Optional[torch.Tensor] = None, stream=None):
+    """Sorted, value-returning top-K: (indices int32 [M, K], values float32 [M, K] or None).
+
+    Each row lists its selected indices by score descending (ties by index ascending),
+    then the sentinel; values are the scores of the listed indices and -inf in sentinel
+    slots. Same inputs and stream semantics as topk_exact.
+    """
+    if scores.dim() != 2 or scores.dtype != torch.float32 or not scores.is_cuda:
+        raise ValueError("scores must be a 2-D float32 GPU tensor")
+    M, N = scores.shape
+    if scores.stride(1) != 1 or (M > 1 and scores.stride(0) != N):
+        raise ValueError("scores must be row-major with row stride N_alloc")
+    if row_len.dtype != torch.int32 or row_len.device != scores.device or tuple(row_len.shape) != (M,) \
+            or not row_len.is_contiguous():
+        raise ValueError("row_len must be a contiguous int32 [M] tensor on the scores' device")
+    dev = scores.device
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.int32, device=dev)
+    elif out.dtype != torch.int32 or out.device != dev or tuple(out.shape) != (M, K) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 [M, K] tensor on the scores' device")
+    if values and out_values is None:
+        out_values = torch.empty((M, K), dtype=torch.float32, device=dev)
+    if out_values is not None and (out_values.dtype != torch.float32 or out_values.device != dev
+                                   or tuple(out_values.shape) != (M, K) or not out_values.is_contiguous()):
+        raise ValueError("out_values must be a contiguous float32 [M, K] tensor on the scores' device")
+    with torch.cuda.device(dev):
+        code = lib().topk_exact_sorted(scores.data_ptr(), row_len.data_ptr(), M, N, K, out.data_ptr(),
+                                       out_values.data_ptr() if out_values is not None else None,
+                                       sentinel, _stream_handle(dev, stream))
+    _check(code, "topk_exact_sorted")
+    return out, out_values
 
 
 def reserve(M_max: int, N_alloc_max: int, K: int = 2048, device=None):

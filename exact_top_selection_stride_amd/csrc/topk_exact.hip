@@ -97,6 +97,7 @@ static_assert(NB % BLOCK == 0, "bins per thread must be integral");
 // candidates overflow them take exact recovery.
 static_assert(TOPK_K_MAX * 7 / 4 + 1 <= CAP, "candidate buffer must hold the tau1 target");
 static_assert(FL_CAP <= BLOCK, "frontier lists are ranked one element per thread");
+static_assert(TOPK_K_MAX <= 8 * BLOCK, "the sorted output holds at most 8 entries per thread");
 
 struct Control {
   uint32_t row_ticket;   // next row of the persistent row loop
@@ -1983,6 +1984,100 @@ int stream_capturing(hipStream_t stream, bool* capturing) {
   return TOPK_OK;
 }
 
+// ------------------------------------------------------------ sorted output
+//
+// The sorted, value-returning output (an option beyond the pages' unordered contract):
+// one workgroup per row orders the row's selected entries by (key descending, index
+// ascending), then writes the indices and their scores; slots past the row's valid
+// entries keep the sentinel and get -inf. Entries are 64-bit composites
+// (key << 32 | ~index), never 0 for a valid entry (indices are below 2^31), so the zero
+// padding sorts last. The order comes from a bitonic network over P = EPT * BLOCK
+// entries, thread t holding entries t*EPT .. t*EPT+EPT-1: exchange distances below EPT
+// stay in registers, those below one wave's share go through cross-lane shuffles, and
+// only the few larger ones go through LDS with barriers.
+template <int EPT>
+__global__ __launch_bounds__(BLOCK) void sort_rows_kernel(const float* __restrict__ scores,
+                                                          const int32_t* __restrict__ row_len,
+                                                          uint32_t N, uint32_t K,
+                                                          int32_t* __restrict__ out_idx,
+                                                          float* __restrict__ out_val, int32_t sentinel) {
+  constexpr uint32_t P = (uint32_t)EPT * BLOCK;
+  __shared__ uint64_t c[P];
+  const uint32_t row = blockIdx.x, t = threadIdx.x;
+  const int32_t len = row_len[row];
+  uint32_t L = len < 0 ? 0u : (uint32_t)len;
+  if (L > N) L = N;
+  const uint32_t n = L < K ? L : K;  // valid entries of the row
+  int32_t* o = out_idx + (size_t)row * K;
+  const uint32_t* x = reinterpret_cast<const uint32_t*>(scores) + (size_t)row * N;
+  uint64_t v[EPT];
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    const uint32_t e = t * EPT + (uint32_t)q;
+    v[q] = 0;
+    if (e < n) {
+      // The selector wrote an index in [0, L) here; the clamp only keeps reads in bounds.
+      const uint32_t i = (uint32_t)o[e] < L ? (uint32_t)o[e] : 0u;
+      v[q] = ((uint64_t)key_of_bits(x[i]) << 32) | (uint64_t)(0xFFFFFFFFu - i);
+    }
+  }
+  // Bitonic network: for each (k, j) every entry e meets e ^ j; a run is descending where
+  // bit k of e is clear, and the lower entry of a pair keeps the larger value there.
+  for (uint32_t k = 2; k <= P; k <<= 1) {
+    for (uint32_t j = k >> 1; j > 0; j >>= 1) {
+      if (j < (uint32_t)EPT) {
+#pragma unroll
+        for (int q = 0; q < EPT; ++q) {
+          if (((uint32_t)q & j) == 0) {
+            const int r = q | (int)j;
+            const bool desc = ((t * EPT + (uint32_t)q) & k) == 0;
+            const uint64_t a = v[q], b = v[r];
+            if (desc ? (a < b) : (a > b)) {
+              v[q] = b;
+              v[r] = a;
+            }
+          }
+        }
+      } else {
+        const uint32_t m = j / EPT;  // partner thread t ^ m, same register slot
+        const bool lo = (t & m) == 0;
+        if (m < (uint32_t)WAVE) {
+#pragma unroll
+          for (int q = 0; q < EPT; ++q) {
+            const uint64_t p = __shfl_xor(v[q], (int)m);
+            const bool desc = ((t * EPT + (uint32_t)q) & k) == 0;
+            v[q] = (desc == lo) ? (v[q] > p ? v[q] : p) : (v[q] < p ? v[q] : p);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < EPT; ++q) c[t * EPT + (uint32_t)q] = v[q];
+          __syncthreads();
+#pragma unroll
+          for (int q = 0; q < EPT; ++q) {
+            const uint64_t p = c[(t * EPT + (uint32_t)q) ^ j];
+            const bool desc = ((t * EPT + (uint32_t)q) & k) == 0;
+            v[q] = (desc == lo) ? (v[q] > p ? v[q] : p) : (v[q] < p ? v[q] : p);
+          }
+          __syncthreads();
+        }
+      }
+    }
+  }
+  float* val = out_val ? out_val + (size_t)row * K : nullptr;
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) {
+    const uint32_t e = t * EPT + (uint32_t)q;
+    if (e < n) {
+      const uint32_t key = (uint32_t)(v[q] >> 32);
+      o[e] = (int32_t)(0xFFFFFFFFu - (uint32_t)v[q]);
+      if (val) val[e] = __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
+    } else if (e < K) {
+      o[e] = sentinel;
+      if (val) val[e] = -__builtin_inff();
+    }
+  }
+}
+
 }  // namespace
 
 // The indexer score producer's host-side checks and launch (indexer_scores.hip).
@@ -2168,6 +2263,32 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
   const int rc = selector_check(scores, row_len, M, N_alloc, K, out_idx, sentinel, stream, &capturing, &st);
   if (rc != TOPK_OK || st == nullptr) return rc;
   return selector_launch(scores, row_len, M, N_alloc, K, out_idx, sentinel, stream, capturing, st);
+}
+
+int topk_exact_sorted(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc, int32_t K,
+                      int32_t* out_idx, float* out_val, int32_t sentinel, hipStream_t stream) {
+  g_err[0] = '\0';
+  bool capturing = false;
+  DevState* st = nullptr;
+  int rc = selector_check(scores, row_len, M, N_alloc, K, out_idx, sentinel, stream, &capturing, &st);
+  if (rc != TOPK_OK || st == nullptr) return rc;
+  if ((reinterpret_cast<uintptr_t>(out_val) & 3u) != 0) return fail(TOPK_ERR_BAD_ARG, "out_val is not 4-byte aligned");
+  rc = selector_launch(scores, row_len, M, N_alloc, K, out_idx, sentinel, stream, capturing, st);
+  if (rc != TOPK_OK) return rc;
+  // Entries per thread: the smallest power of two with EPT * BLOCK >= K (K <= 4096).
+  const dim3 grid((unsigned)M), block(BLOCK);
+  const uint32_t NN = (uint32_t)N_alloc, KK = (uint32_t)K;
+  if (K <= BLOCK)
+    hipLaunchKernelGGL(sort_rows_kernel<1>, grid, block, 0, stream, scores, row_len, NN, KK, out_idx, out_val, sentinel);
+  else if (K <= 2 * BLOCK)
+    hipLaunchKernelGGL(sort_rows_kernel<2>, grid, block, 0, stream, scores, row_len, NN, KK, out_idx, out_val, sentinel);
+  else if (K <= 4 * BLOCK)
+    hipLaunchKernelGGL(sort_rows_kernel<4>, grid, block, 0, stream, scores, row_len, NN, KK, out_idx, out_val, sentinel);
+  else
+    hipLaunchKernelGGL(sort_rows_kernel<8>, grid, block, 0, stream, scores, row_len, NN, KK, out_idx, out_val, sentinel);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "launch sort_rows_kernel");
+  return TOPK_OK;
 }
 
 int topk_indexer_topk(const uint8_t* q, const uint8_t* k, const float* w, const int32_t* row_len,

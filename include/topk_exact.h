@@ -110,6 +110,18 @@ enum {
 int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc,
                int32_t K, int32_t* out_idx, int32_t sentinel, hipStream_t stream);
 
+/* Sorted, value-returning variant (an option beyond the pages' unordered contract): the
+ * same selection as topk_exact, then each row's entries ordered by score descending
+ * (IEEE totalOrder), ties by index ascending. For L > K: the K selected indices in that
+ * order; for L <= K: all L valid indices in that order, then the sentinel.
+ *   out_val  device, row-major [M][K] float32, or NULL for indices only; it receives the
+ *            score of each listed index (bit for bit) and -inf in sentinel slots.
+ * Other arguments, errors and capture behaviour as for topk_exact. The selected set is
+ * the same as topk_exact's; which of several boundary-tied scores are kept is free, the
+ * order of the output is fully determined by that set. */
+int topk_exact_sorted(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc,
+                      int32_t K, int32_t* out_idx, float* out_val, int32_t sentinel, hipStream_t stream);
+
 /* Creates the current device's workspace (control block, recovery queue and, when
  * M_max <= 1024, the row-split state) and resolves launch parameters. Synchronous;
  * call it outside stream capture before capturing topk_exact. */

@@ -80,6 +80,12 @@ def test_argument_validation_without_gpu():
     assert L.topk_indexer_scores(None, fake, fake, fake, 2, 10, 64, 128, fake, None) == B.TOPK_ERR_NULL_POINTER
     assert L.topk_indexer_scores(fake, fake, fake, fake, 2, 10, 64, 128, None, None) == B.TOPK_ERR_NULL_POINTER
     assert L.topk_indexer_scores(None, None, None, None, 0, 10, 64, 128, None, None) == B.TOPK_OK
+    # Sorted variant: the selector's checks, and a misaligned value buffer, before enqueueing.
+    so = L.topk_exact_sorted
+    assert so(fake, fake, 2, 10, 0, fake, fake, -1, None) == B.TOPK_ERR_BAD_K
+    assert so(fake, fake, 2, 10, 4, fake, fake, 3, None) == B.TOPK_ERR_BAD_SENTINEL
+    assert so(fake, fake, 2, 10, 4, None, fake, -1, None) == B.TOPK_ERR_NULL_POINTER
+    assert so(None, None, 0, 10, 4, None, None, -1, None) == B.TOPK_OK
     # Score + select chain: the checks of both steps run before anything is enqueued.
     ch = L.topk_indexer_topk
     assert ch(fake, fake, fake, fake, 2, 10, 64, 128, 0, fake, fake, -1, None) == B.TOPK_ERR_BAD_K

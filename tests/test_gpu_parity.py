@@ -657,3 +657,78 @@ def test_capture_without_reserve_in_a_fresh_process():
     assert res["capture_without_workspace"] == 5  # TOPK_ERR_WORKSPACE
     assert res["violations"] == 0
     assert res["stats"]["rows"] == 2 and res["stats"]["rowsplit"] == 0
+
+
+# ---------------------------------------------------------- sorted, value-returning output
+
+def _check_sorted(scores, lengths, idx, val, K, sentinel=-1, label=""):
+    """GPU sorted output against oracle.topk_sorted. The score sequence is unique, so values
+    must match bit for bit; indices must match wherever the score differs from the row's
+    boundary score (the K-th), and the boundary-tied indices must ascend. The set itself
+    passes the contract check."""
+    s = scores.detach().cpu().numpy()
+    L = lengths.detach().cpu().numpy().astype(np.int32)
+    gi = idx.detach().cpu().numpy()
+    ref_i, ref_v = oracle.topk_sorted(s, L, K, sentinel)
+    n_bad, status = oracle.check_contract(s, L, K, sentinel, gi, oracle.topk(s, L, K, sentinel))
+    assert n_bad == 0, f"{label}: contract {[(int(r), oracle.CHK_NAMES[int(status[r])]) for r in np.nonzero(status)[0][:5]]}"
+    if val is not None:
+        gv = val.detach().cpu().numpy()
+        same = gv.view(np.uint32) == ref_v.view(np.uint32)
+        assert same.all(), f"{label}: values differ in rows {np.nonzero(~same.all(axis=1))[0][:8].tolist()}"
+    for r in range(s.shape[0]):
+        n = min(int(np.clip(L[r], 0, s.shape[1])), K)
+        if n == 0:
+            assert (gi[r] == sentinel).all()
+            continue
+        rv = ref_v[r, :n].view(np.uint32)
+        b = rv[n - 1]
+        strict = rv != b
+        assert np.array_equal(gi[r, :n][strict], ref_i[r, :n][strict]), f"{label}: row {r} order differs"
+        tied = gi[r, :n][~strict]
+        assert (np.diff(tied) > 0).all(), f"{label}: row {r} boundary ties not ascending"
+        assert (s[r, tied].view(np.uint32) == b).all()
+        assert (gi[r, n:] == sentinel).all()
+
+
+def test_sorted_output_workloads():
+    s0, l0 = W.make_window(W.get("c0"), DEV)
+    idx, val = tk.topk_exact_sorted(s0, l0, K=K)
+    torch.cuda.synchronize()
+    _check_sorted(s0, l0, idx, val, K, label="c0")
+    s1, l1 = _window_rows("c1", [(0, 6), (8186, 6)])
+    idx, val = tk.topk_exact_sorted(s1, l1, K=K)
+    torch.cuda.synchronize()
+    _check_sorted(s1, l1, idx, val, K, label="c1")
+    s4, l4 = _window_rows("c4_n65536_m512", [(0, 8)])    # bf16 ties at the boundary
+    idx, val = tk.topk_exact_sorted(s4, l4, K=K)
+    torch.cuda.synchronize()
+    _check_sorted(s4, l4, idx, val, K, label="c4 bf16")
+    idx2, none = tk.topk_exact_sorted(s4, l4, K=K, values=False)
+    torch.cuda.synchronize()
+    assert none is None
+    _check_sorted(s4, l4, idx2, None, K, label="c4 bf16, indices only")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_sorted_output_random_shapes(seed):
+    s, l, Kr, n_alloc = _random_case(200 + seed)
+    for mode in (tk.PATH_AUTO, tk.PATH_SAMPLED, tk.PATH_RECOVERY, tk.PATH_ROWSPLIT):
+        tk.set_path_override(mode)
+        try:
+            idx, val = tk.topk_exact_sorted(s, l, K=Kr)
+            torch.cuda.synchronize()
+        finally:
+            tk.set_path_override(tk.PATH_AUTO)
+        _check_sorted(s, l, idx, val, Kr, label=f"seed {seed} K {Kr} mode {mode}")
+
+
+def test_sorted_output_k4096_and_misaligned_values():
+    s, l = _window_rows("c3a", [(8000, 3)])
+    idx, val = tk.topk_exact_sorted(s, l, K=4096)
+    torch.cuda.synchronize()
+    _check_sorted(s, l, idx, val, 4096, label="1M rows, K 4096")
+    buf = torch.empty(3 * 4096 + 1, dtype=torch.float32, device=DEV)
+    code = tk.lib().topk_exact_sorted(s.data_ptr(), l.data_ptr(), 3, s.shape[1], 4096, idx.data_ptr(),
+                                      buf.data_ptr() + 2, -1, torch.cuda.current_stream().cuda_stream)
+    assert code == 7  # TOPK_ERR_BAD_ARG, nothing enqueued
