@@ -382,8 +382,8 @@ def main():
     if args.summarize_counters:
         return summarize_counters(args)
     if args.gpus != 1:
-        print(json.dumps({"error": "this selector build runs on one GPU only; "
-                                   "the multi-GPU row sharding is a design note, not built",
+        print(json.dumps({"error": "the selector runs on one GPU only (--gpus 1); sharding rows "
+                                   "across GPUs, with no exchange between them, is not implemented",
                           "n_gpus_requested": args.gpus}), flush=True)
         return 2
     if args.workload in CHAIN_NAMES:
