@@ -128,7 +128,9 @@ __global__ __launch_bounds__(WAVES * 64) void indexer_scores_kernel(
       wl[i][hg][0] = wv.x; wl[i][hg][1] = wv.y; wl[i][hg][2] = wv.z; wl[i][hg][3] = wv.w;
     }
   }
-  const int Lmax = max(L[0], L[1]);
+  int Lmax = 0;  // the wave's longest row: blocks past it only write -inf
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) Lmax = max(Lmax, L[i]);
   const float ninf = -__builtin_inff();
 
   // Staging: thread tid copies bytes [part * 32, part * 32 + 32) of key (tid / 4) of a block.
