@@ -161,6 +161,18 @@ def cpu_baseline(scores, lengths, K, sentinel, target_s, max_rows=1024):
                       f"{reps} times on host copies, {spent:.1f} s of selection"}
 
 
+def copy_calibration(dev):
+    """Three plain device copies of exactly 2^28 floats (1 GiB read + 1 GiB written each):
+    known bytes that scale the HBM counters of the same run."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def _counter_rows(d):
     """(kernel name, dispatch id, counter value) rows of a rocprofv3 --pmc csv output dir."""
     import csv
@@ -263,12 +275,7 @@ def run_chain(args):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     if args.copy_calibration:
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(dev)
     q, k, w, L = W.make_chain(c, dev)
     scores = torch.empty((c.M, c.n_alloc), dtype=torch.float32, device=dev)
     idx = torch.empty((c.M, K), dtype=torch.int32, device=dev)
@@ -397,13 +404,7 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     if args.copy_calibration:
-        # A plain copy of exactly 2^28 floats (1 GiB read + 1 GiB written) per launch.
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(dev)
     t_gen = time.perf_counter()
     window, lengths = W.make_window(w, dev)
     torch.cuda.synchronize()
