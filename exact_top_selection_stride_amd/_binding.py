@@ -38,7 +38,7 @@ EXEC_ROWSPLIT = 3
 
 STAT_NAMES = (
     "rows", "sentinel", "direct", "sampled", "tau0", "tau1", "recover_under", "recover_over",
-    "rowsplit", "forced_recovery", "long_exact", "frontier_wide", "queued",
+    "rowsplit", "forced_recovery", "long_exact", "frontier_wide", "queued", "persistent", "row_per_wg",
 )
 STAT_COUNT = 16
 

@@ -208,7 +208,9 @@ __attribute__((visibility("hidden"))) int topk_indexer_check(const uint8_t* q, c
                                                             int64_t T, int64_t S, int32_t H, int32_t D,
                                                             const float* out) {
   if (T < 0) return topk_record_error(TOPK_ERR_BAD_SHAPE, "indexer: T is negative");
-  if (S < 1 || S > INT32_MAX) return topk_record_error(TOPK_ERR_BAD_SHAPE, "indexer: S outside [1, INT32_MAX]");
+  // Key offsets are int arithmetic in the kernel: the last key chunk ends below INT32_MAX.
+  if (S < 1 || S > (int64_t)INT32_MAX - KEYS_PER_WG)
+    return topk_record_error(TOPK_ERR_BAD_SHAPE, "indexer: S outside [1, INT32_MAX - 4096]");
   if (T > INT32_MAX || (T > 0 && S > INT64_MAX / 4 / T))
     return topk_record_error(TOPK_ERR_BAD_SHAPE, "indexer: T outside [0, INT32_MAX] or T * S overflows");
   if (D != DIM) return topk_record_error(TOPK_ERR_BAD_ARG, "indexer: D must be 128");

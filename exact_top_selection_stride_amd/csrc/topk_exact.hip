@@ -1115,19 +1115,22 @@ template <bool STREAM_SAMPLE>
 __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_t x, uint32_t L, gout_t out) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
-  const uint32_t n_s = (L + p.stride - 1) / p.stride;
-  if (n_s > (uint32_t)KEYS_CAP) {
-    if (t == 0) stat_add(p.ctl, TOPK_STAT_LONG_EXACT);
-    exact_full_row(x, L, p.K, 0u, KEY_MAX, out, p.ctl);
-    return;
+  // Rows whose stride-s sample would not fit the LDS key list (L > 16384 s, past the
+  // widths the method is defined on) keep a fixed stride, doubled until it fits: the
+  // positions stay on the stride-s grid, and the proposal only steers the work.
+  uint32_t stride = p.stride;
+  while ((L + stride - 1) / stride > (uint32_t)KEYS_CAP) stride *= 2u;
+  const uint32_t n_s = (L + stride - 1) / stride;
+  if (t == 0) {
+    stat_add(p.ctl, TOPK_STAT_SAMPLED);
+    if (stride != p.stride) stat_add(p.ctl, TOPK_STAT_LONG_EXACT);
   }
-  if (t == 0) stat_add(p.ctl, TOPK_STAT_SAMPLED);
   // Fixed-stride row-local view: keys of x[j * s], j < ceil(L / s), in s.buf[0, n_s).
   // Line-granular sampling (and the line skipping it enables) holds at the method's
   // stride of 128 and is used where it pays (p.line_min, chosen by shape on the host);
   // otherwise, and for other strides, the sample is read element by element and the
   // full pass reads the whole row.
-  const bool by_lines = p.stride == STRIDE && n_s <= LINE_SAMPLE_MAX && n_s >= p.line_min;
+  const bool by_lines = stride == STRIDE && n_s <= LINE_SAMPLE_MAX && n_s >= p.line_min;
   if (by_lines) {
     sample_lines<STREAM_SAMPLE>(x, L, n_s, &s.buf[0], &s.buf[CAP]);
   } else {
@@ -1137,7 +1140,7 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
       // Last sample first: the lines read last are the ones the pass, which runs
       // from the row's start, meets first, while they are still cached.
       const uint32_t j = n_s - 1u - jr;
-      const uint32_t k = key_of_bits(x[(size_t)j * p.stride]);
+      const uint32_t k = key_of_bits(x[(size_t)j * stride]);
       s.buf[j] = k;
       mn = min(mn, k);
       mx = max(mx, k);
@@ -1242,7 +1245,10 @@ void topk_rows_kernel(Params p) {
     // 0.383 ms per call). With persistent execution the rows are staggered and plain
     // loads let the hot sampled lines come back from cache (8192 rows of 1M were 1%
     // slower with non-temporal sample loads).
-    if (t == 0) s.row = (int32_t)blockIdx.x;
+    if (t == 0) {
+      s.row = (int32_t)blockIdx.x;
+      stat_add(p.ctl, TOPK_STAT_ROW_PER_WG);
+    }
     process_row<true>(p, blockIdx.x);
     return;
   }
@@ -1251,6 +1257,7 @@ void topk_rows_kernel(Params p) {
     __syncthreads();
     const uint32_t row = (uint32_t)s.row;
     if (row >= p.M) break;
+    if (t == 0) stat_add(p.ctl, TOPK_STAT_PERSISTENT);
     process_row(p, row);
     __syncthreads();
   }
@@ -1296,7 +1303,7 @@ __global__ __launch_bounds__(BLOCK) void recovery_hist_kernel(Params p) {
     const uint32_t begin = (item - q * per_row) * REC_SEG;
     RecSlot* r = p.rec + q;
     const uint32_t L = r->L;
-    if (begin >= L) continue;
+    if (begin >= L || r->row >= p.M || L > p.N) continue;  // (a slot of a call that failed)
     const uint32_t n = min(REC_SEG, L - begin);
     const uint32_t lo = r->lo, hi = r->hi;
     const uint32_t sh = shift_for(hi - lo);
@@ -1361,7 +1368,7 @@ __global__ __launch_bounds__(BLOCK) void recovery_collect_kernel(Params p) {
     const uint32_t begin = (item - q * per_row) * REC_SEG;
     RecSlot* r = p.rec + q;
     const uint32_t L = r->L;
-    if (begin >= L) continue;
+    if (begin >= L || r->row >= p.M || L > p.N) continue;  // (a slot of a call that failed)
     const uint32_t n = min(REC_SEG, L - begin);
     // The item stays in registers; its loads are issued first so that they overlap
     // the boundary-bin search below. Then this thread's keys above the bin and in
@@ -1509,6 +1516,7 @@ void recovery_finish_kernel(Params p) {
   const uint32_t nq = min(p.ctl->qcount, QMAX);
   for (uint32_t q = blockIdx.x; q < nq; q += gridDim.x) {
     RecSlot* r = p.rec + q;
+    if (r->row >= p.M || r->L > p.N) continue;  // (a slot of a call that failed)
     const uint32_t above = r->bin_above, cb = r->bin_count;
     const uint32_t blo = r->bin_lo, bhi = r->bin_hi;
     const uint32_t need = K - above;
@@ -1881,7 +1889,7 @@ struct DevState {
   int occ_rec = 0;      // resident recovery-collect workgroups per CU
   Control* ctl = nullptr;
   RecSlot* rec = nullptr;
-  RowSplitState* rs = nullptr;  // row-split state for RS_MAX_ROWS rows, made on first use
+  RowSplitState* rs = nullptr;  // row-split state for RS_MAX_ROWS rows
 };
 
 constexpr int MAX_DEVICES = 64;
@@ -1932,9 +1940,11 @@ int get_state(bool capturing, DevState** out) {
         &occ_rec, reinterpret_cast<const void*>(recovery_finish_kernel), BLOCK, 0);
     if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     if (occ_rec < 1) return fail(TOPK_ERR_HIP, "recovery kernel cannot be resident");
-    // One allocation: the control block, then the recovery slots.
+    // One allocation: the control block, the recovery slots, then the row-split state
+    // (about 160 MB in all), so that no later call allocates.
     const size_t rec_off = (sizeof(Control) + 255) / 256 * 256;
-    const size_t bytes = rec_off + sizeof(RecSlot) * QMAX;
+    const size_t rs_off = (rec_off + sizeof(RecSlot) * QMAX + 255) / 256 * 256;
+    const size_t bytes = rs_off + sizeof(RowSplitState) * RS_MAX_ROWS;
     char* ws = nullptr;
     e = hipMalloc(reinterpret_cast<void**>(&ws), bytes);
     if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
@@ -1949,27 +1959,10 @@ int get_state(bool capturing, DevState** out) {
     st.occ_rec = occ_rec;
     st.ctl = reinterpret_cast<Control*>(ws);
     st.rec = reinterpret_cast<RecSlot*>(ws + rec_off);
+    st.rs = reinterpret_cast<RowSplitState*>(ws + rs_off);
     st.ready = true;
   }
   *out = &st;
-  return TOPK_OK;
-}
-
-// Creates the row-split state of a device (not while capturing).
-int ensure_rowsplit(DevState* st) {
-  std::lock_guard<std::mutex> lock(g_mu);
-  if (st->rs) return TOPK_OK;
-  RowSplitState* rs = nullptr;
-  const size_t bytes = sizeof(RowSplitState) * RS_MAX_ROWS;
-  hipError_t e = hipMalloc(reinterpret_cast<void**>(&rs), bytes);
-  if (e != hipSuccess) return hip_fail(e, "hipMalloc(row-split state)");
-  e = hipMemset(rs, 0, bytes);
-  if (e == hipSuccess) e = hipDeviceSynchronize();
-  if (e != hipSuccess) {
-    (void)hipFree(rs);
-    return hip_fail(e, "row-split state initialisation");
-  }
-  st->rs = rs;
   return TOPK_OK;
 }
 
@@ -2176,24 +2169,20 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
   // 1.507 -> 1.485 ms; 512 x 128K and 64K rows, where most lines are hot, lose with
   // it). A forced sampled path keeps it wherever it applies.
   p.line_min = (p.mode == TOPK_PATH_SAMPLED) ? 0u : p.T1;
-  bool split = M <= (int64_t)RS_MAX_ROWS &&
+  const bool split = M <= (int64_t)RS_MAX_ROWS &&
                (ex == TOPK_EXEC_ROWSPLIT || p.mode == TOPK_PATH_ROWSPLIT ||
                 (ex == TOPK_EXEC_AUTO && N_alloc >= ROWSPLIT_MIN_N &&
                  (N_alloc >= 4 * ROWSPLIT_MIN_N ? 4 * M <= resident : 8 * M <= resident)));
-  if (split && !st->rs) {
-    if (capturing) {
-      split = false;  // no state and no allocation under capture: run unsplit (same result)
-    } else {
-      rc = ensure_rowsplit(st);
-      if (rc != TOPK_OK) return rc;
-    }
-  }
   hipError_t e;
   hipEvent_t ev_start = nullptr, ev_stop = nullptr;
   if (!capturing && g_time_start) {
     ev_start = g_time_start;
     ev_stop = g_time_stop;
     g_time_start = g_time_stop = nullptr;
+    // Both events are checked before anything is enqueued: once the selector kernel is,
+    // the recovery kernels must follow it (they rewind the queue it fills).
+    e = hipEventQuery(ev_stop);
+    if (e != hipSuccess && e != hipErrorNotReady) return hip_fail(e, "timing stop event");
     e = hipEventRecord(ev_start, stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord(start)");
   }
@@ -2227,9 +2216,10 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "launch topk_rows_kernel");
   }
+  // From here on every step is enqueued even if one fails; the first error is returned.
   if (ev_stop) {
     e = hipEventRecord(ev_stop, stream);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(stop)");
+    if (e != hipSuccess) rc = hip_fail(e, "hipEventRecord(stop)");
   }
   // Exact recovery of the rows the selector queued (they exit at once if none). At most
   // min(M, QMAX) rows can be queued, so small calls launch correspondingly small grids.
@@ -2238,16 +2228,16 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
   const unsigned rec_grid = (unsigned)(rec_items < (int64_t)st->n_cu * 4 ? rec_items : (int64_t)st->n_cu * 4);
   hipLaunchKernelGGL(recovery_hist_kernel, dim3(rec_grid), dim3(BLOCK), 0, stream, p);
   e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "launch recovery_hist_kernel");
+  if (e != hipSuccess && rc == TOPK_OK) rc = hip_fail(e, "launch recovery_hist_kernel");
   hipLaunchKernelGGL(recovery_collect_kernel, dim3(rec_grid), dim3(BLOCK), 0, stream, p);
   e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "launch recovery_collect_kernel");
+  if (e != hipSuccess && rc == TOPK_OK) rc = hip_fail(e, "launch recovery_collect_kernel");
   const int64_t fin_cap = (int64_t)st->n_cu * st->occ_rec;
   const unsigned fin_grid = (unsigned)(rec_rows < fin_cap ? rec_rows : fin_cap);
   hipLaunchKernelGGL(recovery_finish_kernel, dim3(fin_grid), dim3(BLOCK), 0, stream, p);
   e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "launch recovery_finish_kernel");
-  return TOPK_OK;
+  if (e != hipSuccess && rc == TOPK_OK) rc = hip_fail(e, "launch recovery_finish_kernel");
+  return rc;
 }
 
 
@@ -2314,8 +2304,7 @@ int topk_exact_reserve(int64_t M_max, int64_t N_alloc_max, int32_t K) {
   DevState* st = nullptr;
   int rc = get_state(false, &st);
   if (rc != TOPK_OK) return rc;
-  // Row-split may be chosen for calls of at most RS_MAX_ROWS rows: create its state now.
-  if (M_max <= (int64_t)RS_MAX_ROWS) return ensure_rowsplit(st);
+  (void)M_max;  // the workspace does not depend on the call shape
   return TOPK_OK;
 }
 

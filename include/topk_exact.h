@@ -85,13 +85,18 @@ enum {
   TOPK_STAT_RECOVER_OVER = 7,    /* sampled rows whose candidates overflowed: exact recovery */
   TOPK_STAT_ROWSPLIT = 8,        /* rows scanned by several workgroups (row-split) */
   TOPK_STAT_FORCED_RECOVERY = 9, /* rows sent to exact recovery by TOPK_PATH_RECOVERY */
-  TOPK_STAT_LONG_EXACT = 10,     /* rows too long for the LDS sample: exact full-row path */
+  TOPK_STAT_LONG_EXACT = 10,     /* rows longer than 16384 sample strides: sampled at a coarser
+                                    fixed stride (a multiple of the set one) */
   TOPK_STAT_FRONTIER_WIDE = 11,  /* refinements whose boundary bin exceeded the frontier buffer */
   TOPK_STAT_QUEUED = 12,         /* recovery rows handed to the cooperative recovery kernels */
+  TOPK_STAT_PERSISTENT = 13,     /* rows taken from the device ticket by the persistent grid */
+  TOPK_STAT_ROW_PER_WG = 14,     /* rows given a workgroup of their own */
   TOPK_STAT_COUNT = 16
 };
 
-/* Selects the top-K indices of every row.
+/* Selects the top-K indices of every row: the operation and contract of [Cx] section
+ * "什么叫精确，时间怎么量" (exact set, sentinel padding of short rows, no tolerance),
+ * computed by the sample-guided method of [PD] question 2 (Fig. 4) and [AX] (abstract).
  *   scores   device, row-major [M][N_alloc] float32, row stride N_alloc; read-only. Only
  *            the first clamp(row_len[r], 0, N_alloc) entries of row r are ever read.
  *   row_len  device, [M] int32, valid prefix length per row. Values outside [0, N_alloc]
@@ -103,9 +108,13 @@ enum {
  *            order and slots [L, K) hold `sentinel`.
  *   sentinel value for empty slots; must lie outside [0, N_alloc) (e.g. -1).
  *   stream   every launch is enqueued here; the call never synchronizes, allocates or
- *            reads device memory from the host once the workspace exists, so it may be
- *            captured into a HIP graph (call topk_exact_reserve first in that case).
- * Returns TOPK_OK, or an error code before anything is enqueued. M == 0 is a no-op.
+ *            reads device memory from the host once the workspace exists (made by
+ *            topk_exact_reserve or the first call outside capture), so it may be captured
+ *            into a HIP graph (call topk_exact_reserve first in that case).
+ * Returns TOPK_OK or an error code. Every argument and workspace error is returned before
+ * anything is enqueued. TOPK_ERR_HIP from a failed launch or timing-event record may come
+ * after kernels were enqueued; the call then still enqueues its recovery kernels, which
+ * keep the device-side queue consistent for later calls. M == 0 is a no-op.
  * Asynchronous device faults surface on the stream like any kernel's. */
 int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc,
                int32_t K, int32_t* out_idx, int32_t sentinel, hipStream_t stream);
@@ -122,31 +131,43 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
 int topk_exact_sorted(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc,
                       int32_t K, int32_t* out_idx, float* out_val, int32_t sentinel, hipStream_t stream);
 
-/* Creates the current device's workspace (control block, recovery queue and, when
- * M_max <= 1024, the row-split state) and resolves launch parameters. Synchronous;
- * call it outside stream capture before capturing topk_exact. */
+/* Creates the current device's workspace (control block, recovery queue and row-split
+ * state, about 160 MB, one allocation) and resolves launch parameters, so that the calls
+ * that follow allocate nothing. The first topk_exact call outside capture does the same;
+ * the pages time only graph replays of calls whose set-up is done ([Cx] section
+ * "什么叫精确，时间怎么量"), and this is that set-up. The arguments are checked (M_max >= 0,
+ * 1 <= N_alloc_max <= INT32_MAX, 1 <= K <= TOPK_K_MAX) but the workspace does not depend
+ * on them. Synchronous (allocates, clears and synchronizes the device); call it outside
+ * stream capture before capturing topk_exact. Returns TOPK_OK, TOPK_ERR_BAD_SHAPE,
+ * TOPK_ERR_BAD_K or TOPK_ERR_HIP. */
 int topk_exact_reserve(int64_t M_max, int64_t N_alloc_max, int32_t K);
 
 /* Copies up to n (<= TOPK_STAT_COUNT) statistics counters of the current device into
- * host_counts (host memory). Synchronizes `stream` first. Not capturable. */
+ * host_counts (host memory): row counts per path since the last reset. They are the
+ * path rates the pages report for the proposal (rows certified at tau0, resolved by the
+ * nested tau1, sent to exact recovery; [Cx] section "采样不是处处都该开"). Synchronizes
+ * `stream` first. Not capturable (TOPK_ERR_BAD_ARG under capture). */
 int topk_exact_get_stats(uint64_t* host_counts, int n, hipStream_t stream);
 
-/* Zeroes the current device's statistics counters (enqueued on `stream`). */
+/* Zeroes the current device's statistics counters (the path rates above), enqueued on
+ * `stream` as a small kernel (capturable once the workspace exists). */
 int topk_exact_reset_stats(hipStream_t stream);
 
-/* Forces one execution path for later calls (TOPK_PATH_*); a captured graph keeps the
- * mode that was set when it was captured. Process-wide. */
+/* Forces one execution path for later calls (TOPK_PATH_*): the pages' boundary swap of
+ * the sampled proposal against an exact one ([Cx] section "采样不是处处都该开") and the
+ * forcing of every path for tests. A captured graph keeps the mode that was set when it
+ * was captured. Process-wide. TOPK_ERR_BAD_ARG for an unknown mode. */
 int topk_exact_set_path_override(int mode);
 
-/* Selects how rows map to workgroups for later calls (TOPK_EXEC_*). Auto uses
- * row-split when N_alloc >= 65536 and M is at most a quarter (N_alloc >= 262144) or an
- * eighth (shorter rows) of the resident workgroup count,
+/* Selects how rows map to workgroups for later calls (TOPK_EXEC_*): the persistent,
+ * row-split (KV-split) and one-row-per-unit executions of [AX] (abstract) and [PD]
+ * (question 2). Auto uses row-split when N_alloc >= 65536 and M is at most a quarter
+ * (N_alloc >= 262144) or an eighth (shorter rows) of the resident workgroup count,
  * persistent execution when M is at least four times the resident workgroup count
  * and N_alloc >= 262144, and one workgroup per row otherwise. Every mode gives a
  * result satisfying the same contract; a captured graph keeps the mode set when it
- * was captured. Row-split needs per-row state for up to 1024 rows (~140 MB), made by
- * topk_exact_reserve(M_max <= 1024, ...) or by the first call that uses it; a call
- * under capture without that state runs unsplit. Process-wide. */
+ * was captured. Row-split serves calls of at most 1024 rows. Process-wide.
+ * TOPK_ERR_BAD_ARG for an unknown mode. */
 int topk_exact_set_execution(int mode);
 
 /* Proposal parameters for later calls (ablations of the pages' mechanism tables,
@@ -160,8 +181,9 @@ int topk_exact_set_execution(int mode);
  * keeps the setting made before its capture. */
 int topk_exact_set_proposal(int32_t stride, int32_t rho0_permille, int32_t rho1_permille);
 
-/* Measurement hook: arms a one-shot timing of the next topk_exact call made on this
- * host thread. That call records `start` on its stream just before its first
+/* Measurement hook (no passage defines it; it serves the per-kernel timing of the
+ * roofline report beside the pages' per-call timing, [Cx] section "什么叫精确，时间怎么量"):
+ * arms a one-shot timing of the next topk_exact call made on this host thread. That call records `start` on its stream just before its first
  * selector kernel and `stop` just after its last one, before the exact-recovery
  * kernels, so hipEventElapsedTime(start, stop) is the selector kernels' device time.
  * The events belong to the caller, were created on the current device with timing
@@ -170,10 +192,12 @@ int topk_exact_set_proposal(int32_t stride, int32_t rho0_permille, int32_t rho1_
  * TOPK_ERR_NULL_POINTER if exactly one event is NULL. */
 int topk_exact_time_next_call(hipEvent_t start, hipEvent_t stop);
 
-/* Text of the last error raised on this host thread ("" if none). */
+/* Text of the last error raised on this host thread ("" if none). A library utility; no
+ * passage defines it. */
 const char* topk_exact_last_error(void);
 
-/* Bandwidth probe (measurement only, not part of the selection): reads n floats from
+/* Bandwidth probe (a measurement aid that no passage defines; the measured read ceiling
+ * reported beside the 8 TB/s peak, not part of the selection): reads n floats from
  * `x` (device, 16-byte aligned) with the same 128-bit non-temporal loads as the selector's
  * full-row pass, one workgroup per consecutive 4 MiB chunk, and writes one float per
  * workgroup into `sink` (device, >= 4096 floats; workgroup b writes slot b mod 4096) so the
@@ -193,7 +217,7 @@ int topk_stream_read_probe(const float* x, int64_t n, float* sink, hipStream_t s
  *   k        device, [S][D] bytes, OCP FP8 E4M3 codes (row-major), 16-byte aligned.
  *   w        device, [T][H] float32 head weights, 16-byte aligned.
  *   row_len  device, [T] int32 valid lengths (the selector's row_len).
- *   T, S     T >= 0 query rows, 1 <= S <= INT32_MAX keys (the selector's N_alloc).
+ *   T, S     T >= 0 query rows, 1 <= S <= INT32_MAX - 4096 keys (the selector's N_alloc).
  *   H, D     H in {16, 32, 48, 64} heads, D = 128 (head dimension).
  *   out      device, row-major [T][S] float32; every element is written.
  *   stream   the kernel is enqueued here; no allocation or synchronization (capturable).

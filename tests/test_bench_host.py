@@ -28,24 +28,72 @@ def _write_run(d, counter, rows):
 
 def test_summarize_counters_scales_by_the_copy(tmp_path):
     # Three 1 GiB calibration copies first; FETCH_SIZE reads half the copy's bytes (x2 scale),
-    # WRITE_SIZE all of them (x1). Selector dispatches read 1000 and 1200 KiB raw (mean 1100),
-    # a later large torch copy and an unrelated kernel must be ignored.
+    # WRITE_SIZE all of them (x1). Two calls: selector dispatches read 1000 and 1200 KiB raw,
+    # the recovery kernels after them 10 + 20 + 30 KiB once; a later large torch copy and an
+    # unrelated kernel must be ignored.
     copy = "__amd_rocclr_copyBuffer"
     sel = "void (anonymous namespace)::topk_rows_kernel<true>((anonymous namespace)::Params)"
+    rec = "(anonymous namespace)::recovery_%s_kernel((anonymous namespace)::Params)"
     fetch = [(2, copy, 524288.0), (3, copy, 524290.0), (4, copy, 524286.0), (5, "other_kernel", 9e9),
-             (6, sel, 1000.0), (7, copy, 262144.0), (8, sel, 1200.0)]
-    write = [(2, copy, 1048576.0), (3, copy, 1048576.0), (4, copy, 1048576.0), (6, sel, 10.0), (8, sel, 30.0)]
+             (6, sel, 1000.0), (7, rec % "hist", 10.0), (8, rec % "collect", 20.0), (9, rec % "finish", 30.0),
+             (10, copy, 262144.0), (11, sel, 1200.0), (12, rec % "hist", 0.0)]
+    write = [(2, copy, 1048576.0), (3, copy, 1048576.0), (4, copy, 1048576.0), (6, sel, 10.0), (11, sel, 30.0),
+             (8, rec % "collect", 4.0)]
     _write_run(str(tmp_path / "f"), "FETCH_SIZE", fetch)
     _write_run(str(tmp_path / "w"), "WRITE_SIZE", write)
     args = argparse.Namespace(workload="c3b", summarize_counters=[str(tmp_path / "f"), str(tmp_path / "w")])
     assert bench.summarize_counters(args, out_dir=str(tmp_path)) == 0
     out = json.load(open(tmp_path / "hbm_traffic_c3b.json"))
-    assert out["kernel"] == "topk_rows_kernel<true>"
-    assert out["fetch_dispatches"] == 2 and out["write_dispatches"] == 2
+    assert out["kernel"] == ("recovery_collect_kernel + recovery_finish_kernel + recovery_hist_kernel + "
+                             "topk_rows_kernel<true>")
+    assert out["fetch_calls"] == 2 and out["write_calls"] == 2
     assert abs(out["fetch_scale"] - 2.0) < 1e-5 and out["write_scale"] == 1.0
-    assert abs(out["fetch_bytes"] - 1100.0 * 2.0 * 1024) < 1.0
-    assert out["write_bytes"] == 20.0 * 1024
+    assert abs(out["fetch_bytes"] - (2200.0 + 60.0) / 2 * 2.0 * 1024) < 1.0
+    assert out["write_bytes"] == 22.0 * 1024
+    assert abs(out["selector_bytes_per_launch"] - (1100.0 * 2.0 + 20.0) * 1024) < 1.0
+    assert abs(out["bytes_per_launch"] - ((1130.0 * 2.0) + 22.0) * 1024) < 1.0
     assert out["kernel_source_digest"] == bench.kernel_source_digest("selector")
+
+
+def test_summarize_trace_groups_calls(tmp_path):
+    # Two calls (selector + three recovery kernels each) with a probe kernel between them.
+    d = tmp_path / "t"
+    d.mkdir()
+    sel = "void (anonymous namespace)::topk_rows_kernel<false>((anonymous namespace)::Params)"
+    rec = "(anonymous namespace)::recovery_%s_kernel((anonymous namespace)::Params)"
+    rows = [(100, 200, sel), (210, 220, rec % "hist"), (220, 240, rec % "collect"), (240, 250, rec % "finish"),
+            (300, 330, "(anonymous namespace)::stream_read_probe_kernel(float const*, unsigned long, float*)"),
+            (400, 520, sel), (530, 540, rec % "hist"), (540, 560, rec % "collect"), (560, 580, rec % "finish")]
+    with open(d / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        for a, b, n in rows:
+            w.writerow([n, a, b])
+    out = bench.summarize_trace(str(d))
+    assert out["call_spans"]["calls"] == 2
+    assert out["call_spans"]["mean_ns"] == (150 + 180) / 2
+    k = out["kernels"]["topk_rows_kernel<false>"]
+    assert k["calls"] == 2 and k["average_ns"] == 110 and k["min_ns"] == 100 and k["max_ns"] == 120
+    assert out["kernels"]["recovery_finish_kernel"]["average_ns"] == 15
+
+
+def test_protocol_defaults_and_overrides():
+    a = bench.parse([])
+    assert (a.warmup, a.condition, a.steps, a.calls_per_graph, a.workload) == (10, 100, 700, 1, "c3b")
+    b = bench.parse(["--steps", "20", "--warmup", "5", "--workload", "c0"])
+    assert (b.warmup, b.condition, b.steps, b.calls_per_graph) == (5, 100, 20, 100)
+    c = bench.parse(["--protocol", "quick"])
+    assert (c.warmup, c.condition, c.steps) == (5, 20, 40)
+
+
+def test_device_checksum_is_a_64_bit_pattern_sum():
+    x = torch.tensor([[1.0, -2.0], [float("-inf"), 0.5]], dtype=torch.float32)
+    u = x.view(torch.int32).to(torch.int64)
+    assert bench.device_checksum(x) == f"{int(u.sum()) & 0xFFFFFFFFFFFFFFFF:016x}"
+    y = x.clone()
+    y[1, 1] = 0.25
+    assert bench.device_checksum(y) != bench.device_checksum(x)
+    assert bench.device_checksum(torch.tensor([3, 4], dtype=torch.int32)) == f"{7:016x}"
 
 
 def test_gate_rows_flags_each_violation():

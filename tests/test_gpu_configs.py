@@ -1,0 +1,174 @@
+"""GPU parity of every workload configuration at its own launch shape, every row.
+
+Each configuration of the evaluation matrix (page "几何平均快 1.55 倍，但短行采样会输：
+腾讯怎么测精确 Top-K", sections "20 个形状都最快" and "采样不是处处都该开": the last
+8192-row causal window of a width cut into groups of M rows, and the 16K-64K crossover
+sweep) is run exactly as the benchmark launches it: one call per group, automatic
+dispatch, the production execution mode asserted through the library's row counters.
+Every row of every group is then checked on the host against the CPU oracle under the
+set contract of that page's section "什么叫精确，时间怎么量" (distinct in-prefix
+indices, exactly K of them, min(selected) >= max(unselected), the sorted selected key
+multiset equal to the oracle's bit for bit; short rows: every valid index, then the
+sentinel). Integer work: 0 violations allowed.
+
+The window of a width is generated once on the GPU; the calls of all its
+configurations read views of it. The host check copies the window in row blocks,
+runs the oracle once per block and checks every call's output of those rows against
+that one result.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import exact_top_selection_stride_amd as tk
+from exact_top_selection_stride_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+K = 2048
+SENTINEL = -1
+DEV = "cuda"
+HOST_BLOCK_BYTES = 1 << 31  # rows copied to the host per oracle block
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _calls(window, lengths, M, groups, execution=tk.EXEC_AUTO):
+    """Runs one call per group of M rows of the window in the given execution mode and
+    returns (output [groups * M, K] in window row order, row counters of all calls)."""
+    tk.reserve(M, window.shape[1], K)
+    out = torch.empty((groups * M, K), dtype=torch.int32, device=window.device)
+    tk.reset_stats()
+    with tk.execution(execution):
+        for g in range(groups):
+            tk.topk_exact(window[g * M:(g + 1) * M], lengths[g * M:(g + 1) * M].contiguous(), K=K,
+                          sentinel=SENTINEL, out=out[g * M:(g + 1) * M])
+    torch.cuda.synchronize()
+    return out, tk.get_stats()
+
+
+def _check_every_row(window, lengths, outputs, label):
+    """outputs: {name: (first window row, output tensor [rows, K])}. Every output row is
+    checked against the oracle's selection of the same window row."""
+    N = window.shape[1]
+    rows_total = window.shape[0]
+    blk = max(1, HOST_BLOCK_BYTES // (4 * N))
+    host = torch.empty((min(blk, rows_total), N), dtype=torch.float32, pin_memory=True)
+    lens = lengths.cpu().numpy().astype(np.int32)
+    checked = {name: 0 for name in outputs}
+    for r0 in range(0, rows_total, blk):
+        r1 = min(rows_total, r0 + blk)
+        h = host[:r1 - r0]
+        h.copy_(window[r0:r1])
+        s = h.numpy()
+        ref = oracle.topk(s, lens[r0:r1], K, SENTINEL)
+        for name, (first, out) in outputs.items():
+            a, b = max(r0, first), min(r1, first + out.shape[0])
+            if a >= b:
+                continue
+            o = out[a - first:b - first].cpu().numpy()
+            n_bad, status = oracle.check_contract(s[a - r0:b - r0], lens[a:b], K, SENTINEL, o,
+                                                  ref[a - r0:b - r0])
+            if n_bad:
+                bad = np.nonzero(status)[0][:8]
+                detail = [(int(a + i), oracle.CHK_NAMES[int(status[i])], int(lens[a + i])) for i in bad]
+                pytest.fail(f"{label} {name}: {n_bad} rows violate the contract, first (window row, "
+                            f"check, L): {detail}")
+            checked[name] += b - a
+    for name, (first, out) in outputs.items():
+        assert checked[name] == out.shape[0], f"{label} {name}: {checked[name]} of {out.shape[0]} rows checked"
+    _say(f"{label}: every row of {len(outputs)} call sets checked against the oracle "
+         f"({sum(checked.values())} rows)")
+
+
+def test_c1_every_group_every_row():
+    # 512 x 131072: 16 groups of the causal window, one workgroup per row (element-wise
+    # sample, whole-row pass), as the benchmark launches them.
+    w = W.get("c1")
+    s, l = W.make_window(w, DEV)
+    out, st = _calls(s, l, w.M, w.groups)
+    _say(f"c1 stats {st}")
+    assert st["rows"] == 8192 and st["sampled"] == 8192 and st["row_per_wg"] == 8192
+    assert st["rowsplit"] == 0 and st["persistent"] == 0 and st["direct"] == 0
+    _check_every_row(s, l, {"c1 M=512 x 16 groups": (0, out)}, "c1")
+
+
+def test_c2_every_group_every_row():
+    # 4096 x 524288 (0.5% tail): both groups, persistent execution with line sampling.
+    w = W.get("c2")
+    s, l = W.make_window(w, DEV)
+    out, st = _calls(s, l, w.M, w.groups)
+    _say(f"c2 stats {st}")
+    assert st["rows"] == 8192 and st["sampled"] == 8192 and st["persistent"] == 8192
+    assert st["rowsplit"] == 0 and st["row_per_wg"] == 0
+    _check_every_row(s, l, {"c2 M=4096 x 2 groups": (0, out)}, "c2")
+
+
+def test_c3a_c3b_every_row():
+    # The 1M window once: 8192 rows in one persistent call (c3b) and the 16 groups of 512
+    # rows, one workgroup per row (c3a). The cooperative recovery rows of both are part of
+    # the checked set.
+    wb, wa = W.get("c3b"), W.get("c3a")
+    assert (wb.seed, wb.n_alloc, wb.tail_p) == (wa.seed, wa.n_alloc, wa.tail_p)
+    s, l = W.make_window(wb, DEV)
+    out_b, st_b = _calls(s, l, wb.M, wb.groups)
+    _say(f"c3b stats {st_b}")
+    assert st_b["rows"] == 8192 and st_b["sampled"] == 8192 and st_b["persistent"] == 8192
+    assert st_b["rowsplit"] == 0
+    out_a, st_a = _calls(s, l, wa.M, wa.groups)
+    _say(f"c3a stats {st_a}")
+    assert st_a["rows"] == 8192 and st_a["sampled"] == 8192 and st_a["row_per_wg"] == 8192
+    assert st_a["rowsplit"] == 0
+    assert st_a["queued"] + st_b["queued"] > 0  # exact recovery rows are in the checked set
+    _check_every_row(s, l, {"c3b M=8192": (0, out_b), "c3a M=512 x 16 groups": (0, out_a)}, "c3")
+
+
+@pytest.mark.parametrize("n_alloc", W.C4_WIDTHS)
+def test_c4_every_config_every_row(n_alloc):
+    # bf16-rounded ties, M = 512 ... 32768. Configurations up to 8192 rows cut the causal
+    # window into 8192 / M groups; 16384 and 32768 rows tile it (lengths repeat every 8192
+    # rows). The tiled 32768-row window is generated once; its first 8192 rows are the
+    # window of the smaller configurations (checked on the GPU), its first 16384 the
+    # 16384-row one.
+    big = W.get(f"c4_n{n_alloc}_m32768")
+    s, l = W.make_window(big, DEV)
+    s8, l8 = W.make_window(W.get(f"c4_n{n_alloc}_m512"), DEV)
+    assert torch.equal(s[:8192].view(torch.int32), s8.view(torch.int32)) and torch.equal(l[:8192], l8)
+    del s8, l8
+    s16, _ = W.make_window(W.get(f"c4_n{n_alloc}_m16384"), DEV)
+    assert torch.equal(s[:16384].view(torch.int32), s16.view(torch.int32))
+    del s16
+    outputs = {}
+    for M in W.C4_ROWS:
+        w = W.get(f"c4_n{n_alloc}_m{M}")
+        rows = w.M * w.groups
+        out, st = _calls(s[:rows], l[:rows].contiguous(), w.M, w.groups)
+        assert st["rows"] == rows and st["row_per_wg"] == rows and st["rowsplit"] == 0
+        if n_alloc <= 16384:
+            assert st["direct"] == rows   # every causal row of the 16K window is at most 16384 long
+        else:
+            assert st["sampled"] == rows
+        _say(f"c4 n={n_alloc} M={M}: {w.groups} calls, stats {st}")
+        outputs[f"M={M} x {w.groups} groups"] = (0, out)
+    _check_every_row(s, l, outputs, f"c4 n={n_alloc}")
+
+
+def test_rows_past_the_lds_sample_take_a_coarser_stride():
+    # Rows longer than 16384 sample strides (beyond the widths the method is run on) are
+    # sampled at a doubled fixed stride; the result stays exact.
+    N = 3_000_001
+    s, l = W.make_rows(2, N, [N, 2_500_000], tail_p=0.01, seed=31, device=DEV)
+    for mode in (tk.PATH_AUTO, tk.PATH_SAMPLED):
+        tk.set_path_override(mode)
+        try:
+            tk.reset_stats()
+            out = tk.topk_exact(s, l, K=K)
+            torch.cuda.synchronize()
+            st = tk.get_stats()
+        finally:
+            tk.set_path_override(tk.PATH_AUTO)
+        assert st["long_exact"] == 2 and st["sampled"] == 2
+        _check_every_row(s, l, {f"mode {mode}": (0, out)}, "3M rows")

@@ -70,34 +70,42 @@ def test_c0_full():
     assert st["rows"] == 256 and st["sentinel"] == n_short and st["direct"] == 256 - n_short
 
 
+# Reduced-row windows, run in the execution mode their configuration takes at its full
+# size (a few rows alone would be row-split by the automatic choice); the full-size
+# launches, every row, are in test_gpu_configs.py.
+
 def test_c1_rows():
     s, l = _window_rows("c1", [(0, 24), (4000, 8), (8192 - 32, 32)])
-    out, st = _run(s, l)
+    with tk.execution(tk.EXEC_ROW_PER_WG):
+        out, st = _run(s, l)
     _check(s, l, out, label="c1")
-    assert st["sampled"] == 64
+    assert st["sampled"] == 64 and st["row_per_wg"] == 64 and st["rowsplit"] == 0
     assert st["tau0"] + st["tau1"] + st["recover_under"] + st["recover_over"] == 64
 
 
 def test_c2_rows():
     s, l = _window_rows("c2", [(0, 6), (8192 - 6, 6)])
-    out, st = _run(s, l)
+    with tk.execution(tk.EXEC_PERSISTENT):
+        out, st = _run(s, l)
     _check(s, l, out, label="c2")
-    assert st["sampled"] == 12
+    assert st["sampled"] == 12 and st["persistent"] == 12 and st["rowsplit"] == 0
 
 
 def test_c3_rows():
     s, l = _window_rows("c3b", [(0, 3), (5000, 2), (8192 - 3, 3)])
-    out, st = _run(s, l)
+    with tk.execution(tk.EXEC_PERSISTENT):
+        out, st = _run(s, l)
     _check(s, l, out, label="c3")
-    assert st["sampled"] == 8
+    assert st["sampled"] == 8 and st["persistent"] == 8 and st["rowsplit"] == 0
 
 
 @pytest.mark.parametrize("n_alloc", W.C4_WIDTHS)
 def test_c4_bf16_ties(n_alloc):
     s, l = _window_rows(f"c4_n{n_alloc}_m512", [(0, 20), (8192 - 20, 20)])
-    out, st = _run(s, l)
+    with tk.execution(tk.EXEC_ROW_PER_WG):
+        out, st = _run(s, l)
     _check(s, l, out, label=f"c4 n={n_alloc}")
-    assert st["rows"] == 40
+    assert st["rows"] == 40 and st["row_per_wg"] == 40 and st["rowsplit"] == 0
 
 
 # ------------------------------------------------------------ path forcing
@@ -622,8 +630,8 @@ with torch.cuda.stream(stream):
         except tk.TopKError as e:
             res["capture_without_workspace"] = e.code
 torch.cuda.synchronize()
-# 2. Workspace without row-split state (reserve for more than 1024 rows): a few long rows,
-# which auto dispatch would split, run unsplit under capture and stay exact.
+# 2. With the workspace (reserve makes it whole, row-split state included): a few long
+# rows are split under capture with nothing allocated, and stay exact.
 tk.reserve(4096, 1048576, 2048)
 s2, l2 = W.make_rows(2, 1048576, [1048576, 1000000], device="cuda")
 out2 = torch.empty((2, 2048), dtype=torch.int32, device="cuda")
@@ -644,8 +652,8 @@ print(json.dumps(res))
 
 def test_capture_without_reserve_in_a_fresh_process():
     # A fresh process has no workspace: capturing a call must return TOPK_ERR_WORKSPACE
-    # before enqueueing anything; with the workspace but no row-split state, long rows run
-    # unsplit under capture and stay exact.
+    # before enqueueing anything; once reserve has made it, a captured call of a few long
+    # rows runs row-split and stays exact.
     import json
     import os
     import subprocess
@@ -656,7 +664,7 @@ def test_capture_without_reserve_in_a_fresh_process():
     res = json.loads(r.stdout.strip().splitlines()[-1])
     assert res["capture_without_workspace"] == 5  # TOPK_ERR_WORKSPACE
     assert res["violations"] == 0
-    assert res["stats"]["rows"] == 2 and res["stats"]["rowsplit"] == 0
+    assert res["stats"]["rows"] == 2 and res["stats"]["rowsplit"] == 2
 
 
 # ---------------------------------------------------------- sorted, value-returning output
