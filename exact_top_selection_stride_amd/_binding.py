@@ -46,7 +46,7 @@ EXPORTED = (
     "topk_exact", "topk_exact_reserve", "topk_exact_get_stats", "topk_exact_reset_stats",
     "topk_exact_set_path_override", "topk_exact_last_error", "topk_stream_read_probe",
     "topk_exact_set_execution", "topk_exact_time_next_call", "topk_exact_set_proposal",
-    "topk_indexer_scores", "topk_indexer_topk", "topk_exact_sorted",
+    "topk_indexer_scores", "topk_indexer_topk", "topk_exact_sorted", "topk_exact_noalloc",
 )
 
 
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
         L.topk_exact.restype = ctypes.c_int
         L.topk_exact.argtypes = [vp, vp, i64, i64, i32, vp, i32, vp]
+        L.topk_exact_noalloc.restype = ctypes.c_int
+        L.topk_exact_noalloc.argtypes = [vp, vp, i64, i64, i32, vp, i32, vp]
         L.topk_exact_reserve.restype = ctypes.c_int
         L.topk_exact_reserve.argtypes = [i64, i64, i32]
         L.topk_exact_get_stats.restype = ctypes.c_int
@@ -142,6 +144,36 @@ def topk_exact(scores: torch.Tensor, row_len: torch.Tensor, K: int = 2048, senti
                                 sentinel, _stream_handle(scores.device, stream))
     _check(code, "topk_exact")
     return out
+
+
+def topk_exact_noalloc(scores: torch.Tensor, row_len: torch.Tensor, K: int = 2048, sentinel: int = -1,
+                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """topk_exact through the allocation-free entry point (the library's fixed scratch
+    array instead of its workspace). `out` should be given where the caller cannot
+    allocate; without it torch allocates the output here."""
+    M, N = _check_scores(scores, row_len)
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.int32, device=scores.device)
+    elif (out.dtype != torch.int32 or out.device != scores.device or tuple(out.shape) != (M, K)
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous int32 [M, K] tensor on the scores' device")
+    with torch.cuda.device(scores.device):
+        code = lib().topk_exact_noalloc(scores.data_ptr(), row_len.data_ptr(), M, N, K, out.data_ptr(),
+                                        sentinel, _stream_handle(scores.device, stream))
+    _check(code, "topk_exact_noalloc")
+    return out
+
+
+def _check_scores(scores, row_len):
+    if scores.dim() != 2 or scores.dtype != torch.float32 or not scores.is_cuda:
+        raise ValueError("scores must be a 2-D float32 GPU tensor")
+    M, N = scores.shape
+    if scores.stride(1) != 1 or (M > 1 and scores.stride(0) != N):
+        raise ValueError("scores must be row-major with row stride N_alloc")
+    if row_len.dtype != torch.int32 or row_len.device != scores.device or tuple(row_len.shape) != (M,) \
+            or not row_len.is_contiguous():
+        raise ValueError("row_len must be a contiguous int32 [M] tensor on the scores' device")
+    return M, N
 
 
 def topk_exact_sorted(scores: torch.Tensor, row_len: torch.Tensor, K: int = 2048, sentinel: int = -1,

@@ -86,7 +86,7 @@ constexpr uint32_t FL_RANK_MAX = 64;  // frontiers up to this size are resolved 
 constexpr uint32_t STRIDE = 128;      // sample stride s
 constexpr int UNROLL = 4;             // 128-bit loads per thread per batch
 constexpr uint32_t DIRECT_MAX_DEFAULT = 16384;
-constexpr uint32_t QMAX = 256;        // rows queued for cooperative recovery per call
+constexpr uint32_t QMAX = 256;        // rows queued for cooperative recovery per call (workspace)
 constexpr uint32_t REC_SEG = 16384;   // elements per recovery work item
 constexpr int64_t ROWSPLIT_MIN_N = 65536;  // auto row-split only for rows at least this wide
 constexpr uint32_t KEY_MAX = 0xFFFFFFFFu;
@@ -141,7 +141,8 @@ struct Params {
   uint32_t line_min;    // sampled rows with at least this many sample lines use line sampling
   uint32_t direct_max;  // auto mode: rows up to this length take the direct path
   int32_t mode;
-  RecSlot* rec;         // QMAX recovery slots
+  RecSlot* rec;         // qmax recovery slots
+  uint32_t qmax;        // rows a call can queue for cooperative recovery
   struct RowSplitState* rs;  // per-row state of the row-split kernels
   uint32_t ps;          // row-split: workgroups per row sampling
   uint32_t pp;          // row-split: workgroups per row passing
@@ -1036,7 +1037,7 @@ __device__ __forceinline__ void recover_row(const Params& p, uint32_t row, grow_
   __syncthreads();
   const uint32_t q = s.bcast;
   __syncthreads();
-  if (q < QMAX) {
+  if (q < p.qmax) {
     RecSlot* r = p.rec + q;
     if (t == 0) {
       r->row = row;
@@ -1295,7 +1296,7 @@ __shared__ RecHistSmem g_rh;  // the histogram kernel's LDS state
 
 __global__ __launch_bounds__(BLOCK) void recovery_hist_kernel(Params p) {
   const uint32_t t = threadIdx.x;
-  const uint32_t nq = min(p.ctl->qcount, QMAX);
+  const uint32_t nq = min(p.ctl->qcount, p.qmax);
   const uint32_t per_row = (p.N + REC_SEG - 1) / REC_SEG;
   const uint32_t items = nq * per_row;
   for (uint32_t item = blockIdx.x; item < items; item += gridDim.x) {
@@ -1360,7 +1361,7 @@ __global__ __launch_bounds__(BLOCK) void recovery_collect_kernel(Params p) {
   RecCollectSmem& s = g_rc;
   const uint32_t t = threadIdx.x;
   const uint32_t K = p.K;
-  const uint32_t nq = min(p.ctl->qcount, QMAX);
+  const uint32_t nq = min(p.ctl->qcount, p.qmax);
   const uint32_t per_row = (p.N + REC_SEG - 1) / REC_SEG;
   const uint32_t items = nq * per_row;
   for (uint32_t item = blockIdx.x; item < items; item += gridDim.x) {
@@ -1513,7 +1514,7 @@ void recovery_finish_kernel(Params p) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   const uint32_t K = p.K;
-  const uint32_t nq = min(p.ctl->qcount, QMAX);
+  const uint32_t nq = min(p.ctl->qcount, p.qmax);
   for (uint32_t q = blockIdx.x; q < nq; q += gridDim.x) {
     RecSlot* r = p.rec + q;
     if (r->row >= p.M || r->L > p.N) continue;  // (a slot of a call that failed)
@@ -1889,7 +1890,9 @@ struct DevState {
   int occ_rec = 0;      // resident recovery-collect workgroups per CU
   Control* ctl = nullptr;
   RecSlot* rec = nullptr;
-  RowSplitState* rs = nullptr;  // row-split state for RS_MAX_ROWS rows
+  RowSplitState* rs = nullptr;  // row-split state for rs_rows rows
+  uint32_t qmax = QMAX;         // recovery slots
+  int64_t rs_rows = RS_MAX_ROWS;
 };
 
 constexpr int MAX_DEVICES = 64;
@@ -1916,6 +1919,26 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(TOPK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Launch limits of a device: compute units and resident workgroups per CU of the
+// selector and recovery kernels (queries only; nothing is allocated).
+int launch_limits(int dev, DevState* st) {
+  int n_cu = 0, occ = 0, occ_rec = 0;
+  hipError_t e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(topk_rows_kernel<true>),
+                                                   BLOCK, 0);
+  if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  if (occ < 1) return fail(TOPK_ERR_HIP, "selector kernel cannot be resident (occupancy %d)", occ);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ_rec, reinterpret_cast<const void*>(recovery_finish_kernel),
+                                                   BLOCK, 0);
+  if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  if (occ_rec < 1) return fail(TOPK_ERR_HIP, "recovery kernel cannot be resident");
+  st->n_cu = n_cu;
+  st->occ = occ;
+  st->occ_rec = occ_rec;
+  return TOPK_OK;
+}
+
 // Returns the current device's state, creating it when allowed.
 int get_state(bool capturing, DevState** out) {
   int dev = 0;
@@ -1928,18 +1951,9 @@ int get_state(bool capturing, DevState** out) {
     if (capturing)
       return fail(TOPK_ERR_WORKSPACE,
                   "workspace not created on device %d; call topk_exact_reserve before capturing", dev);
-    int n_cu = 0, occ = 0;
-    e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &occ, reinterpret_cast<const void*>(topk_rows_kernel<true>), BLOCK, 0);
-    if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
-    if (occ < 1) return fail(TOPK_ERR_HIP, "selector kernel cannot be resident (occupancy %d)", occ);
-    int occ_rec = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &occ_rec, reinterpret_cast<const void*>(recovery_finish_kernel), BLOCK, 0);
-    if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
-    if (occ_rec < 1) return fail(TOPK_ERR_HIP, "recovery kernel cannot be resident");
+    DevState lim;
+    int rc = launch_limits(dev, &lim);
+    if (rc != TOPK_OK) return rc;
     // One allocation: the control block, the recovery slots, then the row-split state
     // (about 160 MB in all), so that no later call allocates.
     const size_t rec_off = (sizeof(Control) + 255) / 256 * 256;
@@ -1954,9 +1968,9 @@ int get_state(bool capturing, DevState** out) {
       (void)hipFree(ws);
       return hip_fail(e, "workspace initialisation");
     }
-    st.n_cu = n_cu;
-    st.occ = occ;
-    st.occ_rec = occ_rec;
+    st.n_cu = lim.n_cu;
+    st.occ = lim.occ;
+    st.occ_rec = lim.occ_rec;
     st.ctl = reinterpret_cast<Control*>(ws);
     st.rec = reinterpret_cast<RecSlot*>(ws + rec_off);
     st.rs = reinterpret_cast<RowSplitState*>(ws + rs_off);
@@ -2071,6 +2085,58 @@ __global__ __launch_bounds__(BLOCK) void sort_rows_kernel(const float* __restric
   }
 }
 
+// Scratch of the allocation-free entry point (topk_exact_noalloc): a control block, NA_QMAX
+// cooperative-recovery slots and row-split state for NA_RS_ROWS rows, laid out like the
+// workspace. It exists once per GPU from load to process end, zero at load. In host code
+// `scratch` names a host-side stand-in, never the device memory: the device address comes
+// from hipGetSymbolAddress once per device (noalloc_state) and only that address is used.
+constexpr uint32_t NA_QMAX = 64;
+constexpr int64_t NA_RS_ROWS = 64;
+constexpr size_t NA_REC_OFF = (sizeof(Control) + 255) / 256 * 256;
+constexpr size_t NA_RS_OFF = (NA_REC_OFF + sizeof(RecSlot) * NA_QMAX + 255) / 256 * 256;
+constexpr size_t NA_SCRATCH_BYTES = NA_RS_OFF + sizeof(RowSplitState) * NA_RS_ROWS;
+static_assert(NA_SCRATCH_BYTES <= (16u << 20), "the allocation-free scratch stays under 16 MiB");
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[NA_SCRATCH_BYTES];
+
+namespace {
+
+DevState g_noalloc[MAX_DEVICES];  // per device: limits and the device address of `scratch`
+
+// The allocation-free state of the current device: launch limits (queries only) and the
+// device address of `scratch`, looked up once per device with that device current.
+int noalloc_state(DevState** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(TOPK_ERR_HIP, "device index %d unsupported", dev);
+  std::lock_guard<std::mutex> lock(g_mu);
+  DevState& st = g_noalloc[dev];
+  if (!st.ready) {
+    DevState lim;
+    int rc = launch_limits(dev, &lim);
+    if (rc != TOPK_OK) return rc;
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) return fail(TOPK_ERR_HIP, "hipGetSymbolAddress(scratch) gave no address");
+    char* base = static_cast<char*>(ptr);
+    st.n_cu = lim.n_cu;
+    st.occ = lim.occ;
+    st.occ_rec = lim.occ_rec;
+    st.ctl = reinterpret_cast<Control*>(base);
+    st.rec = reinterpret_cast<RecSlot*>(base + NA_REC_OFF);
+    st.rs = reinterpret_cast<RowSplitState*>(base + NA_RS_OFF);
+    st.qmax = NA_QMAX;
+    st.rs_rows = NA_RS_ROWS;
+    st.ready = true;
+  }
+  *out = &st;
+  return TOPK_OK;
+}
+
 }  // namespace
 
 // The indexer score producer's host-side checks and launch (indexer_scores.hip).
@@ -2087,14 +2153,9 @@ __attribute__((visibility("hidden"))) int topk_record_error(int code, const char
 
 namespace {
 
-// Host-side checks of a selector call and the device state it runs with. Returns an error
-// before anything is enqueued; on success *st_out is null when there is nothing to
-// launch (M == 0).
-int selector_check(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc, int32_t K,
-                   int32_t* out_idx, int32_t sentinel, hipStream_t stream, bool* capturing_out,
-                   DevState** st_out) {
-  *st_out = nullptr;
-  *capturing_out = false;
+// Argument checks of a selector call (no device state is touched).
+int selector_args(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc, int32_t K,
+                  const int32_t* out_idx, int32_t sentinel) {
   if (M < 0) return fail(TOPK_ERR_BAD_SHAPE, "M = %lld is negative", (long long)M);
   if (N_alloc < 1 || N_alloc > INT32_MAX)
     return fail(TOPK_ERR_BAD_SHAPE, "N_alloc = %lld outside [1, INT32_MAX]", (long long)N_alloc);
@@ -2105,13 +2166,25 @@ int selector_check(const float* scores, const int32_t* row_len, int64_t M, int64
   if (sentinel >= 0 && (int64_t)sentinel < N_alloc)
     return fail(TOPK_ERR_BAD_SENTINEL, "sentinel %d lies inside [0, N_alloc = %lld)", sentinel,
                 (long long)N_alloc);
-  if (M == 0) return TOPK_OK;  // *st_out stays null: nothing to launch
+  if (M == 0) return TOPK_OK;
   if (!scores || !row_len || !out_idx) return fail(TOPK_ERR_NULL_POINTER, "null scores/row_len/out_idx");
   if ((reinterpret_cast<uintptr_t>(scores) & 3u) != 0)
     return fail(TOPK_ERR_BAD_ARG, "scores is not 4-byte aligned");
+  return TOPK_OK;
+}
 
+// Host-side checks of a selector call and the device state it runs with. Returns an error
+// before anything is enqueued; on success *st_out is null when there is nothing to
+// launch (M == 0).
+int selector_check(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc, int32_t K,
+                   int32_t* out_idx, int32_t sentinel, hipStream_t stream, bool* capturing_out,
+                   DevState** st_out) {
+  *st_out = nullptr;
+  *capturing_out = false;
+  int rc = selector_args(scores, row_len, M, N_alloc, K, out_idx, sentinel);
+  if (rc != TOPK_OK || M == 0) return rc;  // *st_out stays null for M == 0: nothing to launch
   bool capturing = false;
-  int rc = stream_capturing(stream, &capturing);
+  rc = stream_capturing(stream, &capturing);
   if (rc != TOPK_OK) return rc;
   DevState* st = nullptr;
   rc = get_state(capturing, &st);
@@ -2122,10 +2195,11 @@ int selector_check(const float* scores, const int32_t* row_len, int64_t M, int64
 }
 
 
-// Enqueues the selector and recovery kernels of a checked call.
+// Enqueues the selector and recovery kernels of a checked call on the state st (the
+// workspace, or the allocation-free entry point's scratch). `timing`: the call may take
+// the armed timing events (not under capture).
 int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc, int32_t K,
-                   int32_t* out_idx, int32_t sentinel, hipStream_t stream, bool capturing,
-                    DevState* st) {
+                    int32_t* out_idx, int32_t sentinel, hipStream_t stream, bool timing, DevState* st) {
   int rc = TOPK_OK;
   Params p;
   p.scores = scores;
@@ -2143,6 +2217,7 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
   p.direct_max = DIRECT_MAX_DEFAULT;
   p.mode = g_mode.load();
   p.rec = st->rec;
+  p.qmax = st->qmax;
   p.rs = nullptr;
   p.ps = 1;
   p.pp = 1;
@@ -2169,13 +2244,13 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
   // 1.507 -> 1.485 ms; 512 x 128K and 64K rows, where most lines are hot, lose with
   // it). A forced sampled path keeps it wherever it applies.
   p.line_min = (p.mode == TOPK_PATH_SAMPLED) ? 0u : p.T1;
-  const bool split = M <= (int64_t)RS_MAX_ROWS &&
+  const bool split = M <= st->rs_rows &&
                (ex == TOPK_EXEC_ROWSPLIT || p.mode == TOPK_PATH_ROWSPLIT ||
                 (ex == TOPK_EXEC_AUTO && N_alloc >= ROWSPLIT_MIN_N &&
                  (N_alloc >= 4 * ROWSPLIT_MIN_N ? 4 * M <= resident : 8 * M <= resident)));
   hipError_t e;
   hipEvent_t ev_start = nullptr, ev_stop = nullptr;
-  if (!capturing && g_time_start) {
+  if (timing && g_time_start) {
     ev_start = g_time_start;
     ev_stop = g_time_stop;
     g_time_start = g_time_stop = nullptr;
@@ -2222,8 +2297,8 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
     if (e != hipSuccess) rc = hip_fail(e, "hipEventRecord(stop)");
   }
   // Exact recovery of the rows the selector queued (they exit at once if none). At most
-  // min(M, QMAX) rows can be queued, so small calls launch correspondingly small grids.
-  const int64_t rec_rows = M < (int64_t)QMAX ? M : (int64_t)QMAX;
+  // min(M, qmax) rows can be queued, so small calls launch correspondingly small grids.
+  const int64_t rec_rows = M < (int64_t)st->qmax ? M : (int64_t)st->qmax;
   const int64_t rec_items = rec_rows * ((N_alloc + REC_SEG - 1) / REC_SEG);
   const unsigned rec_grid = (unsigned)(rec_items < (int64_t)st->n_cu * 4 ? rec_items : (int64_t)st->n_cu * 4);
   hipLaunchKernelGGL(recovery_hist_kernel, dim3(rec_grid), dim3(BLOCK), 0, stream, p);
@@ -2252,7 +2327,18 @@ int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N
   DevState* st = nullptr;
   const int rc = selector_check(scores, row_len, M, N_alloc, K, out_idx, sentinel, stream, &capturing, &st);
   if (rc != TOPK_OK || st == nullptr) return rc;
-  return selector_launch(scores, row_len, M, N_alloc, K, out_idx, sentinel, stream, capturing, st);
+  return selector_launch(scores, row_len, M, N_alloc, K, out_idx, sentinel, stream, !capturing, st);
+}
+
+int topk_exact_noalloc(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc, int32_t K,
+                       int32_t* out_idx, int32_t sentinel, hipStream_t stream) {
+  g_err[0] = '\0';
+  int rc = selector_args(scores, row_len, M, N_alloc, K, out_idx, sentinel);
+  if (rc != TOPK_OK || M == 0) return rc;
+  DevState* st = nullptr;
+  rc = noalloc_state(&st);
+  if (rc != TOPK_OK) return rc;
+  return selector_launch(scores, row_len, M, N_alloc, K, out_idx, sentinel, stream, false, st);
 }
 
 int topk_exact_sorted(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc, int32_t K,
@@ -2263,7 +2349,7 @@ int topk_exact_sorted(const float* scores, const int32_t* row_len, int64_t M, in
   int rc = selector_check(scores, row_len, M, N_alloc, K, out_idx, sentinel, stream, &capturing, &st);
   if (rc != TOPK_OK || st == nullptr) return rc;
   if ((reinterpret_cast<uintptr_t>(out_val) & 3u) != 0) return fail(TOPK_ERR_BAD_ARG, "out_val is not 4-byte aligned");
-  rc = selector_launch(scores, row_len, M, N_alloc, K, out_idx, sentinel, stream, capturing, st);
+  rc = selector_launch(scores, row_len, M, N_alloc, K, out_idx, sentinel, stream, !capturing, st);
   if (rc != TOPK_OK) return rc;
   // Entries per thread: the smallest power of two with EPT * BLOCK >= K (K <= 4096).
   const dim3 grid((unsigned)M), block(BLOCK);
@@ -2293,7 +2379,7 @@ int topk_indexer_topk(const uint8_t* q, const uint8_t* k, const float* w, const 
   if (rc != TOPK_OK || st == nullptr) return rc;
   rc = topk_indexer_launch(q, k, w, row_len, T, S, H, scores, stream);
   if (rc != TOPK_OK) return rc;
-  return selector_launch(scores, row_len, T, S, K, out_idx, sentinel, stream, capturing, st);
+  return selector_launch(scores, row_len, T, S, K, out_idx, sentinel, stream, !capturing, st);
 }
 
 int topk_exact_reserve(int64_t M_max, int64_t N_alloc_max, int32_t K) {

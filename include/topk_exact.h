@@ -119,6 +119,26 @@ enum {
 int topk_exact(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc,
                int32_t K, int32_t* out_idx, int32_t sentinel, hipStream_t stream);
 
+/* Allocation-free variant of topk_exact, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, contract, errors and stream behaviour as topk_exact; it never calls
+ * hipMalloc, hipFree or any allocating routine, needs no topk_exact_reserve, and may be
+ * the first call of a process even under capture. Instead of the workspace it uses a
+ * fixed scratch array in device memory of about 13.6 MB (under 16 MiB) per GPU, held
+ * from library load to process end: a control block, 64 cooperative-recovery slots and
+ * row-split state for 64 rows. The scratch does not grow with the call, so no call size
+ * is rejected for it: calls of at most 64 rows may be row-split (larger ones run unsplit,
+ * the same result), and rows needing exact recovery past the 64 queued per call are
+ * recovered in place by their own workgroup. The array starts zeroed and every call
+ * leaves its counters rewound for the next one. Every call on a GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (different streams, or threads, without
+ * ordering) race and must be serialized by the caller; it is separate from the
+ * workspace topk_exact uses, so the two entry points do not race with each other.
+ * Its row counters are not those topk_exact_get_stats reads, and it ignores the timing
+ * hook. */
+int topk_exact_noalloc(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc,
+                       int32_t K, int32_t* out_idx, int32_t sentinel, hipStream_t stream);
+
 /* Sorted, value-returning variant (an option beyond the pages' unordered contract): the
  * same selection as topk_exact, then each row's entries ordered by score descending
  * (IEEE totalOrder), ties by index ascending. For L > K: the K selected indices in that

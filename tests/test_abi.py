@@ -49,6 +49,12 @@ def test_argument_validation_without_gpu():
     assert L.topk_exact(None, None, 0, 10, 4, None, -1, None) == B.TOPK_OK
     # A sentinel at or past N_alloc is allowed.
     assert L.topk_exact(fake, fake, 0, 10, 4, fake, 10, None) == B.TOPK_OK
+    # The allocation-free entry point checks its arguments the same way, before any device work.
+    assert L.topk_exact_noalloc(fake, fake, -1, 10, 4, fake, -1, None) == B.TOPK_ERR_BAD_SHAPE
+    assert L.topk_exact_noalloc(fake, fake, 2, 10, B.TOPK_K_MAX + 1, fake, -1, None) == B.TOPK_ERR_BAD_K
+    assert L.topk_exact_noalloc(fake, fake, 2, 10, 4, fake, 5, None) == B.TOPK_ERR_BAD_SENTINEL
+    assert L.topk_exact_noalloc(fake, None, 2, 10, 4, fake, -1, None) == B.TOPK_ERR_NULL_POINTER
+    assert L.topk_exact_noalloc(None, None, 0, 10, 4, None, -1, None) == B.TOPK_OK
     assert L.topk_exact_set_path_override(99) == B.TOPK_ERR_BAD_ARG
     assert L.topk_exact_set_path_override(-1) == B.TOPK_ERR_BAD_ARG
     assert L.topk_exact_get_stats(None, 4, None) == B.TOPK_ERR_NULL_POINTER

@@ -1,0 +1,156 @@
+"""The allocation-free entry point (topk_exact_noalloc) against topk_exact.
+
+Both are called through the C ABI on the same seeded inputs, two calls in a row with
+the second smaller, and compared to the same bar as every selector output: each passes
+the exact set contract against the CPU oracle (page "几何平均快 1.55 倍，但短行采样会输：
+腾讯怎么测精确 Top-K", section "什么叫精确，时间怎么量"), and per row their selected score
+multisets are equal bit for bit (short rows: the same index set and sentinel layout).
+The inputs exercise every piece of the scratch: row-split state (few long rows), the
+cooperative-recovery queue (rows built to underfill tau1) and its overflow past the 64
+queued rows (forced recovery of more rows than that).
+"""
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import exact_top_selection_stride_amd as tk
+from exact_top_selection_stride_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+K = 2048
+DEV = "cuda"
+
+
+def _abi(name, s, l, out, K=K, sentinel=-1):
+    code = getattr(tk.lib(), name)(s.data_ptr(), l.data_ptr(), s.shape[0], s.shape[1], K, out.data_ptr(),
+                                   sentinel, torch.cuda.current_stream().cuda_stream)
+    assert code == 0, f"{name}: status {code}: {tk.last_error()}"
+
+
+def _underfill_row(L, n_mid, seed):
+    """A row whose stride-128 sample puts tau1 on values that only 1000 + 28 entries reach
+    (C(tau1) < K): exact recovery."""
+    rng = np.random.default_rng(seed)
+    x = rng.uniform(0.0, 40.0, size=L).astype(np.float32)
+    sp = np.arange(0, L, 128)
+    x[sp] = 0.0
+    pick = rng.permutation(len(sp))
+    x[sp[pick[:24]]] = 100.0
+    x[sp[pick[24:28]]] = 50.0
+    rest = np.setdiff1d(np.arange(L), sp)
+    x[rng.choice(rest, size=n_mid, replace=False)] = 75.0
+    return x
+
+
+def _compare(s, l, a, b, label):
+    """a, b: outputs of the two entry points. Both pass the contract; same multisets."""
+    sh = s.cpu().numpy()
+    lh = l.cpu().numpy().astype(np.int32)
+    ref = oracle.topk(sh, lh, K, -1)
+    for name, o in (("noalloc", a), ("topk_exact", b)):
+        n_bad, status = oracle.check_contract(sh, lh, K, -1, o.cpu().numpy(), ref)
+        assert n_bad == 0, f"{label} {name}: {n_bad} rows violate the contract: " \
+                           f"{[(int(r), oracle.CHK_NAMES[int(status[r])]) for r in np.nonzero(status)[0][:5]]}"
+    ah, bh = a.cpu().numpy(), b.cpu().numpy()
+    keys = sh.view(np.uint32)
+    for r in range(sh.shape[0]):
+        L = min(max(int(lh[r]), 0), sh.shape[1])
+        if L > K:
+            ka = np.sort(keys[r, ah[r]])
+            kb = np.sort(keys[r, bh[r]])
+            assert np.array_equal(ka, kb), f"{label}: row {r} selected scores differ"
+        else:
+            assert np.array_equal(np.sort(ah[r, :L]), np.sort(bh[r, :L])) and (ah[r, L:] == -1).all(), \
+                f"{label}: short row {r} differs"
+
+
+def _first_input():
+    # 40 rows of the 128K window (auto dispatch row-splits them: few rows), 3 of them built
+    # to underfill tau1 (cooperative recovery), and 2 short rows.
+    s, l = W.make_window(W.get("c1"), DEV, row_start=100, n_rows=40)
+    L = s.shape[1]
+    for i, r in enumerate((3, 17, 30)):
+        s[r] = torch.from_numpy(_underfill_row(L, 1000, 50 + i)).to(DEV)
+        l[r] = L
+    l[5] = 1500
+    l[6] = 0
+    return s.contiguous(), l.contiguous()
+
+
+def test_noalloc_matches_topk_exact_two_calls():
+    s1, l1 = _first_input()
+    s2, l2 = W.make_window(W.get("c3b"), DEV, row_start=8000, n_rows=6)  # smaller: 6 rows of 1M
+    for i, (s, l) in enumerate(((s1, l1), (s2, l2))):
+        a = torch.full((s.shape[0], K), -7, dtype=torch.int32, device=DEV)
+        b = torch.full((s.shape[0], K), -7, dtype=torch.int32, device=DEV)
+        _abi("topk_exact_noalloc", s, l, a)
+        tk.reset_stats()
+        _abi("topk_exact", s, l, b)
+        torch.cuda.synchronize()
+        st = tk.get_stats()
+        assert st["rowsplit"] > 0  # the reference call took the row-split path too
+        if i == 0:
+            assert st["queued"] >= 3
+        _compare(s, l, a, b, f"call {i + 1} ({s.shape[0]} x {s.shape[1]})")
+
+
+def test_noalloc_recovery_queue_overflow_two_calls():
+    # Forced exact recovery of 100 rows, then of 70: more than the 64 rows the scratch
+    # queues, so the rest are recovered in place; both calls against topk_exact.
+    N = 20000
+    for M in (100, 70):
+        s, l = W.make_rows(M, N, [N - (i % 5) for i in range(M)], tail_p=0.01, seed=M, device=DEV)
+        a = torch.empty((M, K), dtype=torch.int32, device=DEV)
+        b = torch.empty((M, K), dtype=torch.int32, device=DEV)
+        with tk.path_override(tk.PATH_RECOVERY):
+            _abi("topk_exact_noalloc", s, l, a)
+            _abi("topk_exact", s, l, b)
+        torch.cuda.synchronize()
+        _compare(s, l, a, b, f"forced recovery M={M}")
+
+
+_FRESH = r"""
+import json, sys
+sys.path.insert(0, sys.argv[1])
+import numpy as np, torch
+import exact_top_selection_stride_amd as tk
+from exact_top_selection_stride_amd import workloads as W
+import oracle
+# The first library call of this process is the allocation-free one, under capture.
+s, l = W.make_window(W.get("c1"), "cuda", row_start=8000, n_rows=12)
+out = torch.full((12, 2048), -7, dtype=torch.int32, device="cuda")
+stream = torch.cuda.Stream()
+stream.wait_stream(torch.cuda.current_stream())
+torch.cuda.synchronize()
+with torch.cuda.stream(stream):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        code = tk.lib().topk_exact_noalloc(s.data_ptr(), l.data_ptr(), 12, s.shape[1], 2048, out.data_ptr(),
+                                           -1, stream.cuda_stream)
+res = {"code": code, "violations": []}
+sh, lh = s.cpu().numpy(), l.cpu().numpy().astype(np.int32)
+ref = oracle.topk(sh, lh, 2048, -1)
+for rep in range(3):
+    out.fill_(-7)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    res["violations"].append(int(oracle.check_contract(sh, lh, 2048, -1, out.cpu().numpy(), ref)[0]))
+print(json.dumps(res))
+"""
+
+
+def test_noalloc_first_call_of_a_process_under_capture():
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _FRESH, root], capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    res = json.loads(r.stdout.strip().splitlines()[-1])
+    assert res["code"] == 0
+    assert res["violations"] == [0, 0, 0]
