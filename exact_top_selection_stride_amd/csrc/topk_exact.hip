@@ -1112,6 +1112,22 @@ __device__ __forceinline__ uint32_t sample_rank(uint32_t target, uint32_t n_s, u
   return (uint32_t)r;
 }
 
+// Bitmap of the hot sampled lines (line maximum lmax[j] >= tau1 key) in s.fl_idx, which
+// the frontier uses only after the pass: bit j of the list, j < n_s. Each wave writes the
+// two words of its 64 lines per step through one base address and constant offsets, so
+// no per-step address stays live across the row loop.
+__device__ __forceinline__ void write_hot_bitmap(const uint32_t* lmax, uint32_t n_s, uint32_t t1key) {
+  const uint32_t t = threadIdx.x;
+  const uint32_t* lm = lmax + t;
+  uint32_t* words = &g_s.fl_idx[2u * (t / WAVE) + (lane_id() & 1u)];
+  const uint32_t nj = n_s - t;  // lines j = t + m BLOCK below n_s: m BLOCK < nj
+#pragma unroll
+  for (int m = 0; m < LM_PER_THREAD; ++m) {
+    const uint64_t hb = __ballot((uint32_t)m * BLOCK < nj && n_s > t && lm[m * BLOCK] >= t1key);
+    if (lane_id() < 2) words[m * (BLOCK / 32)] = (lane_id() & 1u) ? (uint32_t)(hb >> 32) : (uint32_t)hb;
+  }
+}
+
 template <bool STREAM_SAMPLE>
 __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_t x, uint32_t L, gout_t out) {
   Smem& s = g_s;
@@ -1163,19 +1179,7 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
   // Skipping sampled lines needs a value that is never admitted, which exists
   // unless tau1 is the lowest possible key.
   const bool skip = by_lines && t1key != 0u;
-  if (skip) {
-    // Bitmap of the hot sampled lines (maximum >= tau1) in s.fl_idx, which the
-    // frontier uses only after the pass.
-#pragma unroll
-    for (int m = 0; m < LM_PER_THREAD; ++m) {
-      const uint32_t j = t + (uint32_t)m * BLOCK;
-      const uint64_t hb = __ballot(j < n_s && s.buf[CAP + j] >= t1key);
-      if (lane_id() == 0) {
-        s.fl_idx[j >> 5] = (uint32_t)hb;
-        s.fl_idx[(j >> 5) + 1] = (uint32_t)(hb >> 32);
-      }
-    }
-  }
+  if (skip) write_hot_bitmap(&s.buf[CAP], n_s, t1key);
   reset_row_state();  // its barrier also ends every read of the line maxima in LDS
   if (skip) {
     if (pos) fused_pass<true, true>(x, L, n_s, c);
