@@ -39,8 +39,9 @@ EXEC_ROWSPLIT = 3
 STAT_NAMES = (
     "rows", "sentinel", "direct", "sampled", "tau0", "tau1", "recover_under", "recover_over",
     "rowsplit", "forced_recovery", "long_exact", "frontier_wide", "queued", "persistent", "row_per_wg",
+    "recover_inplace", "inplace_certified", "inplace_full",
 )
-STAT_COUNT = 16
+STAT_COUNT = 24
 
 EXPORTED = (
     "topk_exact", "topk_exact_reserve", "topk_exact_get_stats", "topk_exact_reset_stats",

@@ -88,6 +88,8 @@ constexpr int UNROLL = 4;             // 128-bit loads per thread per batch
 constexpr uint32_t DIRECT_MAX_DEFAULT = 16384;
 constexpr uint32_t QMAX = 256;        // rows queued for cooperative recovery per call (workspace)
 constexpr uint32_t REC_SEG = 16384;   // elements per recovery work item
+constexpr uint32_t INPLACE_MAX = 65536;        // rows up to this length are recovered in place,
+constexpr uint32_t INPLACE_MAX_SPLIT = 262144; // ... and up to this one in row-split calls
 constexpr int64_t ROWSPLIT_MIN_N = 65536;  // auto row-split only for rows at least this wide
 constexpr uint32_t KEY_MAX = 0xFFFFFFFFu;
 
@@ -137,6 +139,8 @@ struct Params {
   int32_t sentinel;
   uint32_t T0;          // primary candidate target, ceil(1.5 K) by default
   uint32_t T1;          // secondary candidate target, ceil(1.75 K) by default
+  uint32_t T2;          // threshold for in-place recovery of underfilled rows (a deeper target)
+  uint32_t inplace_max; // rows up to this length needing exact recovery are recovered in place
   uint32_t stride;      // sample stride s, 128 by default
   uint32_t line_min;    // sampled rows with at least this many sample lines use line sampling
   uint32_t direct_max;  // auto mode: rows up to this length take the direct path
@@ -1025,6 +1029,58 @@ __device__ __forceinline__ void refine_commit(uint32_t n, uint32_t K, const Pass
   refine_list<false>(n, K, c.t1key, c.sh, out, ctl);
 }
 
+__device__ __forceinline__ PassCtx pass_ctx(uint32_t t1key, uint32_t t0key, uint32_t smax) {
+  PassCtx c;
+  c.t1key = t1key;
+  c.t0key = t0key;
+  c.sh = shift_for(smax - t1key);
+  c.thr = t1key >= 0x80000000u ? (t1key ^ 0x80000000u) : ~t1key;
+  return c;
+}
+
+// Exact recovery of a row by its own workgroup: one more pass over the row admitting
+// keys >= thr (a threshold below the K-th key: the deeper sample rank for an
+// underfilled row, the boundary bin of the pass histogram for an overflowing one);
+// when its count certifies (K <= C(thr) <= CAP) the admitted list is refined as usual,
+// otherwise (or with thr = 0) the exact full-row select over [lo, hi] runs. Nothing has
+// been written to the row's output yet. Out of line: the path is rare, and inlined its
+// second pass would raise the register pressure of every kernel that holds it.
+// Takes scalars only: a reference to the launch parameters would force them into
+// scratch memory in every caller.
+__device__ __attribute__((noinline)) void recover_in_place(grow_t x, uint32_t L, uint32_t K, uint32_t thr,
+                                                           uint32_t smax, uint32_t lo, uint32_t hi, gout_t out,
+                                                           Control* ctl) {
+  Smem& s = g_s;
+  if (threadIdx.x == 0) stat_add(ctl, TOPK_STAT_RECOVER_INPLACE);
+  if (thr != 0u) {
+    reset_row_state();
+    const PassCtx c = pass_ctx(thr, thr, smax > thr ? smax : thr);
+    if (thr >= 0x80000000u) fused_pass<true, false>(x, L, 0u, c);
+    else fused_pass<false, false>(x, L, 0u, c);
+    __syncthreads();
+    const uint32_t n = s.cnt;
+    if (n >= K && n <= (uint32_t)CAP) {
+      if (threadIdx.x == 0) stat_add(ctl, TOPK_STAT_INPLACE_CERTIFIED);
+      refine_commit(n, K, c, out, ctl);
+      return;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) stat_add(ctl, TOPK_STAT_INPLACE_FULL);
+  exact_full_row(x, L, K, lo, hi, out, ctl);
+}
+
+// For a row whose admitted keys overflowed the buffer (C(tau1) > CAP >= K): the pass
+// histogram s.hist over (key - t1key) >> sh counted every admitted key, so the bin
+// holding rank K is known; returns its lowest key, with n_ge = the keys at or above it.
+__device__ __forceinline__ uint32_t overflow_threshold(uint32_t K, uint32_t t1key, uint32_t sh, uint32_t& n_ge) {
+  block_find_bin(K);
+  const uint32_t b = g_s.sel_bin;
+  n_ge = g_s.sel_above + g_s.hist[b];
+  __syncthreads();
+  return t1key + (b << sh);
+}
+
 // Hands a row that needs exact full-row recovery to the cooperative recovery
 // kernels (which run after this kernel and spread the row over the whole GPU), or
 // recovers it here when the queue is full. Nothing has been written to the row's
@@ -1050,17 +1106,21 @@ __device__ __forceinline__ void recover_row(const Params& p, uint32_t row, grow_
     }
     for (uint32_t i = t; i < (uint32_t)NB; i += BLOCK) r->hist[i] = 0;
   } else {
+    if (t == 0) {
+      stat_add(p.ctl, TOPK_STAT_RECOVER_INPLACE);
+      stat_add(p.ctl, TOPK_STAT_INPLACE_FULL);
+    }
     exact_full_row(x, L, p.K, lo, hi, out, p.ctl);
   }
 }
 
-// tau1 and tau0: the r1-th and r0-th largest (r0 <= r1) of the n_s sample keys in
-// s.buf[0, n_s), all inside [mn, mx]. One radix round finds the bin holding rank r1;
-// when the keys in that bin and above fit the frontier buffer (the usual case, r1
-// is a few dozen), both ranks are read off by counting inside that short list.
-// Otherwise the general narrowing selection runs.
-__device__ __forceinline__ void select_taus(uint32_t n_s, uint32_t r0, uint32_t r1, uint32_t mn, uint32_t mx,
-                            uint32_t& t0key, uint32_t& t1key) {
+// tau1, tau0 and tau2: the r1-th, r0-th and r2-th largest (r0 <= r1 <= r2) of the n_s
+// sample keys in s.buf[0, n_s), all inside [mn, mx]. One radix round finds the bin
+// holding rank r2; when the keys in that bin and above fit the frontier buffer (the
+// usual case, r2 is a few dozen), the three ranks are read off by counting inside that
+// short list. Otherwise the general narrowing selection runs.
+__device__ __forceinline__ void select_taus(uint32_t n_s, uint32_t r0, uint32_t r1, uint32_t r2, uint32_t mn,
+                                            uint32_t mx, uint32_t& t0key, uint32_t& t1key, uint32_t& t2key) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   const uint32_t sh = shift_for(mx - mn);
@@ -1069,7 +1129,7 @@ __device__ __forceinline__ void select_taus(uint32_t n_s, uint32_t r0, uint32_t 
   __syncthreads();
   for (uint32_t i = t; i < n_s; i += BLOCK) atomicAdd(&s.hist[(s.buf[i] - mn) >> sh], 1u);
   __syncthreads();
-  block_find_bin(r1);
+  block_find_bin(r2);
   const uint32_t b = s.sel_bin;
   const uint32_t m = s.sel_above + s.hist[b];  // sample keys in bin b and above
   const uint32_t blo = mn + (b << sh);
@@ -1090,15 +1150,20 @@ __device__ __forceinline__ void select_taus(uint32_t n_s, uint32_t r0, uint32_t 
     const uint32_t rk = rank_in_list(s.fl_key, m);
     if (rk == r1 - 1) s.sel_above = s.fl_key[t];
     if (rk == r0 - 1) s.sel_bin = s.fl_key[t];
+    if (rk == r2 - 1) s.bcast = s.fl_key[t];
     __syncthreads();
     t1key = s.sel_above;
     t0key = s.sel_bin;
+    t2key = s.bcast;
     __syncthreads();
   } else {
     uint32_t unused;
     select_rank([&](auto&& f) {
       for (uint32_t i = threadIdx.x; i < n_s; i += BLOCK) f(g_s.buf[i]);
-    }, r1, mn, mx, t1key, unused);
+    }, r2, mn, mx, t2key, unused);
+    select_rank([&](auto&& f) {
+      for (uint32_t i = threadIdx.x; i < n_s; i += BLOCK) f(g_s.buf[i]);
+    }, r1, t2key, mx, t1key, unused);
     select_rank([&](auto&& f) {
       for (uint32_t i = threadIdx.x; i < n_s; i += BLOCK) f(g_s.buf[i]);
     }, r0, t1key, mx, t0key, unused);
@@ -1167,8 +1232,9 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
   const uint32_t smin = s.mn, smax = s.mx;
   const uint32_t r1 = sample_rank(p.T1, n_s, L);
   const uint32_t r0 = sample_rank(p.T0, n_s, L);
-  uint32_t t1key, t0key;
-  select_taus(n_s, r0, r1, smin, smax, t0key, t1key);
+  const uint32_t r2 = sample_rank(p.T2, n_s, L);
+  uint32_t t1key, t0key, t2key;
+  select_taus(n_s, r0, r1, r2, smin, smax, t0key, t1key, t2key);
 
   PassCtx c;
   c.t1key = t1key;
@@ -1192,13 +1258,23 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
   __syncthreads();
   const uint32_t c1 = s.cnt, c0 = s.cnt0;
   if (c1 > (uint32_t)CAP) {
-    // Too many admitted to hold: the K-th key is >= tau1, recover exactly.
+    // Too many admitted to hold: the K-th key is >= tau1, recover exactly. A short row
+    // is recovered in place from the boundary bin of the pass histogram, a long one by
+    // the cooperative recovery kernels.
     if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_OVER);
-    recover_row(p, row, x, L, t1key, smax, out);
+    if (L <= p.inplace_max) {
+      uint32_t n_ge;
+      const uint32_t thr = overflow_threshold(p.K, t1key, c.sh, n_ge);
+      recover_in_place(x, L, p.K, n_ge <= (uint32_t)CAP ? thr : 0u, smax, t1key, smax, out, p.ctl);
+    } else {
+      recover_row(p, row, x, L, t1key, smax, out);
+    }
   } else if (c1 < p.K) {
-    // Even the nested threshold underfills: the K-th key is < tau1.
+    // Even the nested threshold underfills: the K-th key is < tau1. A short row is
+    // recovered in place from the deeper sample rank tau2, a long one cooperatively.
     if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_UNDER);
-    recover_row(p, row, x, L, smin, t1key, out);
+    if (L <= p.inplace_max) recover_in_place(x, L, p.K, t2key, smax, smin, t1key, out, p.ctl);
+    else recover_row(p, row, x, L, smin, t1key, out);
   } else {
     if (t == 0) stat_add(p.ctl, c0 >= p.K ? TOPK_STAT_TAU0 : TOPK_STAT_TAU1);
     refine_commit(c1, p.K, c, out, p.ctl);
@@ -1612,8 +1688,8 @@ struct RowSplitState {
   uint32_t mx;          // max sample key (atomicMax)
   uint32_t c1;          // C(tau1): all admitted keys, even past CAP
   uint32_t c0;          // C(tau0)
-  uint32_t t1key, t0key;
-  uint32_t pad[25];
+  uint32_t t1key, t0key, t2key;
+  uint32_t pad[24];
   uint32_t hist[NB];
   uint32_t cand_idx[CAP];
   uint32_t cand_key[CAP];
@@ -1698,22 +1774,16 @@ void split_select_kernel(Params p) {
     if (i < n_s) s.buf[i] = v[m];
   }
   __syncthreads();
-  uint32_t t0key, t1key;
-  select_taus(n_s, sample_rank(p.T0, n_s, L), sample_rank(p.T1, n_s, L), ~rs->mn_inv, rs->mx, t0key, t1key);
+  uint32_t t0key, t1key, t2key;
+  select_taus(n_s, sample_rank(p.T0, n_s, L), sample_rank(p.T1, n_s, L), sample_rank(p.T2, n_s, L), ~rs->mn_inv,
+              rs->mx, t0key, t1key, t2key);
   if (t == 0) {
     rs->t1key = t1key;
     rs->t0key = t0key;
+    rs->t2key = t2key;
   }
 }
 
-__device__ __forceinline__ PassCtx pass_ctx(uint32_t t1key, uint32_t t0key, uint32_t smax) {
-  PassCtx c;
-  c.t1key = t1key;
-  c.t0key = t0key;
-  c.sh = shift_for(smax - t1key);
-  c.thr = t1key >= 0x80000000u ? (t1key ^ 0x80000000u) : ~t1key;
-  return c;
-}
 
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4)))
 void split_pass_kernel(Params p) {
@@ -1790,14 +1860,27 @@ void split_finish_kernel(Params p) {
     grow_t x = (grow_t)(p.scores) + (size_t)row * p.N;
     gout_t out = (gout_t)(p.out) + (size_t)row * p.K;
     const uint32_t c1 = rs->c1, c0 = rs->c0;
-    const uint32_t t1key = rs->t1key, t0key = rs->t0key;
+    const uint32_t t1key = rs->t1key, t0key = rs->t0key, t2key = rs->t2key;
     const uint32_t smin = ~rs->mn_inv, smax = rs->mx;
     if (c1 > (uint32_t)CAP) {
       if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_OVER);
-      recover_row(p, row, x, L, t1key, smax, out);
+      if (L <= p.inplace_max) {
+        // The merged pass histogram (every part's admitted keys) locates the boundary bin.
+        uint32_t thr = 0u, n_ge = 0u;
+        if (t1key != 0u) {
+          reset_row_state();
+          for (uint32_t b = t; b < (uint32_t)NB; b += BLOCK) s.hist[b] = rs->hist[b];
+          __syncthreads();
+          thr = overflow_threshold(p.K, t1key, shift_for(smax - t1key), n_ge);
+        }
+        recover_in_place(x, L, p.K, n_ge <= (uint32_t)CAP ? thr : 0u, smax, t1key, smax, out, p.ctl);
+      } else {
+        recover_row(p, row, x, L, t1key, smax, out);
+      }
     } else if (c1 < p.K) {
       if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_UNDER);
-      recover_row(p, row, x, L, smin, t1key, out);
+      if (L <= p.inplace_max) recover_in_place(x, L, p.K, t2key, smax, smin, t1key, out, p.ctl);
+      else recover_row(p, row, x, L, smin, t1key, out);
     } else {
       if (t == 0) stat_add(p.ctl, c0 >= p.K ? TOPK_STAT_TAU0 : TOPK_STAT_TAU1);
       // The merged histogram and candidates move to LDS with all loads issued first.
@@ -2217,6 +2300,21 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
   // Targets ceil(rho * K) with rho in thousandths: 1.5 K and 1.75 K by default.
   p.T0 = (uint32_t)(((int64_t)g_rho0.load() * K + 999) / 1000);
   p.T1 = (uint32_t)(((int64_t)g_rho1.load() * K + 999) / 1000);
+  // In-place recovery threshold of an underfilled row: a deeper sample rank, about 2.9 K
+  // admitted keys at K = 2048 (halfway from T1 to the buffer, at most 3 K). After an
+  // underfill at tau1 the row holds about C(tau1) + (r2 - r1) L / n_s keys above it.
+  {
+    const uint32_t t2 = (p.T1 + (uint32_t)CAP) / 2u < 3u * (uint32_t)K ? (p.T1 + (uint32_t)CAP) / 2u
+                                                                       : 3u * (uint32_t)K;
+    p.T2 = t2 > p.T1 ? t2 : p.T1;
+  }
+  // Rows that need exact recovery and are short are recovered by their own workgroup
+  // with one more pass (at most 256 KB; 1 MB in row-split calls, which have few rows);
+  // longer ones by the cooperative recovery kernels, which then run after the selector.
+  // Measured on MI355X (graph replays): 8192 x 64K bf16 rows 0.587 -> 0.558 ms per call
+  // and 64 split rows of 128K 49 -> 45 us in place, while 512 x 128K rows in lockstep lose
+  // 3-5 us (the recovering workgroup streams its row alone at the end of the call). Forced
+  // recovery always takes the cooperative kernels.
   p.stride = (uint32_t)g_stride.load();
   p.direct_max = DIRECT_MAX_DEFAULT;
   p.mode = g_mode.load();
@@ -2252,6 +2350,7 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
                (ex == TOPK_EXEC_ROWSPLIT || p.mode == TOPK_PATH_ROWSPLIT ||
                 (ex == TOPK_EXEC_AUTO && N_alloc >= ROWSPLIT_MIN_N &&
                  (N_alloc >= 4 * ROWSPLIT_MIN_N ? 4 * M <= resident : 8 * M <= resident)));
+  p.inplace_max = g_mode.load() == TOPK_PATH_RECOVERY ? 0u : (split ? INPLACE_MAX_SPLIT : INPLACE_MAX);
   hipError_t e;
   hipEvent_t ev_start = nullptr, ev_stop = nullptr;
   if (timing && g_time_start) {
@@ -2300,8 +2399,11 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
     e = hipEventRecord(ev_stop, stream);
     if (e != hipSuccess) rc = hip_fail(e, "hipEventRecord(stop)");
   }
-  // Exact recovery of the rows the selector queued (they exit at once if none). At most
-  // min(M, qmax) rows can be queued, so small calls launch correspondingly small grids.
+  // Exact recovery of the rows the selector queued (they exit at once if none). Only rows
+  // longer than p.inplace_max are queued: with no such row the recovery kernels are not
+  // launched at all. At most min(M, qmax) rows can be queued, so small calls launch
+  // correspondingly small grids.
+  if ((int64_t)p.inplace_max >= N_alloc) return rc;
   const int64_t rec_rows = M < (int64_t)st->qmax ? M : (int64_t)st->qmax;
   const int64_t rec_items = rec_rows * ((N_alloc + REC_SEG - 1) / REC_SEG);
   const unsigned rec_grid = (unsigned)(rec_items < (int64_t)st->n_cu * 4 ? rec_items : (int64_t)st->n_cu * 4);

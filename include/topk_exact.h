@@ -91,7 +91,11 @@ enum {
   TOPK_STAT_QUEUED = 12,         /* recovery rows handed to the cooperative recovery kernels */
   TOPK_STAT_PERSISTENT = 13,     /* rows taken from the device ticket by the persistent grid */
   TOPK_STAT_ROW_PER_WG = 14,     /* rows given a workgroup of their own */
-  TOPK_STAT_COUNT = 16
+  TOPK_STAT_RECOVER_INPLACE = 15, /* recovery rows recovered by their own workgroup (rows up to
+                                     262144 long, or past the cooperative queue's capacity) */
+  TOPK_STAT_INPLACE_CERTIFIED = 16, /* of those: one more pass at a deeper threshold certified */
+  TOPK_STAT_INPLACE_FULL = 17,   /* of those: the exact full-row select over the row ran */
+  TOPK_STAT_COUNT = 24
 };
 
 /* Selects the top-K indices of every row: the operation and contract of [Cx] section

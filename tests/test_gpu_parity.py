@@ -207,7 +207,64 @@ def test_recovery_rows_mixed_with_normal_rows():
     l = torch.cat([l1.clamp(max=L), torch.full((3,), L, dtype=torch.int32, device=DEV)]).contiguous()
     out, st = _run(s, l)
     _check(s, l, out, label="mixed recovery")
-    assert st["queued"] >= 3 and st["recover_under"] >= 3
+    # Rows of 128K are recovered in place by their own workgroup; nothing is queued.
+    assert st["recover_under"] >= 3 and st["recover_inplace"] >= 3 and st["queued"] == 0
+
+
+def _controlled_row(L, kind, seed):
+    """Rows of L = 65536 (512 samples; sample ranks r0 = 24, r1 = 28, r2 = 46 at the
+    method's targets, as for any L that is a multiple of 128) that take each branch of
+    in-place exact recovery:
+      under_certified  tau1 underfills (1028 keys >= 50) but the deeper tau2 = 40 holds
+                       4046 keys: one more pass certifies;
+      under_full       tau1 underfills and every key below it is >= tau2 = 0: the second
+                       pass overflows, the exact full-row select runs;
+      over_certified   9028 keys >= tau1 = 50 (overflow), spread over distinct values: the
+                       boundary bin of the pass histogram bounds a second pass;
+      over_full        9000 copies of one value above tau1: the boundary bin alone exceeds
+                       the buffer, the exact full-row select runs."""
+    rng = np.random.default_rng(seed)
+    sp = _sample_positions(L)
+    rest = np.setdiff1d(np.arange(L), sp)
+    pick = rng.permutation(len(sp))
+    x = rng.uniform(0.0, 30.0, size=L).astype(np.float32)
+    x[sp] = 0.0
+    x[sp[pick[:24]]] = 100.0
+    x[sp[pick[24:28]]] = 50.0
+    if kind == "under_certified":
+        x[sp[pick[28:46]]] = 40.0
+        chosen = rng.choice(rest, size=4000, replace=False)
+        x[chosen[:1000]] = 75.0
+        x[chosen[1000:]] = 45.0
+    elif kind == "under_full":
+        x = rng.uniform(0.0, 40.0, size=L).astype(np.float32)
+        x[sp] = 0.0
+        x[sp[pick[:24]]] = 100.0
+        x[sp[pick[24:28]]] = 50.0
+        x[rng.choice(rest, size=1000, replace=False)] = 75.0
+    elif kind == "over_certified":
+        x[rng.choice(rest, size=9000, replace=False)] = rng.uniform(55.0, 95.0, size=9000).astype(np.float32)
+    else:
+        x[rng.choice(rest, size=9000, replace=False)] = 60.0
+    return x
+
+
+@pytest.mark.parametrize("execution", [tk.EXEC_ROW_PER_WG, tk.EXEC_PERSISTENT, tk.EXEC_ROWSPLIT])
+def test_inplace_recovery_branches(execution):
+    # Each in-place recovery branch on rows built from the known sample positions, in
+    # every execution mode (row-split recovers in its finish kernel); the counters prove
+    # which branch ran, the oracle that the result is exact.
+    L = 65536
+    kinds = ["under_certified", "under_full", "over_certified", "over_full"]
+    rows = np.stack([_controlled_row(L, k, 300 + i) for i, k in enumerate(kinds)])
+    s = torch.from_numpy(rows).to(DEV)
+    l = torch.full((4,), L, dtype=torch.int32, device=DEV)
+    with tk.execution(execution):
+        out, st = _run(s, l)
+    _check(s, l, out, label=f"in-place recovery branches, execution {execution}")
+    assert st["recover_under"] == 2 and st["recover_over"] == 2
+    assert st["recover_inplace"] == 4 and st["queued"] == 0
+    assert st["inplace_certified"] == 2 and st["inplace_full"] == 2
 
 
 # ---------------------------------------------------- inputs and edge cases

@@ -5,9 +5,9 @@ the second smaller, and compared to the same bar as every selector output: each 
 the exact set contract against the CPU oracle (page "几何平均快 1.55 倍，但短行采样会输：
 腾讯怎么测精确 Top-K", section "什么叫精确，时间怎么量"), and per row their selected score
 multisets are equal bit for bit (short rows: the same index set and sentinel layout).
-The inputs exercise every piece of the scratch: row-split state (few long rows), the
-cooperative-recovery queue (rows built to underfill tau1) and its overflow past the 64
-queued rows (forced recovery of more rows than that).
+The inputs exercise every piece of the scratch: row-split state (few long rows), rows
+built to underfill tau1 (recovered in place), the cooperative-recovery queue and its
+overflow past the 64 queued rows (forced recovery of more rows than that).
 """
 import json
 import os
@@ -97,7 +97,7 @@ def test_noalloc_matches_topk_exact_two_calls():
         st = tk.get_stats()
         assert st["rowsplit"] > 0  # the reference call took the row-split path too
         if i == 0:
-            assert st["queued"] >= 3
+            assert st["recover_inplace"] >= 3  # 128K rows: recovered in place
         _compare(s, l, a, b, f"call {i + 1} ({s.shape[0]} x {s.shape[1]})")
 
 
