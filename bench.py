@@ -78,6 +78,9 @@ def parse(argv=None):
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "script with --copy-calibration into profiles/hbm_traffic_<workload>.json")
+    ap.add_argument("--phases", action="store_true",
+                    help="after the timed region, one more call per group records per-row phase stamps "
+                         "(sample, proposal, pass, commit, recovery) and the line reports their medians")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="no GPU work: per-kernel durations and per-call spans of a rocprofv3 "
                          "--kernel-trace run of this script, as one JSON line")
@@ -474,6 +477,60 @@ def run_chain(args):
     return 0 if post_bad == 0 else 1
 
 
+PATH_NAMES = {1: "sentinel", 2: "direct", 3: "tau0", 4: "tau1", 5: "recover_inplace", 6: "recover_queued",
+              7: "forced_recovery"}
+
+
+def phase_summary(records, khz):
+    """Per-row phase records (rows x 8 int64: stamps start, sampled, proposed, passed, end,
+    recovered; where; counts) of one or more calls, each call's rows a list, reduced to
+    medians in microseconds per path: sample, proposal (tau selection), pass, refine +
+    commit, the row's time in its workgroup, and for recovery rows the recovery time after
+    the row's own work; plus, per call, when the last row ended relative to the first
+    start and how far the rows' ends spread."""
+    us = 1e3 / khz
+    paths, calls = {}, []
+    for rec in records:
+        starts, ends, rec_ends = [], [], []
+        for r in rec:
+            start, sampled, proposed, passed, end, recovered, where, counts = (int(v) for v in r)
+            code = where & 0xFF
+            if code == 0:
+                continue
+            name = PATH_NAMES.get(code & 0x7F, str(code)) + ("_split" if code & 0x80 else "")
+            d = paths.setdefault(name, {"rows": 0, "row": [], "sample": [], "proposal": [], "pass": [],
+                                        "refine_commit": [], "recovery": [], "c_tau1": []})
+            d["rows"] += 1
+            d["row"].append((end - start) * us)
+            if sampled and proposed and passed and not code & 0x80:
+                d["sample"].append((sampled - start) * us)
+                d["proposal"].append((proposed - sampled) * us)
+                d["pass"].append((passed - proposed) * us)
+                if code & 0x7F in (3, 4):
+                    d["refine_commit"].append((end - passed) * us)
+            if code & 0x7F in (5, 6) and recovered:
+                d["recovery"].append((recovered - end) * us)
+                rec_ends.append(recovered)
+            if counts:
+                d["c_tau1"].append(counts & 0xFFFFFFFF)
+            starts.append(start)
+            ends.append(end)
+        if starts:
+            t0 = min(starts)
+            calls.append({"last_end_us": (max(ends) - t0) * us, "first_end_us": (min(ends) - t0) * us,
+                          "last_recovered_us": (max(rec_ends) - t0) * us if rec_ends else None})
+    out = {}
+    for name, d in sorted(paths.items()):
+        out[name] = {"rows": d["rows"]}
+        for key in ("row", "sample", "proposal", "pass", "refine_commit", "recovery", "c_tau1"):
+            if d[key]:
+                out[name][f"median_{key}" + ("" if key == "c_tau1" else "_us")] = statistics.median(d[key])
+    med = lambda k: statistics.median([c[k] for c in calls if c[k] is not None]) if any(
+        c[k] is not None for c in calls) else None
+    return {"paths": out, "calls": len(calls), "median_last_end_us": med("last_end_us"),
+            "median_first_end_us": med("first_end_us"), "median_last_recovered_us": med("last_recovered_us")}
+
+
 def versions():
     """Software versions recorded with every line (a drift in torch's RNG stream between
     versions would change the synthetic inputs; the checksums below detect it)."""
@@ -627,6 +684,22 @@ def main(argv=None):
     torch.cuda.synchronize()
     kernel_ms = [kstart[i].elapsed_time(kstop[i]) for i in range(n_hook)]
 
+    phases = None
+    if args.phases:
+        buf = torch.zeros((w.M, 8), dtype=torch.int64, device=dev)
+        khz = tk.record_phases(buf)
+        recs = []
+        try:
+            for g in range(w.groups):
+                buf.zero_()
+                select(g, stream=stream)
+                torch.cuda.synchronize()
+                recs.append(buf.cpu().tolist())
+        finally:
+            tk.record_phases(None)
+        phases = phase_summary(recs, khz)
+        phases["wall_clock_khz"] = khz
+
     # Post-timing contract check of the last output of every group.
     post_bad = 0
     for g, (s, l) in enumerate(groups):
@@ -708,6 +781,7 @@ def main(argv=None):
         "kernel_source_digest": digest,
         "generation_s": round(t_gen, 2),
         "input_checksums": checksums,
+        "phases": phases,
         "versions": versions(),
     }
     if not args.no_probe:

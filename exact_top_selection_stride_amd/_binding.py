@@ -48,6 +48,7 @@ EXPORTED = (
     "topk_exact_set_path_override", "topk_exact_last_error", "topk_stream_read_probe",
     "topk_exact_set_execution", "topk_exact_time_next_call", "topk_exact_set_proposal",
     "topk_indexer_scores", "topk_indexer_topk", "topk_exact_sorted", "topk_exact_noalloc",
+    "topk_exact_record_phases",
 )
 
 
@@ -87,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.topk_exact_set_proposal.argtypes = [i32, i32, i32]
         L.topk_exact_time_next_call.restype = ctypes.c_int
         L.topk_exact_time_next_call.argtypes = [vp, vp]
+        L.topk_exact_record_phases.restype = ctypes.c_int
+        L.topk_exact_record_phases.argtypes = [vp, i64, vp]
         L.topk_exact_last_error.restype = ctypes.c_char_p
         L.topk_exact_last_error.argtypes = []
         L.topk_stream_read_probe.restype = ctypes.c_int
@@ -288,6 +291,28 @@ def time_next_call(start, stop):
     if start is not None and (not h0 or not h1):
         raise ValueError("record both events once before arming the hook")
     _check(lib().topk_exact_time_next_call(h0 or None, h1 or None), "topk_exact_time_next_call")
+
+
+PHASE_WORDS = 8
+PHASE_NAMES = ("start", "sampled", "proposed", "passed", "end", "recovered", "where", "counts")
+PATH_CODES = {1: "sentinel", 2: "direct", 3: "tau0", 4: "tau1", 5: "recover_inplace", 6: "recover_queued",
+              7: "forced_recovery"}
+
+
+def record_phases(buf: Optional[torch.Tensor]) -> int:
+    """Arms (buf: int64 [rows, 8] GPU tensor) or disarms (None) the per-row phase
+    recording of later calls; returns the device wall-clock rate in kHz."""
+    khz = ctypes.c_int64(0)
+    if buf is None:
+        _check(lib().topk_exact_record_phases(None, 0, ctypes.addressof(khz)), "topk_exact_record_phases")
+    else:
+        if buf.dtype != torch.int64 or not buf.is_cuda or buf.dim() != 2 or buf.shape[1] != PHASE_WORDS \
+                or not buf.is_contiguous():
+            raise ValueError("buf must be a contiguous int64 [rows, 8] GPU tensor")
+        with torch.cuda.device(buf.device):
+            _check(lib().topk_exact_record_phases(buf.data_ptr(), buf.shape[0], ctypes.addressof(khz)),
+                   "topk_exact_record_phases")
+    return int(khz.value)
 
 
 def stream_read_probe(x: torch.Tensor, sink: torch.Tensor, stream=None):

@@ -150,6 +150,7 @@ struct Params {
   struct RowSplitState* rs;  // per-row state of the row-split kernels
   uint32_t ps;          // row-split: workgroups per row sampling
   uint32_t pp;          // row-split: workgroups per row passing
+  unsigned long long* phase;  // per-row phase record (PHASE_WORDS per row), or null
 };
 
 struct alignas(16) Smem {
@@ -293,6 +294,43 @@ __device__ __forceinline__ uint32_t shift_for(uint32_t span) {
 
 __device__ __forceinline__ void stat_add(Control* ctl, int slot) {
   atomicAdd(&ctl->stats[slot], 1ull);
+}
+
+// Per-row phase record (measurement hook, armed by topk_exact_record_phases): device
+// wall-clock stamps of the row's phases, its path and where it ran. Written by thread 0
+// of the workgroup that owns the phase; nothing is written while the hook is disarmed.
+constexpr int PHASE_WORDS = 8;
+enum : int {
+  PH_START = 0,      // the row's workgroup starts on it
+  PH_SAMPLED = 1,    // sample read, min/max known
+  PH_PROPOSED = 2,   // tau0 / tau1 / tau2 selected
+  PH_PASSED = 3,     // fused full-row pass done
+  PH_END = 4,        // committed, or handed to the recovery kernels
+  PH_RECOVERED = 5,  // exact recovery done (in place, or by the recovery finish kernel)
+  PH_WHERE = 6,      // path code | XCC id << 8 | hardware wave id << 32
+  PH_COUNTS = 7,     // C(tau1) | C(tau0) << 32
+};
+enum : uint32_t {
+  PATH_SENTINEL = 1, PATH_DIRECT = 2, PATH_TAU0 = 3, PATH_TAU1 = 4, PATH_RECOVER_INPLACE = 5,
+  PATH_RECOVER_QUEUED = 6, PATH_FORCED_RECOVERY = 7, PATH_SPLIT_FLAG = 0x80,
+};
+
+__device__ __forceinline__ void phase_put(unsigned long long* ph, uint32_t row, int slot, unsigned long long v) {
+  if (ph != nullptr && threadIdx.x == 0) ph[(size_t)row * PHASE_WORDS + slot] = v;
+}
+
+__device__ __forceinline__ void phase_mark(unsigned long long* ph, uint32_t row, int slot) {
+  if (ph != nullptr && threadIdx.x == 0) ph[(size_t)row * PHASE_WORDS + slot] = (unsigned long long)wall_clock64();
+}
+
+// Records the row's path with the XCC and hardware wave id (HW_ID register) it ran on.
+__device__ __forceinline__ void phase_path(unsigned long long* ph, uint32_t row, uint32_t code) {
+  if (ph != nullptr && threadIdx.x == 0) {
+    const uint32_t hw = (uint32_t)__builtin_amdgcn_s_getreg((31 << 11) | 4);   // HW_ID, 32 bits
+    const uint32_t xcc = (uint32_t)__builtin_amdgcn_s_getreg((3 << 11) | 20);  // XCC_ID, 4 bits
+    ph[(size_t)row * PHASE_WORDS + PH_WHERE] =
+        (unsigned long long)(code | (xcc << 8)) | ((unsigned long long)hw << 32);
+  }
 }
 
 // Folds per-thread min/max into s.mn / s.mx (initialised by the caller before a
@@ -1230,11 +1268,13 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
     block_minmax(mn, mx);
   }
   const uint32_t smin = s.mn, smax = s.mx;
+  phase_mark(p.phase, row, PH_SAMPLED);
   const uint32_t r1 = sample_rank(p.T1, n_s, L);
   const uint32_t r0 = sample_rank(p.T0, n_s, L);
   const uint32_t r2 = sample_rank(p.T2, n_s, L);
   uint32_t t1key, t0key, t2key;
   select_taus(n_s, r0, r1, r2, smin, smax, t0key, t1key, t2key);
+  phase_mark(p.phase, row, PH_PROPOSED);
 
   PassCtx c;
   c.t1key = t1key;
@@ -1257,6 +1297,8 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
   }
   __syncthreads();
   const uint32_t c1 = s.cnt, c0 = s.cnt0;
+  phase_mark(p.phase, row, PH_PASSED);
+  phase_put(p.phase, row, PH_COUNTS, (unsigned long long)c1 | ((unsigned long long)c0 << 32));
   if (c1 > (uint32_t)CAP) {
     // Too many admitted to hold: the K-th key is >= tau1, recover exactly. A short row
     // is recovered in place from the boundary bin of the pass histogram, a long one by
@@ -1265,19 +1307,33 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
     if (L <= p.inplace_max) {
       uint32_t n_ge;
       const uint32_t thr = overflow_threshold(p.K, t1key, c.sh, n_ge);
+      phase_mark(p.phase, row, PH_END);
       recover_in_place(x, L, p.K, n_ge <= (uint32_t)CAP ? thr : 0u, smax, t1key, smax, out, p.ctl);
+      phase_mark(p.phase, row, PH_RECOVERED);
+      phase_path(p.phase, row, PATH_RECOVER_INPLACE);
     } else {
       recover_row(p, row, x, L, t1key, smax, out);
+      phase_mark(p.phase, row, PH_END);
+      phase_path(p.phase, row, PATH_RECOVER_QUEUED);
     }
   } else if (c1 < p.K) {
     // Even the nested threshold underfills: the K-th key is < tau1. A short row is
     // recovered in place from the deeper sample rank tau2, a long one cooperatively.
     if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_UNDER);
-    if (L <= p.inplace_max) recover_in_place(x, L, p.K, t2key, smax, smin, t1key, out, p.ctl);
-    else recover_row(p, row, x, L, smin, t1key, out);
+    phase_mark(p.phase, row, PH_END);
+    if (L <= p.inplace_max) {
+      recover_in_place(x, L, p.K, t2key, smax, smin, t1key, out, p.ctl);
+      phase_mark(p.phase, row, PH_RECOVERED);
+      phase_path(p.phase, row, PATH_RECOVER_INPLACE);
+    } else {
+      recover_row(p, row, x, L, smin, t1key, out);
+      phase_path(p.phase, row, PATH_RECOVER_QUEUED);
+    }
   } else {
     if (t == 0) stat_add(p.ctl, c0 >= p.K ? TOPK_STAT_TAU0 : TOPK_STAT_TAU1);
     refine_commit(c1, p.K, c, out, p.ctl);
+    phase_mark(p.phase, row, PH_END);
+    phase_path(p.phase, row, c0 >= p.K ? PATH_TAU0 : PATH_TAU1);
   }
 }
 
@@ -1293,9 +1349,12 @@ __device__ __forceinline__ void process_row(const Params& p, uint32_t row) {
   grow_t x = (grow_t)(p.scores) + (size_t)row * p.N;
   gout_t out = (gout_t)(p.out) + (size_t)row * p.K;
   if (t == 0) stat_add(p.ctl, TOPK_STAT_ROWS);
+  phase_mark(p.phase, row, PH_START);
   if (L <= p.K) {
     for (uint32_t j = t; j < p.K; j += BLOCK) out[j] = j < L ? (int32_t)j : p.sentinel;
     if (t == 0) stat_add(p.ctl, TOPK_STAT_SENTINEL);
+    phase_mark(p.phase, row, PH_END);
+    phase_path(p.phase, row, PATH_SENTINEL);
     return;
   }
   reset_row_state();
@@ -1304,9 +1363,13 @@ __device__ __forceinline__ void process_row(const Params& p, uint32_t row) {
     if (t == 0) stat_add(p.ctl, TOPK_STAT_DIRECT);
     if (L <= (uint32_t)KEYS_CAP) direct_exact(x, L, p.K, out, p.ctl);
     else exact_full_row(x, L, p.K, 0u, KEY_MAX, out, p.ctl);
+    phase_mark(p.phase, row, PH_END);
+    phase_path(p.phase, row, PATH_DIRECT);
   } else if (p.mode == TOPK_PATH_RECOVERY) {
     if (t == 0) stat_add(p.ctl, TOPK_STAT_FORCED_RECOVERY);
     recover_row(p, row, x, L, 0u, KEY_MAX, out);
+    phase_mark(p.phase, row, PH_END);
+    phase_path(p.phase, row, PATH_FORCED_RECOVERY);
   } else {
     sampled_row<STREAM_SAMPLE>(p, row, x, L, out);
   }
@@ -1649,6 +1712,7 @@ void recovery_finish_kernel(Params p) {
       });
     }
     __syncthreads();
+    phase_mark(p.phase, r->row, PH_RECOVERED);
   }
   // The last workgroup to leave rewinds the queue for the next call; every
   // workgroup has read qcount before it increments rec_done.
@@ -1856,6 +1920,7 @@ void split_finish_kernel(Params p) {
   if (rs->whole) {
     process_row(p, row);
   } else {
+    phase_mark(p.phase, row, PH_START);
     const uint32_t L = row_length(p, row);
     grow_t x = (grow_t)(p.scores) + (size_t)row * p.N;
     gout_t out = (gout_t)(p.out) + (size_t)row * p.K;
@@ -1908,6 +1973,11 @@ void split_finish_kernel(Params p) {
       __syncthreads();
       refine_commit(c1, p.K, pass_ctx(t1key, t0key, smax), out, p.ctl);
     }
+    phase_mark(p.phase, row, PH_END);
+    phase_put(p.phase, row, PH_COUNTS, (unsigned long long)c1 | ((unsigned long long)c0 << 32));
+    const bool rec = c1 > (uint32_t)CAP || c1 < p.K;
+    phase_path(p.phase, row, PATH_SPLIT_FLAG | (rec ? (L <= p.inplace_max ? PATH_RECOVER_INPLACE : PATH_RECOVER_QUEUED)
+                                                    : (c0 >= p.K ? PATH_TAU0 : PATH_TAU1)));
   }
   // Rewind the row's state for the next call (every read of it is done).
   __syncthreads();
@@ -1991,6 +2061,9 @@ std::atomic<int> g_exec{TOPK_EXEC_AUTO};
 std::atomic<int> g_stride{(int)STRIDE};
 std::atomic<int> g_rho0{1500};
 std::atomic<int> g_rho1{1750};
+// Per-row phase recording (measurement hook): device buffer and its row capacity.
+std::atomic<unsigned long long*> g_phase_buf{nullptr};
+std::atomic<int64_t> g_phase_rows{0};
 thread_local char g_err[512] = "";
 
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -2321,6 +2394,7 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
   p.rec = st->rec;
   p.qmax = st->qmax;
   p.rs = nullptr;
+  p.phase = (timing && M <= g_phase_rows.load()) ? g_phase_buf.load() : nullptr;
   p.ps = 1;
   p.pp = 1;
   // Execution by shape. Row-split when rows are few and long: their scan and
@@ -2573,6 +2647,23 @@ int topk_exact_set_proposal(int32_t stride, int32_t rho0_permille, int32_t rho1_
   g_stride.store(stride);
   g_rho0.store(rho0_permille);
   g_rho1.store(rho1_permille);
+  return TOPK_OK;
+}
+
+int topk_exact_record_phases(uint64_t* buf, int64_t rows, int64_t* wall_clock_khz) {
+  g_err[0] = '\0';
+  if ((buf == nullptr) != (rows == 0) || rows < 0)
+    return fail(TOPK_ERR_BAD_ARG, "buf and rows: both set (rows > 0) or both empty");
+  if (wall_clock_khz != nullptr) {
+    int dev = 0, khz = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(wall clock rate)");
+    *wall_clock_khz = khz;
+  }
+  g_phase_rows.store(0);
+  g_phase_buf.store(reinterpret_cast<unsigned long long*>(buf));
+  g_phase_rows.store(rows);
   return TOPK_OK;
 }
 

@@ -216,6 +216,24 @@ int topk_exact_set_proposal(int32_t stride, int32_t rho0_permille, int32_t rho1_
  * TOPK_ERR_NULL_POINTER if exactly one event is NULL. */
 int topk_exact_time_next_call(hipEvent_t start, hipEvent_t stop);
 
+/* Measurement hook: per-row phase times (no passage defines the hook; it measures what
+ * the pages report about the mechanism, [Cx] section "采样不是处处都该开": the time of the
+ * sampled proposal against an exact one, the cost of the nested fallback and of exact
+ * recovery per affected row). While armed, every topk_exact call of at most `rows` rows
+ * outside stream capture writes, for each row r, 8 words at buf[8 r ...]: device
+ * wall-clock stamps when its workgroup starts it [0], has read its sample [1], has
+ * selected tau0 / tau1 / tau2 [2], has finished the full-row pass [3], has committed it
+ * or handed it to the recovery kernels [4], and when its exact recovery finished [5];
+ * [6] = path code (1 sentinel, 2 direct, 3 tau0, 4 tau1, 5 recovered in place, 6 queued
+ * for the recovery kernels, 7 forced recovery; +128 for row-split rows, whose stamps [0]
+ * and [4] bracket the final per-row kernel) | XCC id << 8 | hardware wave id << 32;
+ * [7] = C(tau1) | C(tau0) << 32. Stamps a row's path does not reach are left as they
+ * were (clear the buffer first). buf is device memory of [rows][8] uint64 owned by the
+ * caller, kept alive while armed; (NULL, 0) disarms. wall_clock_khz (host, may be NULL)
+ * receives the stamp frequency of the current device. Process-wide. Returns TOPK_OK,
+ * TOPK_ERR_BAD_ARG (buf and rows not both set or both empty) or TOPK_ERR_HIP. */
+int topk_exact_record_phases(uint64_t* buf, int64_t rows, int64_t* wall_clock_khz);
+
 /* Text of the last error raised on this host thread ("" if none). A library utility; no
  * passage defines it. */
 const char* topk_exact_last_error(void);

@@ -55,6 +55,9 @@ def test_argument_validation_without_gpu():
     assert L.topk_exact_noalloc(fake, fake, 2, 10, 4, fake, 5, None) == B.TOPK_ERR_BAD_SENTINEL
     assert L.topk_exact_noalloc(fake, None, 2, 10, 4, fake, -1, None) == B.TOPK_ERR_NULL_POINTER
     assert L.topk_exact_noalloc(None, None, 0, 10, 4, None, -1, None) == B.TOPK_OK
+    assert L.topk_exact_record_phases(None, 5, None) == B.TOPK_ERR_BAD_ARG
+    assert L.topk_exact_record_phases(fake, 0, None) == B.TOPK_ERR_BAD_ARG
+    assert L.topk_exact_record_phases(None, 0, None) == B.TOPK_OK
     assert L.topk_exact_set_path_override(99) == B.TOPK_ERR_BAD_ARG
     assert L.topk_exact_set_path_override(-1) == B.TOPK_ERR_BAD_ARG
     assert L.topk_exact_get_stats(None, 4, None) == B.TOPK_ERR_NULL_POINTER

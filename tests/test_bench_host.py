@@ -86,6 +86,29 @@ def test_protocol_defaults_and_overrides():
     assert (c.warmup, c.condition, c.steps) == (5, 20, 40)
 
 
+def test_phase_summary_medians_per_path():
+    # Clock at 100 MHz (10 ns per tick). Call 1: a tau0 row (sample 2 us, proposal 1 us, pass
+    # 10 us, refine 1 us), a tau1 row, a row recovered in place (6 us after its end) and an
+    # empty record; call 2: one tau0 row and a queued row recovered 20 us after its end.
+    def row(start, sampled, proposed, passed, end, recovered, code, c1=3000):
+        return [start, sampled, proposed, passed, end, recovered, code | (3 << 8) | (77 << 32), c1 | (2900 << 32)]
+    call1 = [row(1000, 1200, 1300, 2300, 2400, 0, 3), row(1000, 1250, 1350, 2350, 2500, 0, 4),
+             row(1100, 1300, 1400, 2400, 2400, 3000, 5, 1800), [0] * 8]
+    call2 = [row(0, 200, 300, 1300, 1400, 0, 3), row(0, 200, 300, 1300, 1300, 3300, 6, 1500)]
+    out = bench.phase_summary([call1, call2], khz=100_000)
+    p = out["paths"]
+    assert p["tau0"]["rows"] == 2 and abs(p["tau0"]["median_sample_us"] - 2.0) < 1e-9
+    assert abs(p["tau0"]["median_proposal_us"] - 1.0) < 1e-9 and abs(p["tau0"]["median_pass_us"] - 10.0) < 1e-9
+    assert abs(p["tau0"]["median_refine_commit_us"] - 1.0) < 1e-9 and abs(p["tau0"]["median_row_us"] - 14.0) < 1e-9
+    assert p["tau1"]["rows"] == 1 and abs(p["tau1"]["median_row_us"] - 15.0) < 1e-9
+    assert abs(p["recover_inplace"]["median_recovery_us"] - 6.0) < 1e-9
+    assert abs(p["recover_queued"]["median_recovery_us"] - 20.0) < 1e-9 and p["recover_queued"]["median_c_tau1"] == 1500
+    assert out["calls"] == 2
+    # call 1: first start 1000, last end 2500 -> 15 us; call 2: last end 1400 -> 14 us
+    assert abs(out["median_last_end_us"] - 14.5) < 1e-9
+    assert abs(out["median_last_recovered_us"] - (20.0 + 33.0) / 2) < 1e-9
+
+
 def test_device_checksum_is_a_64_bit_pattern_sum():
     x = torch.tensor([[1.0, -2.0], [float("-inf"), 0.5]], dtype=torch.float32)
     u = x.view(torch.int32).to(torch.int64)

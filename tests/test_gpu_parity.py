@@ -480,6 +480,41 @@ def test_selector_timing_hook():
     assert ev[0].elapsed_time(ev[1]) >= 0.0 and ev[2].elapsed_time(ev[3]) >= 0.0
 
 
+def test_phase_recording_hook():
+    # Per-row phase stamps: ordered in time, path codes matching the row counters, tau1
+    # counts certified; disarmed calls write nothing.
+    s, l = _window_rows("c1", [(0, 20)])
+    L = 131072
+    adv = torch.from_numpy(np.stack([_adversarial_row(L, 1000, 700 + i) for i in range(2)])).to(DEV)
+    s = torch.cat([s, adv]).contiguous()
+    l = torch.cat([l, torch.full((2,), L, dtype=torch.int32, device=DEV)]).contiguous()
+    buf = torch.zeros((s.shape[0], 8), dtype=torch.int64, device=DEV)
+    khz = tk.record_phases(buf)
+    try:
+        with tk.execution(tk.EXEC_ROW_PER_WG):
+            out, st = _run(s, l)
+    finally:
+        tk.record_phases(None)
+    _check(s, l, out, label="phase-recorded call")
+    assert khz > 0
+    rec = buf.cpu().numpy()
+    codes = rec[:, 6] & 0xFF
+    names = [tk.PATH_CODES.get(int(c)) for c in codes]
+    assert names.count("tau0") == st["tau0"] and names.count("tau1") == st["tau1"]
+    assert names.count("recover_queued") == st["queued"] >= 2
+    for r, n in zip(rec, names):
+        start, sampled, proposed, passed, end = (int(v) for v in r[:5])
+        assert 0 < start <= sampled <= proposed <= passed <= end, n
+        c1 = int(r[7]) & 0xFFFFFFFF
+        if n in ("tau0", "tau1"):
+            assert c1 >= K and r[5] == 0
+        else:
+            assert c1 < K and int(r[5]) >= end  # recovered by the cooperative kernels after
+    buf.zero_()
+    _run(s, l)
+    assert int(buf.abs().sum()) == 0
+
+
 def test_graph_replay():
     s, l = _window_rows("c1", [(0, 12)])
     s0, l0 = W.make_window(W.get("c0"), DEV)
