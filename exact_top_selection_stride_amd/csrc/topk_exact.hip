@@ -286,6 +286,41 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, WAVE - 1);
 }
 
+// Exchange with lane ^ J across the wave: DPP within rows of 16 lanes for J <= 8 (quad
+// permutes for 1 and 2; a shift each way, limited to the banks it serves, for 4 and 8),
+// a permute through the LDS crossbar for 16 and 32.
+template <int J>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (J == 1) return dpp<DPP_QUAD_SWAP1>(0u, v);
+  else if constexpr (J == 2) return dpp<DPP_QUAD_SWAP2>(0u, v);
+  else if constexpr (J == 4) return dpp<DPP_ROW_SHR + 4, 0xf, 0xa>(dpp<DPP_ROW_SHL + 4, 0xf, 0x5>(0u, v), v);
+  else if constexpr (J == 8) return dpp<DPP_ROW_SHR + 8, 0xf, 0xc>(dpp<DPP_ROW_SHL + 8, 0xf, 0x3>(0u, v), v);
+  else return (uint32_t)__shfl_xor((int)v, J);
+}
+
+// One bitonic stage over the wave: lane pairs (l, l ^ J) compare-exchange, the lower lane
+// keeping the larger value where bit KB of the lane is clear (descending runs).
+template <int KB, int J>
+__device__ __forceinline__ uint32_t bitonic_step(uint32_t v) {
+  const uint32_t p = lane_xor<J>(v);
+  const uint32_t l = lane_id();
+  const bool keep_max = ((l & (uint32_t)J) == 0u) == ((l & (1u << KB)) == 0u);
+  return keep_max ? max(v, p) : min(v, p);
+}
+
+// The wave's 64 values sorted in descending order across its lanes (lane 0 the largest).
+__device__ __forceinline__ uint32_t wave_sort_desc(uint32_t v) {
+  v = bitonic_step<1, 1>(v);
+  v = bitonic_step<2, 2>(v);  v = bitonic_step<2, 1>(v);
+  v = bitonic_step<3, 4>(v);  v = bitonic_step<3, 2>(v);  v = bitonic_step<3, 1>(v);
+  v = bitonic_step<4, 8>(v);  v = bitonic_step<4, 4>(v);  v = bitonic_step<4, 2>(v);  v = bitonic_step<4, 1>(v);
+  v = bitonic_step<5, 16>(v); v = bitonic_step<5, 8>(v);  v = bitonic_step<5, 4>(v);  v = bitonic_step<5, 2>(v);
+  v = bitonic_step<5, 1>(v);
+  v = bitonic_step<6, 32>(v); v = bitonic_step<6, 16>(v); v = bitonic_step<6, 8>(v);  v = bitonic_step<6, 4>(v);
+  v = bitonic_step<6, 2>(v);  v = bitonic_step<6, 1>(v);
+  return v;
+}
+
 // Smallest shift such that span >> shift fits in NB bins (at most 21).
 __device__ __forceinline__ uint32_t shift_for(uint32_t span) {
   if (span < (uint32_t)NB) return 0;
@@ -1158,13 +1193,16 @@ __device__ __forceinline__ void recover_row(const Params& p, uint32_t row, grow_
 // usual case, r2 is a few dozen), the three ranks are read off by counting inside that
 // short list. Otherwise the general narrowing selection runs.
 __device__ __forceinline__ void select_taus(uint32_t n_s, uint32_t r0, uint32_t r1, uint32_t r2, uint32_t mn,
-                                            uint32_t mx, uint32_t& t0key, uint32_t& t1key, uint32_t& t2key) {
+                                            uint32_t mx, uint32_t& t0key, uint32_t& t1key, uint32_t& t2key,
+                                            bool hist_is_zero = false) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   const uint32_t sh = shift_for(mx - mn);
-  for (uint32_t i = t; i < (uint32_t)NB; i += BLOCK) s.hist[i] = 0;
-  if (t == 0) s.fl_cnt = 0;
-  __syncthreads();
+  if (!hist_is_zero) {
+    for (uint32_t i = t; i < (uint32_t)NB; i += BLOCK) s.hist[i] = 0;
+    if (t == 0) s.fl_cnt = 0;
+    __syncthreads();
+  }
   for (uint32_t i = t; i < n_s; i += BLOCK) atomicAdd(&s.hist[(s.buf[i] - mn) >> sh], 1u);
   __syncthreads();
   block_find_bin(r2);
@@ -1185,15 +1223,26 @@ __device__ __forceinline__ void select_taus(uint32_t n_s, uint32_t r0, uint32_t 
       }
     }
     __syncthreads();
-    const uint32_t rk = rank_in_list(s.fl_key, m);
-    if (rk == r1 - 1) s.sel_above = s.fl_key[t];
-    if (rk == r0 - 1) s.sel_bin = s.fl_key[t];
-    if (rk == r2 - 1) s.bcast = s.fl_key[t];
-    __syncthreads();
-    t1key = s.sel_above;
-    t0key = s.sel_bin;
-    t2key = s.bcast;
-    __syncthreads();
+    if (m <= (uint32_t)WAVE) {
+      // Every wave sorts the short list across its lanes and reads the three ranks off:
+      // no rank counting by one wave, no barrier to broadcast the result. (The list is
+      // not written again before the next row's barriers.)
+      const uint32_t l = lane_id();
+      const uint32_t srt = wave_sort_desc(l < m ? s.fl_key[l] : 0u);
+      t1key = (uint32_t)__builtin_amdgcn_readlane((int)srt, (int)(r1 - 1));
+      t0key = (uint32_t)__builtin_amdgcn_readlane((int)srt, (int)(r0 - 1));
+      t2key = (uint32_t)__builtin_amdgcn_readlane((int)srt, (int)(r2 - 1));
+    } else {
+      const uint32_t rk = rank_in_list(s.fl_key, m);
+      if (rk == r1 - 1) s.sel_above = s.fl_key[t];
+      if (rk == r0 - 1) s.sel_bin = s.fl_key[t];
+      if (rk == r2 - 1) s.bcast = s.fl_key[t];
+      __syncthreads();
+      t1key = s.sel_above;
+      t0key = s.sel_bin;
+      t2key = s.bcast;
+      __syncthreads();
+    }
   } else {
     uint32_t unused;
     select_rank([&](auto&& f) {
@@ -1273,7 +1322,9 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
   const uint32_t r0 = sample_rank(p.T0, n_s, L);
   const uint32_t r2 = sample_rank(p.T2, n_s, L);
   uint32_t t1key, t0key, t2key;
-  select_taus(n_s, r0, r1, r2, smin, smax, t0key, t1key, t2key);
+  // The histogram and list counters are still zero from the row's reset (the sample does
+  // not touch them).
+  select_taus(n_s, r0, r1, r2, smin, smax, t0key, t1key, t2key, true);
   phase_mark(p.phase, row, PH_PROPOSED);
 
   PassCtx c;
