@@ -2490,14 +2490,22 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord(start)");
   }
   if (split) {
-    // Workgroups per row: enough units to keep every resident slot busy several
-    // times over, but no unit smaller than ~256 sampled lines / ~170 periods.
+    // Workgroups per row: enough units to keep every resident slot busy several times
+    // over, at most `cap` per row, and no unit smaller than `unit_p` periods (pass) /
+    // `unit_s` sampled lines (sample). Measured on MI355X (graph replays, median call):
+    // a cap of 64 rows for 1-4 rows of 1M takes 1 row from 50.3 to 42.0 us and 4 rows from
+    // 52.1 to 43.3 us (16 and 64 rows unchanged at 16); units of 64 periods / lines for at
+    // most 16 rows of up to 256K take 1 row of 128K from 37.4 to 33.5 us and 16 rows from
+    // 38.2 to 34.9 us, while 64 rows lose with them (43.8 -> 54.0 us).
     const int64_t n_s_max = (N_alloc + STRIDE - 1) / STRIDE;
+    const int64_t cap = M <= 4 ? 64 : (M <= 8 ? 32 : 16);
+    const bool small_units = M <= 16 && n_s_max <= 2048;
+    const int64_t unit_p = small_units ? 64 : 170, unit_s = small_units ? 64 : 256;
     int64_t pp = (4 * resident + M - 1) / M, ps = (2 * resident + M - 1) / M;
-    pp = pp < 1 ? 1 : (pp > 16 ? 16 : pp);
-    ps = ps < 1 ? 1 : (ps > 16 ? 16 : ps);
-    const int64_t pp_cap = n_s_max / 170 > 1 ? n_s_max / 170 : 1;
-    const int64_t ps_cap = n_s_max / 256 > 1 ? n_s_max / 256 : 1;
+    pp = pp < 1 ? 1 : (pp > cap ? cap : pp);
+    ps = ps < 1 ? 1 : (ps > cap ? cap : ps);
+    const int64_t pp_cap = n_s_max / unit_p > 1 ? n_s_max / unit_p : 1;
+    const int64_t ps_cap = n_s_max / unit_s > 1 ? n_s_max / unit_s : 1;
     p.pp = (uint32_t)(pp < pp_cap ? pp : pp_cap);
     p.ps = (uint32_t)(ps < ps_cap ? ps : ps_cap);
     p.rs = st->rs;
