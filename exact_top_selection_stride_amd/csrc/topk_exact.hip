@@ -74,6 +74,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef const GLB uint32_t* grow_t;   // a row of score bit patterns
 typedef GLB int32_t* gout_t;          // a row of output indices
 
+// A row's output: its K index slots and, for the sorted output, the selected keys in the
+// same slots (so that the sort needs no second read of the scores). Every selected
+// element is written through put().
+struct RowOut {
+  gout_t idx;
+  GLB uint32_t* key;  // null unless the keys are wanted
+  __device__ __forceinline__ void put(uint32_t slot, uint32_t index, uint32_t k) const {
+    idx[slot] = (int32_t)index;
+    if (key != nullptr) key[slot] = k;
+  }
+};
+
 constexpr int BLOCK = 512;            // threads per workgroup (8 waves of 64)
 constexpr int WAVE = 64;
 constexpr int NWAVES = BLOCK / WAVE;
@@ -151,7 +163,15 @@ struct Params {
   uint32_t ps;          // row-split: workgroups per row sampling
   uint32_t pp;          // row-split: workgroups per row passing
   unsigned long long* phase;  // per-row phase record (PHASE_WORDS per row), or null
+  uint32_t* okey;       // [M][K] selected keys beside out (sorted output), or null
 };
+
+__device__ __forceinline__ RowOut row_out(const Params& p, uint32_t row) {
+  RowOut o;
+  o.idx = (gout_t)(p.out) + (size_t)row * p.K;
+  o.key = p.okey != nullptr ? (GLB uint32_t*)(p.okey) + (size_t)row * p.K : nullptr;
+  return o;
+}
 
 struct alignas(16) Smem {
   uint32_t buf[2 * CAP];       // candidates: idx in [0,CAP), key in [CAP,2CAP); or keys only
@@ -536,7 +556,7 @@ __device__ __forceinline__ void reset_row_state() {
 // Commits keys > T (slots continue from s.out_gt) and up to K - gt_total keys == T
 // (slots gt_total + 0..) from a key list in LDS with indices idx (or the position).
 __device__ __forceinline__ void commit_list(const uint32_t* keys, const uint32_t* idx, uint32_t n,
-                                            uint32_t T, uint32_t gt_total, uint32_t K, gout_t out) {
+                                            uint32_t T, uint32_t gt_total, uint32_t K, RowOut out) {
   Smem& s = g_s;
   const uint32_t ties = K - gt_total;
   // Count this thread's keys of each kind, reserve their slots once per wave, then write.
@@ -552,10 +572,10 @@ __device__ __forceinline__ void commit_list(const uint32_t* keys, const uint32_t
   for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
     const uint32_t k = keys[i];
     if (k > T) {
-      if (p < K) out[p] = (int32_t)(idx ? idx[i] : i);
+      if (p < K) out.put(p, idx ? idx[i] : i, k);
       ++p;
     } else if (k == T) {
-      if (q < ties && gt_total + q < K) out[gt_total + q] = (int32_t)(idx ? idx[i] : i);
+      if (q < ties && gt_total + q < K) out.put(gt_total + q, idx ? idx[i] : i, k);
       ++q;
     }
   }
@@ -570,7 +590,7 @@ __device__ __forceinline__ void commit_list(const uint32_t* keys, const uint32_t
 // into LDS; the bin is then resolved exactly. If the bin exceeds the LDS buffer,
 // it is narrowed by further passes over the row instead.
 __device__ __attribute__((noinline)) void exact_full_row(grow_t x, uint32_t L, uint32_t K, uint32_t lo,
-                                                         uint32_t hi, gout_t out, Control* ctl) {
+                                                         uint32_t hi, RowOut out, Control* ctl) {
   Smem& s = g_s;
   reset_row_state();
   const uint32_t sh = shift_for(hi - lo);
@@ -595,7 +615,7 @@ __device__ __attribute__((noinline)) void exact_full_row(grow_t x, uint32_t L, u
     const uint32_t k = key_of_bits(u);
     const bool g = k > bhi;
     const uint32_t p = wave_reserve(g, &s.out_gt);
-    if (g && p < K) out[p] = (int32_t)e;
+    if (g && p < K) out.put(p, e, k);
     if (fits) {
       const bool in = k >= blo && k <= bhi;
       const uint32_t f = wave_reserve(in, &s.cnt);
@@ -624,10 +644,10 @@ __device__ __attribute__((noinline)) void exact_full_row(grow_t x, uint32_t L, u
       const uint32_t k = key_of_bits(u);
       const bool g = k > T && k <= bhi;
       const uint32_t p = wave_reserve(g, &s.out_gt);
-      if (g && p < K) out[p] = (int32_t)e;
+      if (g && p < K) out.put(p, e, k);
       const bool q_ = k == T;
       const uint32_t q = wave_reserve(q_, &s.out_tie);
-      if (q_ && q < ties && gt_total + q < K) out[gt_total + q] = (int32_t)e;
+      if (q_ && q < ties && gt_total + q < K) out.put(gt_total + q, e, k);
     });
   }
 }
@@ -638,10 +658,10 @@ __device__ __attribute__((noinline)) void exact_full_row(grow_t x, uint32_t L, u
 // read), its first histogram over [min, max] is built there, and the LDS list is
 // refined like a certified candidate list (refine_list, below).
 template <bool KEYS_ONLY>
-__device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t base, uint32_t sh, gout_t out,
+__device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t base, uint32_t sh, RowOut out,
                                             Control* ctl);
 
-__device__ __forceinline__ void direct_exact(grow_t x, uint32_t L, uint32_t K, gout_t out, Control* ctl) {
+__device__ __forceinline__ void direct_exact(grow_t x, uint32_t L, uint32_t K, RowOut out, Control* ctl) {
   Smem& s = g_s;
   uint32_t mn = KEY_MAX, mx = 0;
   for_each_element(x, L, [&](uint32_t u, uint32_t e) {
@@ -965,7 +985,7 @@ __device__ __forceinline__ void sample_lines(grow_t x, uint32_t L, uint32_t n_s,
 // bin's keys move to the frontier buffer (or, when too many, only their extremes are
 // noted), and the frontier is resolved exactly.
 template <bool KEYS_ONLY>
-__device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t base, uint32_t sh, gout_t out,
+__device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t base, uint32_t sh, RowOut out,
                                             Control* ctl) {
   Smem& s = g_s;
   // The list: (index, key) pairs at s.buf[i], s.buf[CAP + i], or keys only at s.buf[i]
@@ -1007,7 +1027,7 @@ __device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t bas
       for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
         const uint32_t k = key_at(i);
         if (k > bhi) {
-          if (p < K) out[p] = (int32_t)id_at(i);
+          if (p < K) out.put(p, id_at(i), k);
           ++p;
         } else if (fits && k >= blo) {
           if (f < (uint32_t)FL_CAP) {
@@ -1033,7 +1053,7 @@ __device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t bas
     const uint32_t rk = rank_in_list(s.fl_key, cb);
     const bool sel = rk < need;
     const uint32_t pp = wave_reserve(sel, &s.out_gt);
-    if (sel && pp < K) out[pp] = (int32_t)s.fl_idx[threadIdx.x];
+    if (sel && pp < K) out.put(pp, s.fl_idx[threadIdx.x], s.fl_key[threadIdx.x]);
   } else if (fits) {
     // A longer frontier (one key per thread): find the K-th key T inside it, from the
     // extremes when it is a single repeated key, else by radix narrowing over
@@ -1055,10 +1075,10 @@ __device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t bas
     const uint32_t id = has ? s.fl_idx[threadIdx.x] : 0u;
     const bool g = has && k > T;
     const uint32_t pg = wave_reserve(g, &s.out_gt);
-    if (g && pg < K) out[pg] = (int32_t)id;
+    if (g && pg < K) out.put(pg, id, k);
     const bool e = has && k == T;
     const uint32_t q = wave_reserve(e, &s.out_tie);
-    if (e && q < ties && gt_total + q < K) out[gt_total + q] = (int32_t)id;
+    if (e && q < ties && gt_total + q < K) out.put(gt_total + q, id, k);
   } else {
     if (threadIdx.x == 0) stat_add(ctl, TOPK_STAT_FRONTIER_WIDE);
     if (s.mn == s.mx) {
@@ -1085,10 +1105,10 @@ __device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t bas
       for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
         const uint32_t k = key_at(i);
         if (k > T && k <= bhi) {
-          if (p < K) out[p] = (int32_t)id_at(i);
+          if (p < K) out.put(p, id_at(i), k);
           ++p;
         } else if (k == T) {
-          if (q < ties && gt_total + q < K) out[gt_total + q] = (int32_t)id_at(i);
+          if (q < ties && gt_total + q < K) out.put(gt_total + q, id_at(i), k);
           ++q;
         }
       }
@@ -1098,7 +1118,7 @@ __device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t bas
 
 // After a certified sampled pass: n = C(tau1) <= CAP candidates in LDS with the first
 // histogram over (key - key(tau1)) >> sh.
-__device__ __forceinline__ void refine_commit(uint32_t n, uint32_t K, const PassCtx c, gout_t out, Control* ctl) {
+__device__ __forceinline__ void refine_commit(uint32_t n, uint32_t K, const PassCtx c, RowOut out, Control* ctl) {
   refine_list<false>(n, K, c.t1key, c.sh, out, ctl);
 }
 
@@ -1121,7 +1141,7 @@ __device__ __forceinline__ PassCtx pass_ctx(uint32_t t1key, uint32_t t0key, uint
 // Takes scalars only: a reference to the launch parameters would force them into
 // scratch memory in every caller.
 __device__ __attribute__((noinline)) void recover_in_place(grow_t x, uint32_t L, uint32_t K, uint32_t thr,
-                                                           uint32_t smax, uint32_t lo, uint32_t hi, gout_t out,
+                                                           uint32_t smax, uint32_t lo, uint32_t hi, RowOut out,
                                                            Control* ctl) {
   Smem& s = g_s;
   if (threadIdx.x == 0) stat_add(ctl, TOPK_STAT_RECOVER_INPLACE);
@@ -1159,7 +1179,7 @@ __device__ __forceinline__ uint32_t overflow_threshold(uint32_t K, uint32_t t1ke
 // recovers it here when the queue is full. Nothing has been written to the row's
 // output yet. [lo, hi] is the key range the recovery histogram bins.
 __device__ __forceinline__ void recover_row(const Params& p, uint32_t row, grow_t x, uint32_t L, uint32_t lo, uint32_t hi,
-                            gout_t out) {
+                            RowOut out) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   if (t == 0) s.bcast = atomicAdd(&p.ctl->qcount, 1u);
@@ -1281,7 +1301,7 @@ __device__ __forceinline__ void write_hot_bitmap(const uint32_t* lmax, uint32_t 
 }
 
 template <bool STREAM_SAMPLE>
-__device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_t x, uint32_t L, gout_t out) {
+__device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_t x, uint32_t L, RowOut out) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   // Rows whose stride-s sample would not fit the LDS key list (L > 16384 s, past the
@@ -1398,11 +1418,11 @@ __device__ __forceinline__ void process_row(const Params& p, uint32_t row) {
   uint32_t L = len < 0 ? 0u : (uint32_t)len;
   if (L > p.N) L = p.N;
   grow_t x = (grow_t)(p.scores) + (size_t)row * p.N;
-  gout_t out = (gout_t)(p.out) + (size_t)row * p.K;
+  const RowOut out = row_out(p, row);
   if (t == 0) stat_add(p.ctl, TOPK_STAT_ROWS);
   phase_mark(p.phase, row, PH_START);
   if (L <= p.K) {
-    for (uint32_t j = t; j < p.K; j += BLOCK) out[j] = j < L ? (int32_t)j : p.sentinel;
+    for (uint32_t j = t; j < p.K; j += BLOCK) out.idx[j] = j < L ? (int32_t)j : p.sentinel;
     if (t == 0) stat_add(p.ctl, TOPK_STAT_SENTINEL);
     phase_mark(p.phase, row, PH_END);
     phase_path(p.phase, row, PATH_SENTINEL);
@@ -1635,7 +1655,7 @@ __global__ __launch_bounds__(BLOCK) void recovery_collect_kernel(Params p) {
       r->bin_lo = blo;
       r->bin_hi = bhi;
     }
-    gout_t out = (gout_t)(p.out) + (size_t)r->row * K;
+    const RowOut out = row_out(p, r->row);
     uint32_t na = 0, nb = 0;
 #pragma unroll
     for (int u = 0; u < REC_CHUNKS; ++u) {
@@ -1685,7 +1705,7 @@ __global__ __launch_bounds__(BLOCK) void recovery_collect_kernel(Params p) {
         const bool ok = o >= off && o < off + n;
         const uint32_t e = begin + o - off;  // element index in the row
         if (ok && k > bhi) {
-          if (pa < K) out[pa] = (int32_t)e;
+          if (pa < K) out.put(pa, e, k);
           ++pa;
         }
         if (ok && fits && k >= blo && k <= bhi) {
@@ -1717,7 +1737,7 @@ void recovery_finish_kernel(Params p) {
     const uint32_t need = K - above;
     const uint32_t L = r->L;
     grow_t x = (grow_t)(p.scores) + (size_t)r->row * p.N;
-    gout_t out = (gout_t)(p.out) + (size_t)r->row * K;
+    const RowOut out = row_out(p, r->row);
     if (t == 0) {
       s.out_gt = above;
       s.out_tie = 0;
@@ -1732,7 +1752,7 @@ void recovery_finish_kernel(Params p) {
       const uint32_t rk = rank_in_list(s.fl_key, cb);
       const bool sel = rk < need;
       const uint32_t pp = wave_reserve(sel, &s.out_gt);
-      if (sel && pp < K) out[pp] = (int32_t)s.fl_idx[t];
+      if (sel && pp < K) out.put(pp, s.fl_idx[t], s.fl_key[t]);
     } else if (cb <= (uint32_t)CAP) {
       for (uint32_t i = t; i < cb; i += BLOCK) {
         s.buf[i] = r->cand_idx[i];
@@ -1756,10 +1776,10 @@ void recovery_finish_kernel(Params p) {
         const uint32_t k = key_of_bits(u);
         const bool g = k > T && k <= bhi;
         const uint32_t pp = wave_reserve(g, &s.out_gt);
-        if (g && pp < K) out[pp] = (int32_t)e;
+        if (g && pp < K) out.put(pp, e, k);
         const bool q_ = k == T;
         const uint32_t qq = wave_reserve(q_, &s.out_tie);
-        if (q_ && qq < ties && gt_total + qq < K) out[gt_total + qq] = (int32_t)e;
+        if (q_ && qq < ties && gt_total + qq < K) out.put(gt_total + qq, e, k);
       });
     }
     __syncthreads();
@@ -1974,7 +1994,7 @@ void split_finish_kernel(Params p) {
     phase_mark(p.phase, row, PH_START);
     const uint32_t L = row_length(p, row);
     grow_t x = (grow_t)(p.scores) + (size_t)row * p.N;
-    gout_t out = (gout_t)(p.out) + (size_t)row * p.K;
+    const RowOut out = row_out(p, row);
     const uint32_t c1 = rs->c1, c0 = rs->c0;
     const uint32_t t1key = rs->t1key, t0key = rs->t0key, t2key = rs->t2key;
     const uint32_t smin = ~rs->mn_inv, smax = rs->mx;
@@ -2218,7 +2238,7 @@ __global__ __launch_bounds__(BLOCK) void sort_rows_kernel(const float* __restric
                                                           const int32_t* __restrict__ row_len,
                                                           uint32_t N, uint32_t K,
                                                           int32_t* __restrict__ out_idx,
-                                                          float* __restrict__ out_val, int32_t sentinel) {
+                                                          float* out_val, int32_t sentinel) {
   constexpr uint32_t P = (uint32_t)EPT * BLOCK;
   __shared__ uint64_t c[P];
   const uint32_t row = blockIdx.x, t = threadIdx.x;
@@ -2228,6 +2248,11 @@ __global__ __launch_bounds__(BLOCK) void sort_rows_kernel(const float* __restric
   const uint32_t n = L < K ? L : K;  // valid entries of the row
   int32_t* o = out_idx + (size_t)row * K;
   const uint32_t* x = reinterpret_cast<const uint32_t*>(scores) + (size_t)row * N;
+  // For rows longer than K the selector left each selected key in out_val, beside its
+  // index (read contiguously here); otherwise the scores are read at the indices (short
+  // rows: the first L scores of the row, in order).
+  const uint32_t* kin = (out_val != nullptr && L > K) ? reinterpret_cast<const uint32_t*>(out_val) + (size_t)row * K
+                                                      : nullptr;
   uint64_t v[EPT];
 #pragma unroll
   for (int q = 0; q < EPT; ++q) {
@@ -2236,9 +2261,11 @@ __global__ __launch_bounds__(BLOCK) void sort_rows_kernel(const float* __restric
     if (e < n) {
       // The selector wrote an index in [0, L) here; the clamp only keeps reads in bounds.
       const uint32_t i = (uint32_t)o[e] < L ? (uint32_t)o[e] : 0u;
-      v[q] = ((uint64_t)key_of_bits(x[i]) << 32) | (uint64_t)(0xFFFFFFFFu - i);
+      const uint32_t k = kin != nullptr ? kin[e] : key_of_bits(x[i]);
+      v[q] = ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - i);
     }
   }
+  __syncthreads();  // every key of the row is read before any thread overwrites out_val
   // Bitonic network: for each (k, j) every entry e meets e ^ j; a run is descending where
   // bit k of e is clear, and the lower entry of a pair keeps the larger value there.
   for (uint32_t k = 2; k <= P; k <<= 1) {
@@ -2409,8 +2436,11 @@ int selector_check(const float* scores, const int32_t* row_len, int64_t M, int64
 // Enqueues the selector and recovery kernels of a checked call on the state st (the
 // workspace, or the allocation-free entry point's scratch). `timing`: the call may take
 // the armed timing events (not under capture).
+// `okey`: device [M][K], receives each selected element's key in its output slot
+// (sorted output), or null.
 int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc, int32_t K,
-                    int32_t* out_idx, int32_t sentinel, hipStream_t stream, bool timing, DevState* st) {
+                    int32_t* out_idx, int32_t sentinel, hipStream_t stream, bool timing, DevState* st,
+                    uint32_t* okey = nullptr) {
   int rc = TOPK_OK;
   Params p;
   p.scores = scores;
@@ -2446,6 +2476,7 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
   p.qmax = st->qmax;
   p.rs = nullptr;
   p.phase = (timing && M <= g_phase_rows.load()) ? g_phase_buf.load() : nullptr;
+  p.okey = okey;
   p.ps = 1;
   p.pp = 1;
   // Execution by shape. Row-split when rows are few and long: their scan and
@@ -2588,7 +2619,10 @@ int topk_exact_sorted(const float* scores, const int32_t* row_len, int64_t M, in
   int rc = selector_check(scores, row_len, M, N_alloc, K, out_idx, sentinel, stream, &capturing, &st);
   if (rc != TOPK_OK || st == nullptr) return rc;
   if ((reinterpret_cast<uintptr_t>(out_val) & 3u) != 0) return fail(TOPK_ERR_BAD_ARG, "out_val is not 4-byte aligned");
-  rc = selector_launch(scores, row_len, M, N_alloc, K, out_idx, sentinel, stream, !capturing, st);
+  // With values wanted, the selector also writes each selected key into out_val (same
+  // slot as its index); the sort then reads those instead of gathering the scores again.
+  rc = selector_launch(scores, row_len, M, N_alloc, K, out_idx, sentinel, stream, !capturing, st,
+                       reinterpret_cast<uint32_t*>(out_val));
   if (rc != TOPK_OK) return rc;
   // Entries per thread: the smallest power of two with EPT * BLOCK >= K (K <= 4096).
   const dim3 grid((unsigned)M), block(BLOCK);

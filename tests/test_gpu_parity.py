@@ -823,6 +823,36 @@ def test_sorted_output_random_shapes(seed):
         _check_sorted(s, l, idx, val, Kr, label=f"seed {seed} K {Kr} mode {mode}")
 
 
+@pytest.mark.parametrize("execution", [tk.EXEC_PERSISTENT, tk.EXEC_ROW_PER_WG, tk.EXEC_ROWSPLIT])
+def test_sorted_output_every_execution(execution):
+    # The selector leaves each selected key in out_val for the sort (rows longer than K);
+    # every commit path (tau0 / tau1 refinement, in-place and queued exact recovery, the
+    # direct path, short rows) in every execution mode, with values and without them (the
+    # indices-only call gathers the scores instead).
+    L = 131072
+    s1, l1 = _window_rows("c1", [(0, 6)])
+    adv = torch.from_numpy(np.stack([_adversarial_row(L, 1000, 900), _adversarial_row(L, 2030, 901)])).to(DEV)
+    short = torch.from_numpy(np.stack([_controlled_row(65536, "under_certified", 902),
+                                       _controlled_row(65536, "over_full", 903)])).to(DEV)
+    short = torch.nn.functional.pad(short, (0, L - 65536), value=float("-inf"))
+    s = torch.cat([s1, adv, short]).contiguous()
+    l = torch.cat([l1, torch.full((2,), L, dtype=torch.int32, device=DEV),
+                   torch.full((2,), 65536, dtype=torch.int32, device=DEV)]).contiguous()
+    l[2] = 9000   # direct path
+    l[3] = 1500   # shorter than K
+    with tk.execution(execution):
+        tk.reset_stats()
+        idx, val = tk.topk_exact_sorted(s, l, K=K)
+        torch.cuda.synchronize()
+        st = tk.get_stats()
+        idx2, _ = tk.topk_exact_sorted(s, l, K=K, values=False)
+        torch.cuda.synchronize()
+    _check_sorted(s, l, idx, val, K, label=f"sorted, execution {execution}")
+    _check_sorted(s, l, idx2, None, K, label=f"sorted indices only, execution {execution}")
+    assert st["direct"] == 1 and st["sentinel"] == 1
+    assert st["recover_under"] + st["recover_over"] >= 3
+
+
 def test_sorted_output_k4096_and_misaligned_values():
     s, l = _window_rows("c3a", [(8000, 3)])
     idx, val = tk.topk_exact_sorted(s, l, K=4096)
