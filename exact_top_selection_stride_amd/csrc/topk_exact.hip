@@ -125,16 +125,23 @@ struct Control {
 // One row queued for cooperative exact recovery. Written by the workgroup that
 // queues the row; the histogram, counters and candidates are filled by the
 // recovery kernels.
+// Recovery slot modes. REC_WINDOW: the K-th key is known to lie in [bin_lo, bin_hi]
+// (the row's own pass located it), so the collect and finish kernels complete the row
+// alone. REC_HIST: nothing is known; the histogram kernel first bins the whole row.
+constexpr uint32_t REC_HIST = 0u, REC_WINDOW = 1u;
+
 struct RecSlot {
   uint32_t row;
   uint32_t L;
-  uint32_t lo, hi;       // key range binned by the first histogram
-  uint32_t out_gt;       // output slots taken by keys above the boundary bin
-  uint32_t cnt;          // candidates collected from the boundary bin
+  uint32_t lo, hi;       // key range binned by the histogram (REC_HIST); fallback range (REC_WINDOW)
+  uint32_t out_gt;       // next output slot for keys above the boundary bin
+  uint32_t cnt;          // candidates collected from the boundary bin (all, even past CAP)
   uint32_t bin_above;    // keys above the boundary bin
-  uint32_t bin_count;    // keys in the boundary bin
+  uint32_t bin_count;    // keys in the boundary bin (REC_HIST)
   uint32_t bin_lo, bin_hi;
-  uint32_t pad[22];
+  uint32_t mode;         // REC_HIST or REC_WINDOW
+  uint32_t commit;       // REC_WINDOW: the collect kernel commits the keys above bin_hi
+  uint32_t pad[20];
   uint32_t hist[NB];
   uint32_t cand_idx[CAP];
   uint32_t cand_key[CAP];
@@ -1174,6 +1181,71 @@ __device__ __forceinline__ uint32_t overflow_threshold(uint32_t K, uint32_t t1ke
   return t1key + (b << sh);
 }
 
+// Hands a row whose K-th key lies in [wlo, whi] to the collect and finish recovery
+// kernels (no histogram pass): `above` keys of the row exceed whi; with commit they are
+// committed by the collect kernel, otherwise the caller has already written them to
+// output slots [0, above). If the queue is full the row is recovered here instead (the
+// exact full-row select over [lo, hi], which rewrites every slot).
+__device__ __forceinline__ void recover_row_window(const Params& p, uint32_t row, grow_t x, uint32_t L, uint32_t wlo,
+                                                   uint32_t whi, uint32_t above, bool commit, uint32_t lo,
+                                                   uint32_t hi, RowOut out) {
+  Smem& s = g_s;
+  const uint32_t t = threadIdx.x;
+  if (t == 0) s.bcast = atomicAdd(&p.ctl->qcount, 1u);
+  __syncthreads();
+  const uint32_t q = s.bcast;
+  __syncthreads();
+  if (q < p.qmax) {
+    if (t == 0) {
+      RecSlot* r = p.rec + q;
+      r->row = row;
+      r->L = L;
+      r->lo = lo;
+      r->hi = hi;
+      r->mode = REC_WINDOW;
+      r->commit = commit ? 1u : 0u;
+      r->bin_lo = wlo;
+      r->bin_hi = whi;
+      r->bin_above = above;
+      r->out_gt = commit ? 0u : above;
+      r->cnt = 0;
+      stat_add(p.ctl, TOPK_STAT_QUEUED);
+    }
+  } else {
+    if (t == 0) {
+      stat_add(p.ctl, TOPK_STAT_RECOVER_INPLACE);
+      stat_add(p.ctl, TOPK_STAT_INPLACE_FULL);
+    }
+    exact_full_row(x, L, p.K, lo, hi, out, p.ctl);
+  }
+}
+
+// An overflowing row (C(tau1) > CAP >= K) for the recovery kernels: the pass histogram
+// s.hist over (key - t1key) >> sh counted every admitted key, so the bin holding rank K
+// and the count of keys above it are known, and the collect kernel commits the keys
+// above that bin and gathers the bin itself.
+__device__ __forceinline__ void queue_overflow(const Params& p, uint32_t row, grow_t x, uint32_t L, uint32_t t1key,
+                                               uint32_t sh, uint32_t smax, RowOut out) {
+  block_find_bin(p.K);
+  const uint32_t b = g_s.sel_bin, above = g_s.sel_above;
+  const uint32_t blo = t1key + (b << sh);
+  const uint32_t wdt = (1u << sh) - 1u;
+  const uint32_t bhi = (b == (uint32_t)(NB - 1)) ? KEY_MAX : blo + ((KEY_MAX - blo) < wdt ? (KEY_MAX - blo) : wdt);
+  recover_row_window(p, row, x, L, blo, bhi, above, true, t1key, smax, out);
+}
+
+// An underfilled row (C(tau1) < K) for the recovery kernels: its C(tau1) admitted keys
+// (idx[i], key[i], i < c1) are all in the top K and are committed here; the remaining
+// K - C(tau1) lie below tau1, and the collect kernel gathers [tau2, tau1) for them. If
+// that window holds too few, the finish kernel selects over the whole row instead.
+template <class P>
+__device__ __forceinline__ void queue_underfill(const Params& p, uint32_t row, grow_t x, uint32_t L, uint32_t c1,
+                                                uint32_t t1key, uint32_t t2key, uint32_t smin, P idx, P key,
+                                                RowOut out) {
+  for (uint32_t i = threadIdx.x; i < c1; i += BLOCK) out.put(i, idx[i], key[i]);
+  recover_row_window(p, row, x, L, t2key, t1key - 1u, c1, false, smin, t1key, out);
+}
+
 // Hands a row that needs exact full-row recovery to the cooperative recovery
 // kernels (which run after this kernel and spread the row over the whole GPU), or
 // recovers it here when the queue is full. Nothing has been written to the row's
@@ -1193,6 +1265,8 @@ __device__ __forceinline__ void recover_row(const Params& p, uint32_t row, grow_
       r->L = L;
       r->lo = lo;
       r->hi = hi;
+      r->mode = REC_HIST;
+      r->commit = 1u;
       r->out_gt = 0;
       r->cnt = 0;
       stat_add(p.ctl, TOPK_STAT_QUEUED);
@@ -1383,7 +1457,7 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
       phase_mark(p.phase, row, PH_RECOVERED);
       phase_path(p.phase, row, PATH_RECOVER_INPLACE);
     } else {
-      recover_row(p, row, x, L, t1key, smax, out);
+      queue_overflow(p, row, x, L, t1key, c.sh, smax, out);
       phase_mark(p.phase, row, PH_END);
       phase_path(p.phase, row, PATH_RECOVER_QUEUED);
     }
@@ -1397,7 +1471,8 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
       phase_mark(p.phase, row, PH_RECOVERED);
       phase_path(p.phase, row, PATH_RECOVER_INPLACE);
     } else {
-      recover_row(p, row, x, L, smin, t1key, out);
+      queue_underfill(p, row, x, L, c1, t1key, t2key, smin, (const uint32_t*)&s.buf[0], (const uint32_t*)&s.buf[CAP],
+                      out);
       phase_path(p.phase, row, PATH_RECOVER_QUEUED);
     }
   } else {
@@ -1519,6 +1594,7 @@ __global__ __launch_bounds__(BLOCK) void recovery_hist_kernel(Params p) {
     RecSlot* r = p.rec + q;
     const uint32_t L = r->L;
     if (begin >= L || r->row >= p.M || L > p.N) continue;  // (a slot of a call that failed)
+    if (r->mode != REC_HIST) continue;                     // the row's own pass located its bin
     const uint32_t n = min(REC_SEG, L - begin);
     const uint32_t lo = r->lo, hi = r->hi;
     const uint32_t sh = shift_for(hi - lo);
@@ -1600,60 +1676,70 @@ __global__ __launch_bounds__(BLOCK) void recovery_collect_kernel(Params p) {
       const uint32_t g = 4u * (t + (uint32_t)u * BLOCK);
       v[u] = load4(ab + (g < glast ? g : glast));
     }
-    // The boundary bin, from the completed histogram (every item derives the same).
-    uint32_t h[NB / BLOCK];
-    uint32_t sum = 0;
-#pragma unroll
-    for (int j = 0; j < NB / BLOCK; ++j) {
-      h[j] = r->hist[t * (NB / BLOCK) + j];
-      sum += h[j];
-      s.hist[t * (NB / BLOCK) + j] = h[j];
-    }
-    uint32_t incl = wave_incl_scan(sum);
+    // The window of keys to gather, [blo, bhi], and whether the keys above it are
+    // committed here: given by the row's own pass (REC_WINDOW), or derived in every item
+    // from the completed histogram (REC_HIST).
     const uint32_t w = t / WAVE;
-    if (lane_id() == WAVE - 1) s.wtmp[w] = incl;
-    if (t == 0) {
-      s.sel_bin = 0;
-      s.sel_above = 0;
-    }
-    __syncthreads();
-    uint32_t before = 0, total = 0;
+    uint32_t blo, bhi;
+    bool fits = true, commit = true;
+    if (r->mode == REC_WINDOW) {
+      blo = r->bin_lo;
+      bhi = r->bin_hi;
+      commit = r->commit != 0u;
+    } else {
+      // The boundary bin, from the completed histogram (every item derives the same).
+      uint32_t h[NB / BLOCK];
+      uint32_t sum = 0;
 #pragma unroll
-    for (int i = 0; i < NWAVES; ++i) {
-      const uint32_t v = s.wtmp[i];
-      before += ((uint32_t)i < w) ? v : 0u;
-      total += v;
-    }
-    incl += before;
-    const uint32_t hi_cnt = total - incl;
-    if (hi_cnt < K && K <= hi_cnt + sum) {
-      uint32_t cum = hi_cnt;
-#pragma unroll
-      for (int j = NB / BLOCK - 1; j >= 0; --j) {
-        if (cum + h[j] >= K) {
-          s.sel_bin = t * (NB / BLOCK) + j;
-          s.sel_above = cum;
-          break;
-        }
-        cum += h[j];
+      for (int j = 0; j < NB / BLOCK; ++j) {
+        h[j] = r->hist[t * (NB / BLOCK) + j];
+        sum += h[j];
+        s.hist[t * (NB / BLOCK) + j] = h[j];
       }
-    }
-    __syncthreads();
-    const uint32_t b = s.sel_bin, above = s.sel_above;
-    const uint32_t cb = s.hist[b];
-    const uint32_t lo = r->lo, hi = r->hi;
-    const uint32_t sh = shift_for(hi - lo);
-    const uint32_t braw = lo + (b << sh);
-    const uint32_t blo = (b == 0) ? 0u : braw;
-    const uint32_t wdt = (1u << sh) - 1u;
-    const uint32_t bhi = (b == (uint32_t)(NB - 1)) ? KEY_MAX
-                                                   : braw + ((KEY_MAX - braw) < wdt ? (KEY_MAX - braw) : wdt);
-    const bool fits = cb <= (uint32_t)CAP;
-    if (begin == 0 && t == 0) {  // one item per row records the bin for the finish kernel
-      r->bin_above = above;
-      r->bin_count = cb;
-      r->bin_lo = blo;
-      r->bin_hi = bhi;
+      uint32_t incl = wave_incl_scan(sum);
+      if (lane_id() == WAVE - 1) s.wtmp[w] = incl;
+      if (t == 0) {
+        s.sel_bin = 0;
+        s.sel_above = 0;
+      }
+      __syncthreads();
+      uint32_t before = 0, total = 0;
+#pragma unroll
+      for (int i = 0; i < NWAVES; ++i) {
+        const uint32_t v = s.wtmp[i];
+        before += ((uint32_t)i < w) ? v : 0u;
+        total += v;
+      }
+      incl += before;
+      const uint32_t hi_cnt = total - incl;
+      if (hi_cnt < K && K <= hi_cnt + sum) {
+        uint32_t cum = hi_cnt;
+#pragma unroll
+        for (int j = NB / BLOCK - 1; j >= 0; --j) {
+          if (cum + h[j] >= K) {
+            s.sel_bin = t * (NB / BLOCK) + j;
+            s.sel_above = cum;
+            break;
+          }
+          cum += h[j];
+        }
+      }
+      __syncthreads();
+      const uint32_t b = s.sel_bin, above = s.sel_above;
+      const uint32_t cb = s.hist[b];
+      const uint32_t lo = r->lo, hi = r->hi;
+      const uint32_t sh = shift_for(hi - lo);
+      const uint32_t braw = lo + (b << sh);
+      blo = (b == 0) ? 0u : braw;
+      const uint32_t wdt = (1u << sh) - 1u;
+      bhi = (b == (uint32_t)(NB - 1)) ? KEY_MAX : braw + ((KEY_MAX - braw) < wdt ? (KEY_MAX - braw) : wdt);
+      fits = cb <= (uint32_t)CAP;
+      if (begin == 0 && t == 0) {  // one item per row records the bin for the finish kernel
+        r->bin_above = above;
+        r->bin_count = cb;
+        r->bin_lo = blo;
+        r->bin_hi = bhi;
+      }
     }
     const RowOut out = row_out(p, r->row);
     uint32_t na = 0, nb = 0;
@@ -1666,7 +1752,7 @@ __global__ __launch_bounds__(BLOCK) void recovery_collect_kernel(Params p) {
         const uint32_t o = g + i;
         const uint32_t k = key_of_bits(w4[i]);
         const bool ok = o >= off && o < off + n;
-        na += (ok && k > bhi) ? 1u : 0u;
+        na += (ok && commit && k > bhi) ? 1u : 0u;
         nb += (ok && fits && k >= blo && k <= bhi) ? 1u : 0u;
       }
     }
@@ -1704,7 +1790,7 @@ __global__ __launch_bounds__(BLOCK) void recovery_collect_kernel(Params p) {
         const uint32_t k = key_of_bits(w4[i]);
         const bool ok = o >= off && o < off + n;
         const uint32_t e = begin + o - off;  // element index in the row
-        if (ok && k > bhi) {
+        if (ok && commit && k > bhi) {
           if (pa < K) out.put(pa, e, k);
           ++pa;
         }
@@ -1732,7 +1818,9 @@ void recovery_finish_kernel(Params p) {
   for (uint32_t q = blockIdx.x; q < nq; q += gridDim.x) {
     RecSlot* r = p.rec + q;
     if (r->row >= p.M || r->L > p.N) continue;  // (a slot of a call that failed)
-    const uint32_t above = r->bin_above, cb = r->bin_count;
+    const bool window = r->mode == REC_WINDOW;
+    const uint32_t above = r->bin_above;
+    const uint32_t cb = window ? r->cnt : r->bin_count;  // (window: every key gathered, even past CAP)
     const uint32_t blo = r->bin_lo, bhi = r->bin_hi;
     const uint32_t need = K - above;
     const uint32_t L = r->L;
@@ -1743,7 +1831,13 @@ void recovery_finish_kernel(Params p) {
       s.out_tie = 0;
     }
     uint32_t T, gt2;
-    if (cb <= (uint32_t)FL_CAP) {
+    if (window && cb < need) {
+      // The window [tau2, tau1) of an underfilled row held fewer keys than it still
+      // needs: the exact full-row select over the row, by this workgroup (it rewrites
+      // every output slot).
+      if (t == 0) stat_add(p.ctl, TOPK_STAT_INPLACE_FULL);
+      exact_full_row(x, L, K, r->lo, r->hi, out, p.ctl);
+    } else if (cb <= (uint32_t)FL_CAP) {
       if (t < cb) {
         s.fl_idx[t] = r->cand_idx[t];
         s.fl_key[t] = r->cand_key[t];
@@ -2010,13 +2104,21 @@ void split_finish_kernel(Params p) {
           thr = overflow_threshold(p.K, t1key, shift_for(smax - t1key), n_ge);
         }
         recover_in_place(x, L, p.K, n_ge <= (uint32_t)CAP ? thr : 0u, smax, t1key, smax, out, p.ctl);
+      } else if (t1key != 0u) {
+        reset_row_state();
+        for (uint32_t b = t; b < (uint32_t)NB; b += BLOCK) s.hist[b] = rs->hist[b];
+        __syncthreads();
+        queue_overflow(p, row, x, L, t1key, shift_for(smax - t1key), smax, out);
       } else {
-        recover_row(p, row, x, L, t1key, smax, out);
+        // The lowest key (only a NaN pattern maps to it) admitted everything and the parts
+        // built no histogram: the exact full-row select, here.
+        recover_in_place(x, L, p.K, 0u, smax, t1key, smax, out, p.ctl);
       }
     } else if (c1 < p.K) {
       if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_UNDER);
       if (L <= p.inplace_max) recover_in_place(x, L, p.K, t2key, smax, smin, t1key, out, p.ctl);
-      else recover_row(p, row, x, L, smin, t1key, out);
+      else queue_underfill(p, row, x, L, c1, t1key, t2key, smin, (const GLB uint32_t*)rs->cand_idx,
+                           (const GLB uint32_t*)rs->cand_key, out);
     } else {
       if (t == 0) stat_add(p.ctl, c0 >= p.K ? TOPK_STAT_TAU0 : TOPK_STAT_TAU1);
       // The merged histogram and candidates move to LDS with all loads issued first.
@@ -2571,9 +2673,13 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
   const int64_t rec_rows = M < (int64_t)st->qmax ? M : (int64_t)st->qmax;
   const int64_t rec_items = rec_rows * ((N_alloc + REC_SEG - 1) / REC_SEG);
   const unsigned rec_grid = (unsigned)(rec_items < (int64_t)st->n_cu * 4 ? rec_items : (int64_t)st->n_cu * 4);
-  hipLaunchKernelGGL(recovery_hist_kernel, dim3(rec_grid), dim3(BLOCK), 0, stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess && rc == TOPK_OK) rc = hip_fail(e, "launch recovery_hist_kernel");
+  // Only forced recovery queues rows with nothing known about their K-th key; every
+  // other queued row comes with the window its own pass located, and needs no histogram.
+  if (p.mode == TOPK_PATH_RECOVERY) {
+    hipLaunchKernelGGL(recovery_hist_kernel, dim3(rec_grid), dim3(BLOCK), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess && rc == TOPK_OK) rc = hip_fail(e, "launch recovery_hist_kernel");
+  }
   hipLaunchKernelGGL(recovery_collect_kernel, dim3(rec_grid), dim3(BLOCK), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess && rc == TOPK_OK) rc = hip_fail(e, "launch recovery_collect_kernel");
