@@ -2553,15 +2553,29 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
   p.N = (uint32_t)N_alloc;
   p.K = (uint32_t)K;
   p.sentinel = sentinel;
-  // Targets ceil(rho * K) with rho in thousandths: 1.5 K and 1.75 K by default.
-  p.T0 = (uint32_t)(((int64_t)g_rho0.load() * K + 999) / 1000);
-  p.T1 = (uint32_t)(((int64_t)g_rho1.load() * K + 999) / 1000);
-  // In-place recovery threshold of an underfilled row: a deeper sample rank, about 2.9 K
-  // admitted keys at K = 2048 (halfway from T1 to the buffer, at most 3 K). After an
+  // Targets ceil(rho * K) with rho in thousandths: 1.5 K and 1.75 K by default (3072 and
+  // 3584 at K = 2048). Away from that operating point they are bounded: at least 12 and
+  // 16 samples' worth (a sample rank below that estimates its quantile too coarsely:
+  // 5% of 128K rows underfilled at K = 512 with tau1 at rank 7), and at most 5/8 and 3/4
+  // of the candidate buffer (the spread of C(tau1) is about 1/sqrt(rank) of it: at
+  // K = 4096, 1.75 K = 7168 overflowed 8192 slots in 17% of 1M rows).
+  {
+    const int64_t s_ = g_stride.load();
+    int64_t t0 = ((int64_t)g_rho0.load() * K + 999) / 1000, t1 = ((int64_t)g_rho1.load() * K + 999) / 1000;
+    t0 = t0 < 12 * s_ ? 12 * s_ : t0;
+    t1 = t1 < 16 * s_ ? 16 * s_ : t1;
+    t0 = t0 > 5 * CAP / 8 ? 5 * CAP / 8 : t0;
+    t1 = t1 > 3 * CAP / 4 ? 3 * CAP / 4 : t1;
+    p.T0 = (uint32_t)t0;
+    p.T1 = (uint32_t)(t1 > t0 ? t1 : t0);
+  }
+  // Recovery threshold of an underfilled row: a deeper sample rank, about 2.9 K admitted
+  // keys at K = 2048 (halfway from T1 to the buffer, at most max(3 K, 2 T1)). After an
   // underfill at tau1 the row holds about C(tau1) + (r2 - r1) L / n_s keys above it.
   {
-    const uint32_t t2 = (p.T1 + (uint32_t)CAP) / 2u < 3u * (uint32_t)K ? (p.T1 + (uint32_t)CAP) / 2u
-                                                                       : 3u * (uint32_t)K;
+    const uint32_t half = (p.T1 + (uint32_t)CAP) / 2u;
+    const uint32_t lim = 3u * (uint32_t)K > 2u * p.T1 ? 3u * (uint32_t)K : 2u * p.T1;
+    const uint32_t t2 = half < lim ? half : lim;
     p.T2 = t2 > p.T1 ? t2 : p.T1;
   }
   // Rows that need exact recovery and are short are recovered by their own workgroup
