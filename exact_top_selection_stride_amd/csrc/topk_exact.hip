@@ -96,7 +96,8 @@ constexpr int KEYS_CAP = 2 * CAP;     // keys-only capacity of the same region
 constexpr int FL_CAP = 512;           // frontier (index, key) pairs
 constexpr uint32_t FL_RANK_MAX = 64;  // frontiers up to this size are resolved by rank counting
 constexpr uint32_t STRIDE = 128;      // sample stride s
-constexpr int UNROLL = 4;             // 128-bit loads per thread per batch
+constexpr int UNROLL = 4;             // 128-bit loads per thread per batch (whole-row walks)
+constexpr int PASS_UNROLL = 6;        // 128-bit loads per lane per batch of the fused pass
 constexpr uint32_t DIRECT_MAX_DEFAULT = 16384;
 constexpr uint32_t QMAX = 256;        // rows queued for cooperative recovery per call (workspace)
 constexpr uint32_t REC_SEG = 16384;   // elements per recovery work item
@@ -191,6 +192,7 @@ struct alignas(16) Smem {
   uint32_t fl_cnt;
   uint32_t out_gt;             // output slots taken by keys above the threshold
   uint32_t out_tie;            // output slots taken by keys equal to the threshold
+  uint32_t pass_next;          // next batch of the full-row pass to claim
   uint32_t mn, mx;
   uint32_t sel_bin, sel_above;
   uint32_t bcast;              // block-wide broadcast of a value read by thread 0
@@ -554,6 +556,7 @@ __device__ __forceinline__ void reset_row_state() {
     s.fl_cnt = 0;
     s.out_gt = 0;
     s.out_tie = 0;
+    s.pass_next = 0;
     s.mn = KEY_MAX;
     s.mx = 0;
   }
@@ -782,18 +785,25 @@ __device__ __forceinline__ void admit_quad(const u32x4& v, uint32_t e, const Pas
 }
 
 // The mandatory full-row pass: certification counts, candidate compaction and the
-// first histogram, fused. The next batch of loads is issued before the current one
-// is examined so that each thread keeps 2 x UNROLL 128-bit loads in flight.
+// first histogram, fused. The row body is cut into batches of PASS_UNROLL 128-bit loads
+// per lane of one wave (6 KB); each wave claims its next batch from an LDS counter and
+// issues that batch's loads before it examines the current one, so it keeps up to
+// 2 x PASS_UNROLL loads in flight. Waves of a workgroup do not issue at the same rate (the
+// older ones are served first); claiming batches dynamically keeps every wave busy
+// until the row's last batch, where a fixed split of the row left the fast waves
+// waiting at the closing barrier while the slow ones finished their share with fewer
+// loads in flight. The counter s.pass_next is zeroed by reset_row_state.
 //
 // With SKIP, the row's sampled lines were read whole by the line sampler, and bit P
 // of the LDS bitmap s.fl_idx says whether the sampled line of period P (offsets
 // [128 P, 128 P + 32) from the 128-byte line below x, P < n_s) holds a key >= tau1.
 // Chunks of the other sampled lines are not loaded: none of their elements can be
-// admitted, so skipping them changes no result. The access pattern stays that of the
-// whole-row pass, with those lanes idle. The loads go through a buffer resource over
-// the row's body: a skipped chunk is given an offset past the resource's end, which
-// the hardware answers with zeros and no memory access. The loads stay unconditional
-// in the control flow, so the compiler can still wait for one batch at a time.
+// admitted, so skipping them changes no result. The loads go through a buffer resource
+// over the row's body: a skipped chunk is given an offset past the resource's end,
+// which the hardware answers with zeros and no memory access. The loads stay
+// unconditional in the control flow, so the compiler can still wait for one batch at
+// a time. Without SKIP, lanes past the body's end read its last chunk again (always
+// in bounds) and are masked.
 // x[0, L) may be a segment of a row whose element 0 is row element ebase (candidates
 // record row indices); with SKIP the segment must start on a sampled line, and P
 // counts periods from there.
@@ -802,6 +812,7 @@ __device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, uint32_t n_s, c
                                            uint32_t ebase = 0u) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
+  const uint32_t l = lane_id();
   uint32_t c0l = 0;
   uint32_t head = (uint32_t)((4u - ((uint32_t)((uintptr_t)x >> 2) & 3u)) & 3u);
   if (head > L) head = L;
@@ -809,65 +820,91 @@ __device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, uint32_t n_s, c
   const uint32_t nv = (L - head) >> 2;
   grow_t body = x + head;
   const uint32_t gb = ((uint32_t)((uintptr_t)x & 127u) >> 2) + head;  // body offset from the line below x
-  const uint32_t per = BLOCK * UNROLL;
-  const uint32_t nfull = nv / per;
-  // Raw buffer over the body (16 nv bytes; rows on this path are at most a few MB).
-  // Word 3 is the gfx9-family buffer format word; the load's cache policy 2 is "nt".
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)body, (short)0, (int)(16u * nv), 0x00020000);
-  // Loads chunk q; `inert` receives the value to OR into it before it is examined
-  // (never_admitted for a skipped chunk, which reads as zeros, else 0). Applying it
-  // at examination rather than here keeps the compiler from waiting for the
-  // prefetched batch, and keeps the load itself unconditional (no branch around it).
-  auto fetch = [&](uint32_t q, uint32_t& inert) -> u32x4 {
+  constexpr uint32_t PERW = WAVE * PASS_UNROLL;  // quads per wave batch
+  static_assert(4 * PERW / 128 + 1 + 31 < 64, "a batch's periods lie within two bitmap words");
+  const uint32_t nb = (nv + PERW - 1u) / PERW;
+  // Raw buffer over the body (16 nv bytes; rows with SKIP are at most 8192 sample
+  // periods long). Word 3 is the gfx9-family buffer format word; the load's cache
+  // policy 2 is "nt".
+  // The base and size are the same in every lane; reading them from the first lane
+  // puts the resource in scalar registers (otherwise each load is wrapped in a loop
+  // over the distinct resource values).
+  const uint64_t bp = (uint64_t)(uintptr_t)body;
+  const uint32_t bp_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bp);
+  const uint32_t bp_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(bp >> 32));
+  const int nrec = __builtin_amdgcn_readfirstlane(SKIP ? (int)(16u * nv) : 0);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(uintptr_t)(((uint64_t)bp_hi << 32) | bp_lo), (short)0, nrec, 0x00020000);
+  // Loads batch b; inert[u] receives the value to OR into chunk u before it is
+  // examined (never_admitted for a skipped or past-the-end chunk, else 0). Applying it
+  // at examination rather than here keeps the compiler from waiting for the prefetched
+  // batch, and keeps the loads themselves unconditional (no branch around them). The
+  // batch's periods lie within two bitmap words, read once per batch.
+  auto fetch = [&](uint32_t b, u32x4 (&v)[PASS_UNROLL], uint32_t (&inert)[PASS_UNROLL]) {
+    const uint32_t q0 = b * PERW;
+    uint64_t hot = 0;
+    uint32_t p0 = 0;
     if (SKIP) {
-      const uint32_t g = gb + 4u * q;
-      const uint32_t P = g >> 7;
-      const uint32_t w = s.fl_idx[(P >> 5) & (uint32_t)(FL_CAP - 1)];
-      const bool cold = ((g >> 5) & 3u) == 0u && P < n_s && ((w >> (P & 31u)) & 1u) == 0u;
-      inert = cold ? never_admitted<POS>() : 0u;
-      return __builtin_amdgcn_raw_buffer_load_b128(rsrc, cold ? 0xFFFFFFF0u : 16u * q, 0, 2);
+      const uint32_t w0 = (gb + 4u * q0) >> 12;  // bitmap word of the batch's first period
+      hot = (uint64_t)s.fl_idx[w0 & (uint32_t)(FL_CAP - 1)] |
+            ((uint64_t)s.fl_idx[(w0 + 1u) & (uint32_t)(FL_CAP - 1)] << 32);
+      p0 = 32u * w0;
     }
-    inert = 0u;
-    return load4_stream(body + 4u * q);
-  };
-  auto examine = [&](const u32x4 (&raw)[UNROLL], const uint32_t (&inert)[UNROLL], uint32_t it) {
-    u32x4 v[UNROLL];
-    uint32_t e[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      v[u] = SKIP ? (raw[u] | splat4(inert[u])) : raw[u];
-      e[u] = ebase + head + 4u * (it * per + u * BLOCK + t);
+    for (int u = 0; u < PASS_UNROLL; ++u) {
+      const uint32_t q = q0 + (uint32_t)u * WAVE + l;
+      const bool past = q >= nv;
+      if (SKIP) {
+        const uint32_t g = gb + 4u * q;
+        const uint32_t P = g >> 7;
+        const bool cold = ((g >> 5) & 3u) == 0u && P < n_s && ((hot >> (P - p0)) & 1u) == 0u;
+        const bool off = past | cold;
+        inert[u] = off ? never_admitted<POS>() : 0u;
+        v[u] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off ? 0xFFFFFFF0u : 16u * q, 0, 2);
+      } else {
+        inert[u] = past ? never_admitted<POS>() : 0u;
+        v[u] = load4_stream(body + 4u * (past ? nv - 1u : q));
+      }
     }
-    admit_batch<POS, UNROLL>(v, e, c, c0l);
   };
-  if (nfull > 0) {
-    // The prefetch is unconditional inside the loop (the last batch is peeled) so
-    // the compiler waits only for the batch being examined, not for the next one.
-    u32x4 a[UNROLL];
-    uint32_t am[UNROLL];
+  auto claim = [&]() -> uint32_t {
+    uint32_t v = 0;
+    if (l == 0) v = atomicAdd(&s.pass_next, 1u);
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+  };
+  auto examine = [&](const u32x4 (&raw)[PASS_UNROLL], const uint32_t (&inert)[PASS_UNROLL], uint32_t b) {
+    u32x4 v[PASS_UNROLL];
+    uint32_t e[PASS_UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) a[u] = fetch(u * BLOCK + t, am[u]);
-    uint32_t it = 0;
-    for (; it + 1 < nfull; ++it) {
-      u32x4 nx[UNROLL];
-      uint32_t nm[UNROLL];
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) nx[u] = fetch((it + 1) * per + u * BLOCK + t, nm[u]);
+    for (int u = 0; u < PASS_UNROLL; ++u) {
+      v[u] = raw[u] | splat4(inert[u]);
+      e[u] = ebase + head + 4u * (b * PERW + (uint32_t)u * WAVE + l);
+    }
+    admit_batch<POS, PASS_UNROLL>(v, e, c, c0l);
+  };
+  uint32_t b = claim();
+  if (b < nb) {
+    u32x4 a[PASS_UNROLL];
+    uint32_t am[PASS_UNROLL];
+    fetch(b, a, am);
+    for (;;) {
+      const uint32_t bn = claim();
+      if (bn >= nb) {
+        examine(a, am, b);
+        break;
+      }
+      u32x4 nx[PASS_UNROLL];
+      uint32_t nm[PASS_UNROLL];
+      fetch(bn, nx, nm);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the examination
-      examine(a, am, it);
+      examine(a, am, b);
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
+      for (int u = 0; u < PASS_UNROLL; ++u) {
         a[u] = nx[u];
         am[u] = nm[u];
       }
+      b = bn;
     }
-    examine(a, am, it);
-  }
-  for (uint32_t q = nfull * per + t; q < nv; q += BLOCK) {
-    uint32_t inert;
-    const u32x4 v = fetch(q, inert);
-    admit_quad<POS>(v | splat4(inert), ebase + head + 4u * q, c, c0l);
   }
   const uint32_t tail0 = head + 4u * nv;
   if (t < L - tail0) admit_one<POS>(true, x[tail0 + t], ebase + tail0 + t, c, c0l);
