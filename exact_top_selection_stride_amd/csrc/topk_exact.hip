@@ -2369,9 +2369,92 @@ int stream_capturing(hipStream_t stream, bool* capturing) {
 // entries keep the sentinel and get -inf. Entries are 64-bit composites
 // (key << 32 | ~index), never 0 for a valid entry (indices are below 2^31), so the zero
 // padding sorts last. The order comes from a bitonic network over P = EPT * BLOCK
-// entries, thread t holding entries t*EPT .. t*EPT+EPT-1: exchange distances below EPT
-// stay in registers, those below one wave's share go through cross-lane shuffles, and
-// only the few larger ones go through LDS with barriers.
+// entries, thread t holding entries t*EPT .. t*EPT+EPT-1. Every stage is a separate
+// instantiation with its run length and exchange distance known at compile time:
+// distances below EPT stay in registers, those up to 32 EPT go across the lanes of a wave
+// (see lane_xor64), and the larger ones (across waves) through LDS, double-buffered so
+// that each such stage needs one barrier.
+
+// Exchange of a 64-bit value with lane ^ M. The network is bound by vector ALU issue, so
+// only the one-instruction quad permutes (M = 1, 2) use DPP; M = 4, 8, 16 go through the
+// LDS crossbar's swizzle (bit mode: lane ^ M within groups of 32) and M = 32 through a
+// permute, both issued to the LDS pipe instead of the vector ALU.
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor_lds(uint32_t v) {
+  if constexpr (M <= 2) return lane_xor<M>(v);
+  else if constexpr (M <= 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (M << 10) | 0x1F);
+  else return (uint32_t)__shfl_xor((int)v, M);
+}
+template <int M>
+__device__ __forceinline__ uint64_t lane_xor64(uint64_t v) {
+  const uint32_t lo = lane_xor_lds<M>((uint32_t)v), hi = lane_xor_lds<M>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Stage (KB, J): runs of 2^KB entries, exchange distance J. An entry e meets e ^ J; the
+// lower entry of the pair keeps the larger value where bit KB of e is clear.
+template <int EPT, int KB, uint32_t J>
+__device__ __forceinline__ void sort_stage(uint64_t (&v)[EPT], uint32_t t, uint64_t (*c)[EPT * BLOCK],
+                                           int& buf) {
+  constexpr uint32_t K = 1u << KB;
+  if constexpr (J < (uint32_t)EPT) {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      if (((uint32_t)q & J) == 0u) {
+        const int r = q | (int)J;
+        const bool desc = ((t * EPT + (uint32_t)q) & K) == 0u;
+        const uint64_t x = v[q], y = v[r];
+        // One compare: with x == y swapping changes nothing, so "y > x" may stand for
+        // "x < y" and its negation for "x > y".
+        const bool swap = (y > x) == desc;
+        v[q] = swap ? y : x;
+        v[r] = swap ? x : y;
+      }
+    }
+  } else {
+    constexpr uint32_t M = J / EPT;  // partner thread t ^ M, same register slot
+    const bool lo = (t & M) == 0u;
+    const bool desc = ((t * EPT) & K) == 0u;  // K >= J >= EPT: the same for every slot
+    const bool keep_max = desc == lo;
+    if constexpr (M < (uint32_t)WAVE) {
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) {
+        const uint64_t p = lane_xor64<(int)M>(v[q]);
+        v[q] = ((p > v[q]) == keep_max) ? p : v[q];  // equal values: either is the result
+      }
+    } else {
+      uint64_t* cb = c[buf];
+      buf ^= 1;
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) cb[t * EPT + (uint32_t)q] = v[q];
+      __syncthreads();
+      const uint32_t pt = t ^ M;
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) {
+        const uint64_t p = cb[pt * EPT + (uint32_t)q];
+        v[q] = ((p > v[q]) == keep_max) ? p : v[q];
+      }
+    }
+  }
+}
+
+// Every stage of runs of 2^KB, distances J, J / 2, ..., 1.
+template <int EPT, int KB, uint32_t J>
+__device__ __forceinline__ void sort_merge(uint64_t (&v)[EPT], uint32_t t, uint64_t (*c)[EPT * BLOCK], int& buf) {
+  sort_stage<EPT, KB, J>(v, t, c, buf);
+  if constexpr (J > 1u) sort_merge<EPT, KB, J / 2>(v, t, c, buf);
+}
+
+// Runs of 2^KB, 2^(KB+1), ..., P.
+template <int EPT, int KB>
+__device__ __forceinline__ void sort_levels(uint64_t (&v)[EPT], uint32_t t, uint64_t (*c)[EPT * BLOCK], int& buf) {
+  constexpr uint32_t P = (uint32_t)EPT * BLOCK;
+  if constexpr ((1u << KB) <= P) {
+    sort_merge<EPT, KB, (1u << KB) / 2>(v, t, c, buf);
+    sort_levels<EPT, KB + 1>(v, t, c, buf);
+  }
+}
+
 template <int EPT>
 __global__ __launch_bounds__(BLOCK) void sort_rows_kernel(const float* __restrict__ scores,
                                                           const int32_t* __restrict__ row_len,
@@ -2379,7 +2462,7 @@ __global__ __launch_bounds__(BLOCK) void sort_rows_kernel(const float* __restric
                                                           int32_t* __restrict__ out_idx,
                                                           float* out_val, int32_t sentinel) {
   constexpr uint32_t P = (uint32_t)EPT * BLOCK;
-  __shared__ uint64_t c[P];
+  __shared__ uint64_t c[2][P];
   const uint32_t row = blockIdx.x, t = threadIdx.x;
   const int32_t len = row_len[row];
   uint32_t L = len < 0 ? 0u : (uint32_t)len;
@@ -2392,72 +2475,68 @@ __global__ __launch_bounds__(BLOCK) void sort_rows_kernel(const float* __restric
   // rows: the first L scores of the row, in order).
   const uint32_t* kin = (out_val != nullptr && L > K) ? reinterpret_cast<const uint32_t*>(out_val) + (size_t)row * K
                                                       : nullptr;
+  float* val = out_val ? out_val + (size_t)row * K : nullptr;
+  // Groups of four entries go through 16-byte loads and stores where the row's index,
+  // key and value slots are 16-byte aligned and the group is entirely valid.
+  const bool vec = (EPT % 4 == 0) && kin != nullptr &&
+                   ((reinterpret_cast<uintptr_t>(o) | reinterpret_cast<uintptr_t>(kin)) & 15u) == 0u;
   uint64_t v[EPT];
 #pragma unroll
-  for (int q = 0; q < EPT; ++q) {
-    const uint32_t e = t * EPT + (uint32_t)q;
-    v[q] = 0;
-    if (e < n) {
-      // The selector wrote an index in [0, L) here; the clamp only keeps reads in bounds.
-      const uint32_t i = (uint32_t)o[e] < L ? (uint32_t)o[e] : 0u;
-      const uint32_t k = kin != nullptr ? kin[e] : key_of_bits(x[i]);
-      v[q] = ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - i);
+  for (int g = 0; g < EPT; g += 4) {
+    const uint32_t e0 = t * EPT + (uint32_t)g;
+    if (EPT % 4 == 0 && vec && e0 + 3u < n) {
+      const u32x4 iv = *reinterpret_cast<const u32x4*>(o + e0);
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(kin + e0);
+      v[g] = ((uint64_t)kv.x << 32) | (uint64_t)(0xFFFFFFFFu - iv.x);
+      v[g + 1] = ((uint64_t)kv.y << 32) | (uint64_t)(0xFFFFFFFFu - iv.y);
+      v[g + 2] = ((uint64_t)kv.z << 32) | (uint64_t)(0xFFFFFFFFu - iv.z);
+      v[g + 3] = ((uint64_t)kv.w << 32) | (uint64_t)(0xFFFFFFFFu - iv.w);
+      continue;
     }
-  }
-  __syncthreads();  // every key of the row is read before any thread overwrites out_val
-  // Bitonic network: for each (k, j) every entry e meets e ^ j; a run is descending where
-  // bit k of e is clear, and the lower entry of a pair keeps the larger value there.
-  for (uint32_t k = 2; k <= P; k <<= 1) {
-    for (uint32_t j = k >> 1; j > 0; j >>= 1) {
-      if (j < (uint32_t)EPT) {
 #pragma unroll
-        for (int q = 0; q < EPT; ++q) {
-          if (((uint32_t)q & j) == 0) {
-            const int r = q | (int)j;
-            const bool desc = ((t * EPT + (uint32_t)q) & k) == 0;
-            const uint64_t a = v[q], b = v[r];
-            if (desc ? (a < b) : (a > b)) {
-              v[q] = b;
-              v[r] = a;
-            }
-          }
-        }
-      } else {
-        const uint32_t m = j / EPT;  // partner thread t ^ m, same register slot
-        const bool lo = (t & m) == 0;
-        if (m < (uint32_t)WAVE) {
-#pragma unroll
-          for (int q = 0; q < EPT; ++q) {
-            const uint64_t p = __shfl_xor(v[q], (int)m);
-            const bool desc = ((t * EPT + (uint32_t)q) & k) == 0;
-            v[q] = (desc == lo) ? (v[q] > p ? v[q] : p) : (v[q] < p ? v[q] : p);
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < EPT; ++q) c[t * EPT + (uint32_t)q] = v[q];
-          __syncthreads();
-#pragma unroll
-          for (int q = 0; q < EPT; ++q) {
-            const uint64_t p = c[(t * EPT + (uint32_t)q) ^ j];
-            const bool desc = ((t * EPT + (uint32_t)q) & k) == 0;
-            v[q] = (desc == lo) ? (v[q] > p ? v[q] : p) : (v[q] < p ? v[q] : p);
-          }
-          __syncthreads();
-        }
+    for (int q = g; q < g + 4 && q < EPT; ++q) {
+      const uint32_t e = t * EPT + (uint32_t)q;
+      v[q] = 0;
+      if (e < n) {
+        // The selector wrote an index in [0, L) here; the clamp only keeps reads in bounds.
+        const uint32_t i = (uint32_t)o[e] < L ? (uint32_t)o[e] : 0u;
+        const uint32_t k = kin != nullptr ? kin[e] : key_of_bits(x[i]);
+        v[q] = ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - i);
       }
     }
   }
-  float* val = out_val ? out_val + (size_t)row * K : nullptr;
+  __syncthreads();  // every key of the row is read before any thread overwrites out_val
+  int buf = 0;
+  sort_levels<EPT, 1>(v, t, c, buf);
+  const bool vec_out = vec && val != nullptr && (reinterpret_cast<uintptr_t>(val) & 15u) == 0u;
+  auto value_of = [](uint32_t key) { return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key); };
 #pragma unroll
-  for (int q = 0; q < EPT; ++q) {
-    const uint32_t e = t * EPT + (uint32_t)q;
-    if (e < n) {
-      const uint32_t key = (uint32_t)(v[q] >> 32);
-      o[e] = (int32_t)(0xFFFFFFFFu - (uint32_t)v[q]);
-      if (val) val[e] = __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
-    } else if (e < K) {
-      o[e] = sentinel;
-      if (val) val[e] = -__builtin_inff();
+  for (int g = 0; g < EPT; g += 4) {
+    const uint32_t e0 = t * EPT + (uint32_t)g;
+    if (EPT % 4 == 0 && vec_out && e0 + 3u < n) {
+      u32x4 iv, fv;
+      iv.x = 0xFFFFFFFFu - (uint32_t)v[g];
+      iv.y = 0xFFFFFFFFu - (uint32_t)v[g + 1];
+      iv.z = 0xFFFFFFFFu - (uint32_t)v[g + 2];
+      iv.w = 0xFFFFFFFFu - (uint32_t)v[g + 3];
+      fv.x = __float_as_uint(value_of((uint32_t)(v[g] >> 32)));
+      fv.y = __float_as_uint(value_of((uint32_t)(v[g + 1] >> 32)));
+      fv.z = __float_as_uint(value_of((uint32_t)(v[g + 2] >> 32)));
+      fv.w = __float_as_uint(value_of((uint32_t)(v[g + 3] >> 32)));
+      *reinterpret_cast<u32x4*>(o + e0) = iv;
+      *reinterpret_cast<u32x4*>(val + e0) = fv;
+      continue;
+    }
+#pragma unroll
+    for (int q = g; q < g + 4 && q < EPT; ++q) {
+      const uint32_t e = t * EPT + (uint32_t)q;
+      if (e < n) {
+        o[e] = (int32_t)(0xFFFFFFFFu - (uint32_t)v[q]);
+        if (val) val[e] = value_of((uint32_t)(v[q] >> 32));
+      } else if (e < K) {
+        o[e] = sentinel;
+        if (val) val[e] = -__builtin_inff();
+      }
     }
   }
 }
