@@ -100,7 +100,9 @@ constexpr int UNROLL = 4;             // 128-bit loads per thread per batch (who
 constexpr int PASS_UNROLL = 6;        // 128-bit loads per lane per batch of the fused pass
 constexpr uint32_t DIRECT_MAX_DEFAULT = 16384;
 constexpr uint32_t QMAX = 256;        // rows queued for cooperative recovery per call (workspace)
-constexpr uint32_t REC_SEG = 16384;   // elements per recovery work item
+constexpr uint32_t REC_SEG = 16384;   // elements per recovery work item (rows wider than 256K)
+constexpr uint32_t REC_SEG_SHORT = 4096;  // ... and for rows of up to 256K
+constexpr int64_t REC_SHORT_MAX_N = 262144;
 constexpr uint32_t INPLACE_MAX = 65536;        // rows up to this length are recovered in place,
 constexpr uint32_t INPLACE_MAX_SPLIT = 262144; // ... and up to this one in row-split calls
 constexpr int64_t ROWSPLIT_MIN_N = 65536;  // auto row-split only for rows at least this wide
@@ -1612,7 +1614,9 @@ void topk_rows_kernel(Params p) {
 // order the three steps, so no cross-workgroup fences are needed. All three exit
 // at once when the queue is empty; the finish kernel's last workgroup rewinds it.
 
-constexpr int REC_CHUNKS = REC_SEG / 4 / BLOCK + 1;  // 16-byte chunks per thread per item
+// 16-byte chunks per thread per work item of SEG elements.
+template <uint32_t SEG>
+constexpr int rec_chunks() { return (int)(SEG / 4 / BLOCK + 1); }
 
 struct RecHistSmem {
   uint32_t hist[NB];
@@ -1620,19 +1624,21 @@ struct RecHistSmem {
 __shared__ RecHistSmem g_rh;  // the histogram kernel's LDS state
 
 
+template <uint32_t SEG>
 __global__ __launch_bounds__(BLOCK) void recovery_hist_kernel(Params p) {
+  constexpr int REC_CHUNKS = rec_chunks<SEG>();
   const uint32_t t = threadIdx.x;
   const uint32_t nq = min(p.ctl->qcount, p.qmax);
-  const uint32_t per_row = (p.N + REC_SEG - 1) / REC_SEG;
+  const uint32_t per_row = (p.N + SEG - 1) / SEG;
   const uint32_t items = nq * per_row;
   for (uint32_t item = blockIdx.x; item < items; item += gridDim.x) {
     const uint32_t q = item / per_row;
-    const uint32_t begin = (item - q * per_row) * REC_SEG;
+    const uint32_t begin = (item - q * per_row) * SEG;
     RecSlot* r = p.rec + q;
     const uint32_t L = r->L;
     if (begin >= L || r->row >= p.M || L > p.N) continue;  // (a slot of a call that failed)
     if (r->mode != REC_HIST) continue;                     // the row's own pass located its bin
-    const uint32_t n = min(REC_SEG, L - begin);
+    const uint32_t n = min(SEG, L - begin);
     const uint32_t lo = r->lo, hi = r->hi;
     const uint32_t sh = shift_for(hi - lo);
     // The whole item is loaded at once (one memory latency per item): offsets are in
@@ -1684,20 +1690,22 @@ struct RecCollectSmem {
 
 __shared__ RecCollectSmem g_rc;
 
+template <uint32_t SEG>
 __global__ __launch_bounds__(BLOCK) void recovery_collect_kernel(Params p) {
+  constexpr int REC_CHUNKS = rec_chunks<SEG>();
   RecCollectSmem& s = g_rc;
   const uint32_t t = threadIdx.x;
   const uint32_t K = p.K;
   const uint32_t nq = min(p.ctl->qcount, p.qmax);
-  const uint32_t per_row = (p.N + REC_SEG - 1) / REC_SEG;
+  const uint32_t per_row = (p.N + SEG - 1) / SEG;
   const uint32_t items = nq * per_row;
   for (uint32_t item = blockIdx.x; item < items; item += gridDim.x) {
     const uint32_t q = item / per_row;
-    const uint32_t begin = (item - q * per_row) * REC_SEG;
+    const uint32_t begin = (item - q * per_row) * SEG;
     RecSlot* r = p.rec + q;
     const uint32_t L = r->L;
     if (begin >= L || r->row >= p.M || L > p.N) continue;  // (a slot of a call that failed)
-    const uint32_t n = min(REC_SEG, L - begin);
+    const uint32_t n = min(SEG, L - begin);
     // The item stays in registers; its loads are issued first so that they overlap
     // the boundary-bin search below. Then this thread's keys above the bin and in
     // the bin are counted, the item's output and candidate slots are reserved with
@@ -2801,16 +2809,23 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
   // correspondingly small grids.
   if ((int64_t)p.inplace_max >= N_alloc) return rc;
   const int64_t rec_rows = M < (int64_t)st->qmax ? M : (int64_t)st->qmax;
-  const int64_t rec_items = rec_rows * ((N_alloc + REC_SEG - 1) / REC_SEG);
+  // Work items of 4K elements for rows of up to 256K (more workgroups on the few items of
+  // a short row: 512 x 128K 99 -> 94 us per call), of 16K for longer rows (fewer items each
+  // workgroup walks in turn: 4K items cost 8192 x 1M rows about 20 us more).
+  const bool short_items = N_alloc <= REC_SHORT_MAX_N;
+  const int64_t seg = short_items ? REC_SEG_SHORT : REC_SEG;
+  const int64_t rec_items = rec_rows * ((N_alloc + seg - 1) / seg);
   const unsigned rec_grid = (unsigned)(rec_items < (int64_t)st->n_cu * 4 ? rec_items : (int64_t)st->n_cu * 4);
   // Only forced recovery queues rows with nothing known about their K-th key; every
   // other queued row comes with the window its own pass located, and needs no histogram.
   if (p.mode == TOPK_PATH_RECOVERY) {
-    hipLaunchKernelGGL(recovery_hist_kernel, dim3(rec_grid), dim3(BLOCK), 0, stream, p);
+    if (short_items) hipLaunchKernelGGL(recovery_hist_kernel<REC_SEG_SHORT>, dim3(rec_grid), dim3(BLOCK), 0, stream, p);
+    else hipLaunchKernelGGL(recovery_hist_kernel<REC_SEG>, dim3(rec_grid), dim3(BLOCK), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess && rc == TOPK_OK) rc = hip_fail(e, "launch recovery_hist_kernel");
   }
-  hipLaunchKernelGGL(recovery_collect_kernel, dim3(rec_grid), dim3(BLOCK), 0, stream, p);
+  if (short_items) hipLaunchKernelGGL(recovery_collect_kernel<REC_SEG_SHORT>, dim3(rec_grid), dim3(BLOCK), 0, stream, p);
+  else hipLaunchKernelGGL(recovery_collect_kernel<REC_SEG>, dim3(rec_grid), dim3(BLOCK), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess && rc == TOPK_OK) rc = hip_fail(e, "launch recovery_collect_kernel");
   const int64_t fin_cap = (int64_t)st->n_cu * st->occ_rec;
