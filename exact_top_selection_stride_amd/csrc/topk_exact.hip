@@ -172,6 +172,7 @@ struct Params {
   struct RowSplitState* rs;  // per-row state of the row-split kernels
   uint32_t ps;          // row-split: workgroups per row sampling
   uint32_t pp;          // row-split: workgroups per row passing
+  uint32_t pass_taus;   // row-split: each passing workgroup selects the row's taus itself
   unsigned long long* phase;  // per-row phase record (PHASE_WORDS per row), or null
   uint32_t* okey;       // [M][K] selected keys beside out (sorted output), or null
 };
@@ -2067,14 +2068,41 @@ void split_pass_kernel(Params p) {
   if (rs->whole) return;
   const uint32_t L = row_length(p, row);
   const uint32_t n_s = (L + STRIDE - 1) / STRIDE;
-  const uint32_t t1key = rs->t1key;
+  uint32_t t0key, t1key;
+  if (p.pass_taus) {
+    // The taus from the whole sample, in every part (no separate select launch); part 0
+    // records them for the finish.
+    uint32_t v[LM_PER_THREAD];
+#pragma unroll
+    for (int m = 0; m < LM_PER_THREAD; ++m) {
+      const uint32_t i = t + (uint32_t)m * BLOCK;
+      v[m] = i < n_s ? rs->skey[i] : 0u;
+    }
+#pragma unroll
+    for (int m = 0; m < LM_PER_THREAD; ++m) {
+      const uint32_t i = t + (uint32_t)m * BLOCK;
+      if (i < n_s) s.buf[i] = v[m];
+    }
+    __syncthreads();
+    uint32_t t2key;
+    select_taus(n_s, sample_rank(p.T0, n_s, L), sample_rank(p.T1, n_s, L), sample_rank(p.T2, n_s, L),
+                ~rs->mn_inv, rs->mx, t0key, t1key, t2key);
+    if (part == 0 && t == 0) {
+      rs->t1key = t1key;
+      rs->t0key = t0key;
+      rs->t2key = t2key;
+    }
+  } else {
+    t1key = rs->t1key;
+    t0key = rs->t0key;
+  }
   if (t1key == 0u) {
     // Every key is admitted at the lowest threshold: count the row as overflowing
     // so that it is recovered exactly.
     if (part == 0 && t == 0) atomicAdd(&rs->c1, (uint32_t)CAP + 1u);
     return;
   }
-  const PassCtx c = pass_ctx(t1key, rs->t0key, rs->mx);
+  const PassCtx c = pass_ctx(t1key, t0key, rs->mx);
   grow_t x = (grow_t)(p.scores) + (size_t)row * p.N;
   // This part covers the sample periods [q0, q1): row elements [e0, e1), where period
   // P starts at offset 128 P from the 128-byte line below x (the last part runs to the
@@ -2719,6 +2747,7 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
   p.okey = okey;
   p.ps = 1;
   p.pp = 1;
+  p.pass_taus = 0;
   // Execution by shape. Row-split when rows are few and long: their scan and
   // sampling are divided among several workgroups. Measured on MI355X (512 resident
   // slots, graph replays): for rows of 1M, row-split takes 44-62 us for 1-32 rows
@@ -2780,8 +2809,14 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
     p.pp = (uint32_t)(pp < pp_cap ? pp : pp_cap);
     p.ps = (uint32_t)(ps < ps_cap ? ps : ps_cap);
     p.rs = st->rs;
+    // When the passing grid fits in one round of resident workgroups, each of them
+    // selects its row's taus from the sample (a few microseconds, overlapped across the
+    // grid) instead of waiting for a select kernel: 1-16 rows of 128K and 1 row of 1M
+    // gain 1.0-1.6 us, 64 rows of 128K 0.7 us. A larger grid repeats that work in later
+    // rounds, and 64 rows of 1M lose 6 us with it.
+    p.pass_taus = (int64_t)p.pp * M <= resident ? 1u : 0u;
     hipLaunchKernelGGL(split_sample_kernel, dim3(p.ps, (unsigned)M), dim3(BLOCK), 0, stream, p);
-    hipLaunchKernelGGL(split_select_kernel, dim3((unsigned)M), dim3(BLOCK), 0, stream, p);
+    if (!p.pass_taus) hipLaunchKernelGGL(split_select_kernel, dim3((unsigned)M), dim3(BLOCK), 0, stream, p);
     hipLaunchKernelGGL(split_pass_kernel, dim3(p.pp, (unsigned)M), dim3(BLOCK), 0, stream, p);
     hipLaunchKernelGGL(split_finish_kernel, dim3((unsigned)M), dim3(BLOCK), 0, stream, p);
     e = hipGetLastError();
