@@ -2811,9 +2811,10 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
     p.rs = st->rs;
     // When the passing grid fits in one round of resident workgroups, each of them
     // selects its row's taus from the sample (a few microseconds, overlapped across the
-    // grid) instead of waiting for a select kernel: 1-16 rows of 128K and 1 row of 1M
-    // gain 1.0-1.6 us, 64 rows of 128K 0.7 us. A larger grid repeats that work in later
-    // rounds, and 64 rows of 1M lose 6 us with it.
+    // grid) instead of waiting for a select kernel. Measured on MI355X (selector kernels,
+    // graph replays): 1-16 rows of 128K and 1-4 rows of 1M gain 1.1-1.6 us, 64 rows of
+    // 128K and 16 rows of 1M 0.6-0.9 us. A larger grid repeats that work in later rounds,
+    // and 64 rows of 1M lose 6 us with it.
     p.pass_taus = (int64_t)p.pp * M <= resident ? 1u : 0u;
     hipLaunchKernelGGL(split_sample_kernel, dim3(p.ps, (unsigned)M), dim3(BLOCK), 0, stream, p);
     if (!p.pass_taus) hipLaunchKernelGGL(split_select_kernel, dim3((unsigned)M), dim3(BLOCK), 0, stream, p);
