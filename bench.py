@@ -478,7 +478,7 @@ def run_chain(args):
 
 
 PATH_NAMES = {1: "sentinel", 2: "direct", 3: "tau0", 4: "tau1", 5: "recover_inplace", 6: "recover_queued",
-              7: "forced_recovery"}
+              7: "forced_recovery", 8: "tau_a"}
 
 
 def phase_summary(records, khz):

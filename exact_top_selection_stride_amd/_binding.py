@@ -39,7 +39,7 @@ EXEC_ROWSPLIT = 3
 STAT_NAMES = (
     "rows", "sentinel", "direct", "sampled", "tau0", "tau1", "recover_under", "recover_over",
     "rowsplit", "forced_recovery", "long_exact", "frontier_wide", "queued", "persistent", "row_per_wg",
-    "recover_inplace", "inplace_certified", "inplace_full",
+    "recover_inplace", "inplace_certified", "inplace_full", "tau_a",
 )
 STAT_COUNT = 24
 
@@ -48,7 +48,7 @@ EXPORTED = (
     "topk_exact_set_path_override", "topk_exact_last_error", "topk_stream_read_probe",
     "topk_exact_set_execution", "topk_exact_time_next_call", "topk_exact_set_proposal",
     "topk_indexer_scores", "topk_indexer_topk", "topk_exact_sorted", "topk_exact_noalloc",
-    "topk_exact_record_phases",
+    "topk_exact_record_phases", "topk_exact_set_admission",
 )
 
 
@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.topk_exact_set_execution.argtypes = [ctypes.c_int]
         L.topk_exact_set_proposal.restype = ctypes.c_int
         L.topk_exact_set_proposal.argtypes = [i32, i32, i32]
+        L.topk_exact_set_admission.restype = ctypes.c_int
+        L.topk_exact_set_admission.argtypes = [i32]
         L.topk_exact_time_next_call.restype = ctypes.c_int
         L.topk_exact_time_next_call.argtypes = [vp, vp]
         L.topk_exact_record_phases.restype = ctypes.c_int
@@ -277,6 +279,21 @@ def proposal(stride: int = 128, rho0: float = 1.5, rho1: float = 1.75):
         _check(lib().topk_exact_set_proposal(0, 0, 0), "topk_exact_set_proposal")
 
 
+def set_admission(rho_a: float = 2.25):
+    """Admission target rho_a*K of rows sampled one element per period (0 turns the deeper
+    admission off: every row admits at tau1). Any setting gives an exact result."""
+    _check(lib().topk_exact_set_admission(int(round(rho_a * 1000))), "topk_exact_set_admission")
+
+
+@contextlib.contextmanager
+def admission(rho_a: float = 2.25):
+    set_admission(rho_a)
+    try:
+        yield
+    finally:
+        _check(lib().topk_exact_set_admission(-1), "topk_exact_set_admission")
+
+
 def time_next_call(start, stop):
     """Arms the one-shot selector timing of the next topk_exact call on this thread.
 
@@ -296,7 +313,7 @@ def time_next_call(start, stop):
 PHASE_WORDS = 8
 PHASE_NAMES = ("start", "sampled", "proposed", "passed", "end", "recovered", "where", "counts")
 PATH_CODES = {1: "sentinel", 2: "direct", 3: "tau0", 4: "tau1", 5: "recover_inplace", 6: "recover_queued",
-              7: "forced_recovery"}
+              7: "forced_recovery", 8: "tau_a"}
 
 
 def record_phases(buf: Optional[torch.Tensor]) -> int:

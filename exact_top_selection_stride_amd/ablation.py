@@ -159,12 +159,14 @@ def main(argv=None):
         # up to 16K, above that the sampled path with element-wise sampling (line
         # sampling, which the forced sampled path uses at stride 128, is reserved for
         # the longest rows).
-        settings = [("direct", 128, 1.5, 1.75), ("auto", 128, 1.5, 1.75)]
-        settings += [("sampled", s, r, r + 0.25) for s in args.strides for r in args.rho0]
+        # rho_a: the admission target of element-sampled rows (0: admission at tau1, the
+        # pages' design; the library's default admits down to 2.25 K).
+        settings = [("direct", 128, 1.5, 1.75, 2.25), ("auto", 128, 1.5, 1.75, 2.25), ("auto", 128, 1.5, 1.75, 0.0)]
+        settings += [("sampled", s, r, r + 0.25, 2.25) for s in args.strides for r in args.rho0]
         paths = {"direct": tk.PATH_DIRECT, "auto": tk.PATH_AUTO, "sampled": tk.PATH_SAMPLED}
-        for mode, stride, rho0, rho1 in settings:
+        for mode, stride, rho0, rho1, rho_a in settings:
             path = paths[mode]
-            with tk.path_override(path), tk.proposal(stride, rho0, rho1):
+            with tk.path_override(path), tk.proposal(stride, rho0, rho1), tk.admission(rho_a):
                 tk.reset_stats()
                 for g, (s, l) in enumerate(groups):
                     tk.topk_exact(s, l, K=K, out=outs[g])
@@ -173,9 +175,9 @@ def main(argv=None):
                 ms = _time_call(groups, outs, K, args.steps, stream)
             rows = max(st["rows"], 1)
             print(json.dumps({
-                "workload": w.name, "mode": mode, "stride": stride, "rho0": rho0, "rho1": rho1,
+                "workload": w.name, "mode": mode, "stride": stride, "rho0": rho0, "rho1": rho1, "rho_a": rho_a,
                 "median_call_ms": round(ms, 5), "rows_per_s": round(w.M / ms * 1e3),
-                "tau0_rate": st["tau0"] / rows, "tau1_rate": st["tau1"] / rows,
+                "tau0_rate": st["tau0"] / rows, "tau1_rate": st["tau1"] / rows, "tau_a_rate": st["tau_a"] / rows,
                 "recovery_rate": (st["recover_under"] + st["recover_over"]) / rows,
                 "long_exact_rate": st["long_exact"] / rows,
             }), flush=True)

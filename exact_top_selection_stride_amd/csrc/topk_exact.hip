@@ -162,6 +162,7 @@ struct Params {
   uint32_t T0;          // primary candidate target, ceil(1.5 K) by default
   uint32_t T1;          // secondary candidate target, ceil(1.75 K) by default
   uint32_t T2;          // threshold for in-place recovery of underfilled rows (a deeper target)
+  uint32_t TA;          // admission target of element-sampled rows (T1 <= TA <= T2)
   uint32_t inplace_max; // rows up to this length needing exact recovery are recovered in place
   uint32_t stride;      // sample stride s, 128 by default
   uint32_t line_min;    // sampled rows with at least this many sample lines use line sampling
@@ -191,7 +192,8 @@ struct alignas(16) Smem {
   uint32_t fl_key[FL_CAP];
   uint32_t wtmp[NWAVES];
   uint32_t cnt;                // admitted / collected count
-  uint32_t cnt0;               // admitted keys >= tau0
+  uint32_t cnt0;               // admitted keys >= tau0 (counted from the list after the pass)
+  uint32_t cnt1;               // admitted keys >= tau1 (likewise)
   uint32_t fl_cnt;
   uint32_t out_gt;             // output slots taken by keys above the threshold
   uint32_t out_tie;            // output slots taken by keys equal to the threshold
@@ -199,6 +201,7 @@ struct alignas(16) Smem {
   uint32_t mn, mx;
   uint32_t sel_bin, sel_above;
   uint32_t bcast;              // block-wide broadcast of a value read by thread 0
+  uint32_t bcast2;
   int32_t row;
 };
 
@@ -268,6 +271,7 @@ __device__ __forceinline__ uint32_t wave_reserve_n(uint32_t cnt, uint32_t* count
 // lists of up to 16384 entries.
 constexpr int LIST_BITS = 6;
 static_assert((KEYS_CAP + BLOCK - 1) / BLOCK < (1 << LIST_BITS), "per-thread list counts fit LIST_BITS");
+static_assert(CAP < 0x10000, "two per-wave counts of admitted keys share one word");
 
 // Cross-lane steps through DPP (GFX9 family controls): row_shr:n moves each lane's value
 // n lanes up within its row of 16; row_bcast:15 / row_bcast:31 pass lane 15 / 31 on to
@@ -370,16 +374,16 @@ constexpr int PHASE_WORDS = 8;
 enum : int {
   PH_START = 0,      // the row's workgroup starts on it
   PH_SAMPLED = 1,    // sample read, min/max known
-  PH_PROPOSED = 2,   // tau0 / tau1 / tau2 selected
+  PH_PROPOSED = 2,   // tau0 / tau1 / tau_a / tau2 selected
   PH_PASSED = 3,     // fused full-row pass done
   PH_END = 4,        // committed, or handed to the recovery kernels
   PH_RECOVERED = 5,  // exact recovery done (in place, or by the recovery finish kernel)
   PH_WHERE = 6,      // path code | XCC id << 8 | hardware wave id << 32
-  PH_COUNTS = 7,     // C(tau1) | C(tau0) << 32
+  PH_COUNTS = 7,     // C(tau1) | C(tau0) << 32 (the admitted count alone past the buffer)
 };
 enum : uint32_t {
   PATH_SENTINEL = 1, PATH_DIRECT = 2, PATH_TAU0 = 3, PATH_TAU1 = 4, PATH_RECOVER_INPLACE = 5,
-  PATH_RECOVER_QUEUED = 6, PATH_FORCED_RECOVERY = 7, PATH_SPLIT_FLAG = 0x80,
+  PATH_RECOVER_QUEUED = 6, PATH_FORCED_RECOVERY = 7, PATH_TAUA = 8, PATH_SPLIT_FLAG = 0x80,
 };
 
 __device__ __forceinline__ void phase_put(unsigned long long* ph, uint32_t row, int slot, unsigned long long v) {
@@ -556,6 +560,7 @@ __device__ __forceinline__ void reset_row_state() {
   if (t == 0) {
     s.cnt = 0;
     s.cnt0 = 0;
+    s.cnt1 = 0;
     s.fl_cnt = 0;
     s.out_gt = 0;
     s.out_tie = 0;
@@ -695,28 +700,26 @@ __device__ __forceinline__ void direct_exact(grow_t x, uint32_t L, uint32_t K, R
 
 struct PassCtx {
   uint32_t thr;    // raw-bit admission threshold (see admits)
-  uint32_t t1key;  // key(tau1): admitted keys are >= it
-  uint32_t t0key;  // key(tau0)
+  uint32_t akey;   // admission key (tau1, or the deeper admission rank): admitted keys are >= it
   uint32_t sh;     // first-histogram shift
 };
 
-// key(u) >= key(tau1), evaluated on raw bits: for tau1 >= +0 it is a signed compare
-// against tau1's bits, for tau1 <= -0 an unsigned <= against tau1's bits.
+// key(u) >= the admission key, evaluated on raw bits: for a threshold >= +0 it is a
+// signed compare against its bits, for one <= -0 an unsigned <= against its bits.
 template <bool POS>
 __device__ __forceinline__ bool admits(uint32_t u, uint32_t thr) {
   return POS ? ((int32_t)u >= (int32_t)thr) : (u <= thr);
 }
 
-// A value that never passes admits<POS> (tau1 key != 0 is required for NEG).
+// A value that never passes admits<POS> (an admission key != 0 is required for NEG).
 template <bool POS>
 constexpr uint32_t never_admitted() { return POS ? 0x80000000u : 0xFFFFFFFFu; }
 
 // Candidate formation for one element slot across the wave: ballot, one LDS atomic
-// per wave for the base slot, prefix count for each lane's slot, histogram update
-// and this lane's tau0 count. Every active lane of the wave must reach it.
+// per wave for the base slot, prefix count for each lane's slot and histogram update.
+// Every active lane of the wave must reach it.
 template <bool POS>
-__device__ __forceinline__ void admit_one(bool valid, uint32_t u, uint32_t e, const PassCtx c,
-                                          uint32_t& c0l) {
+__device__ __forceinline__ void admit_one(bool valid, uint32_t u, uint32_t e, const PassCtx c) {
   Smem& s = g_s;
   const bool pred = valid && admits<POS>(u, c.thr);
   const uint64_t m = __ballot(pred);
@@ -731,9 +734,8 @@ __device__ __forceinline__ void admit_one(bool valid, uint32_t u, uint32_t e, co
       s.buf[pos] = e;
       s.buf[CAP + pos] = k;
     }
-    const uint32_t d = (k - c.t1key) >> c.sh;
+    const uint32_t d = (k - c.akey) >> c.sh;
     atomicAdd(&s.hist[d < (uint32_t)(NB - 1) ? d : (uint32_t)(NB - 1)], 1u);
-    c0l += k >= c.t0key ? 1u : 0u;
   }
 }
 
@@ -744,8 +746,7 @@ __device__ __forceinline__ void admit_one(bool valid, uint32_t u, uint32_t e, co
 // then writes its candidates to consecutive slots. Every active lane of the wave must
 // reach it.
 template <bool POS, int NQ>
-__device__ __forceinline__ void admit_batch(const u32x4 (&v)[NQ], const uint32_t (&e)[NQ], const PassCtx c,
-                                            uint32_t& c0l) {
+__device__ __forceinline__ void admit_batch(const u32x4 (&v)[NQ], const uint32_t (&e)[NQ], const PassCtx c) {
   Smem& s = g_s;
   constexpr int NBITS = 32 - __builtin_clz(4u * NQ);  // bits of a count in [0, 4 NQ]
   uint32_t n = 0;
@@ -765,9 +766,8 @@ __device__ __forceinline__ void admit_batch(const u32x4 (&v)[NQ], const uint32_t
         s.buf[pos] = idx;
         s.buf[CAP + pos] = k;
       }
-      const uint32_t d = (k - c.t1key) >> c.sh;
+      const uint32_t d = (k - c.akey) >> c.sh;
       atomicAdd(&s.hist[d < (uint32_t)(NB - 1) ? d : (uint32_t)(NB - 1)], 1u);
-      c0l += k >= c.t0key ? 1u : 0u;
       ++pos;
     }
   };
@@ -781,10 +781,10 @@ __device__ __forceinline__ void admit_batch(const u32x4 (&v)[NQ], const uint32_t
 }
 
 template <bool POS>
-__device__ __forceinline__ void admit_quad(const u32x4& v, uint32_t e, const PassCtx c, uint32_t& c0l) {
+__device__ __forceinline__ void admit_quad(const u32x4& v, uint32_t e, const PassCtx c) {
   const u32x4 vv[1] = {v};
   const uint32_t ee[1] = {e};
-  admit_batch<POS, 1>(vv, ee, c, c0l);
+  admit_batch<POS, 1>(vv, ee, c);
 }
 
 // The mandatory full-row pass: certification counts, candidate compaction and the
@@ -816,10 +816,9 @@ __device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, uint32_t n_s, c
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   const uint32_t l = lane_id();
-  uint32_t c0l = 0;
   uint32_t head = (uint32_t)((4u - ((uint32_t)((uintptr_t)x >> 2) & 3u)) & 3u);
   if (head > L) head = L;
-  if (t < head) admit_one<POS>(true, x[t], ebase + t, c, c0l);
+  if (t < head) admit_one<POS>(true, x[t], ebase + t, c);
   const uint32_t nv = (L - head) >> 2;
   grow_t body = x + head;
   const uint32_t gb = ((uint32_t)((uintptr_t)x & 127u) >> 2) + head;  // body offset from the line below x
@@ -883,7 +882,7 @@ __device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, uint32_t n_s, c
       v[u] = raw[u] | splat4(inert[u]);
       e[u] = ebase + head + 4u * (b * PERW + (uint32_t)u * WAVE + l);
     }
-    admit_batch<POS, PASS_UNROLL>(v, e, c, c0l);
+    admit_batch<POS, PASS_UNROLL>(v, e, c);
   };
   uint32_t b = claim();
   if (b < nb) {
@@ -910,8 +909,27 @@ __device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, uint32_t n_s, c
     }
   }
   const uint32_t tail0 = head + 4u * nv;
-  if (t < L - tail0) admit_one<POS>(true, x[tail0 + t], ebase + tail0 + t, c, c0l);
-  if (c0l != 0) atomicAdd(&s.cnt0, c0l);
+  if (t < L - tail0) admit_one<POS>(true, x[tail0 + t], ebase + tail0 + t, c);
+}
+
+// After a pass that admitted n <= CAP keys: the admitted keys >= k0 and >= k1, read
+// from the list in LDS, in s.cnt0 and s.cnt1 (zeroed by reset_row_state). Counting
+// here rather than in the pass keeps two instructions per examined slot out of the
+// pass, which is short of vector ALU time on rows of 128K. Ends with a barrier.
+__device__ __forceinline__ void count_admitted(uint32_t n, uint32_t k0, uint32_t k1) {
+  Smem& s = g_s;
+  // Both counts in one word (each at most CAP per wave), summed over the wave.
+  uint32_t ab = 0;
+  for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
+    const uint32_t k = s.buf[CAP + i];
+    ab += (k >= k0 ? 1u : 0u) + (k >= k1 ? 0x10000u : 0u);
+  }
+  ab = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(ab), WAVE - 1);
+  if (lane_id() == 0 && ab != 0) {
+    atomicAdd(&s.cnt0, ab & 0xFFFFu);
+    atomicAdd(&s.cnt1, ab >> 16);
+  }
+  __syncthreads();
 }
 
 // ------------------------------------------------ line-granular sampling
@@ -1166,15 +1184,14 @@ __device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t bas
 // After a certified sampled pass: n = C(tau1) <= CAP candidates in LDS with the first
 // histogram over (key - key(tau1)) >> sh.
 __device__ __forceinline__ void refine_commit(uint32_t n, uint32_t K, const PassCtx c, RowOut out, Control* ctl) {
-  refine_list<false>(n, K, c.t1key, c.sh, out, ctl);
+  refine_list<false>(n, K, c.akey, c.sh, out, ctl);
 }
 
-__device__ __forceinline__ PassCtx pass_ctx(uint32_t t1key, uint32_t t0key, uint32_t smax) {
+__device__ __forceinline__ PassCtx pass_ctx(uint32_t akey, uint32_t smax) {
   PassCtx c;
-  c.t1key = t1key;
-  c.t0key = t0key;
-  c.sh = shift_for(smax - t1key);
-  c.thr = t1key >= 0x80000000u ? (t1key ^ 0x80000000u) : ~t1key;
+  c.akey = akey;
+  c.sh = shift_for(smax - akey);
+  c.thr = akey >= 0x80000000u ? (akey ^ 0x80000000u) : ~akey;
   return c;
 }
 
@@ -1194,7 +1211,7 @@ __device__ __attribute__((noinline)) void recover_in_place(grow_t x, uint32_t L,
   if (threadIdx.x == 0) stat_add(ctl, TOPK_STAT_RECOVER_INPLACE);
   if (thr != 0u) {
     reset_row_state();
-    const PassCtx c = pass_ctx(thr, thr, smax > thr ? smax : thr);
+    const PassCtx c = pass_ctx(thr, smax > thr ? smax : thr);
     if (thr >= 0x80000000u) fused_pass<true, false>(x, L, 0u, c);
     else fused_pass<false, false>(x, L, 0u, c);
     __syncthreads();
@@ -1321,14 +1338,14 @@ __device__ __forceinline__ void recover_row(const Params& p, uint32_t row, grow_
   }
 }
 
-// tau1, tau0 and tau2: the r1-th, r0-th and r2-th largest (r0 <= r1 <= r2) of the n_s
-// sample keys in s.buf[0, n_s), all inside [mn, mx]. One radix round finds the bin
-// holding rank r2; when the keys in that bin and above fit the frontier buffer (the
-// usual case, r2 is a few dozen), the three ranks are read off by counting inside that
-// short list. Otherwise the general narrowing selection runs.
-__device__ __forceinline__ void select_taus(uint32_t n_s, uint32_t r0, uint32_t r1, uint32_t r2, uint32_t mn,
-                                            uint32_t mx, uint32_t& t0key, uint32_t& t1key, uint32_t& t2key,
-                                            bool hist_is_zero = false) {
+// tau1, tau0, taua and tau2: the r1-th, r0-th, ra-th and r2-th largest
+// (r0 <= r1 <= ra <= r2) of the n_s sample keys in s.buf[0, n_s), all inside [mn, mx].
+// One radix round finds the bin holding rank r2; when the keys in that bin and above fit
+// the frontier buffer (the usual case, r2 is a few dozen), the four ranks are read off by
+// counting inside that short list. Otherwise the general narrowing selection runs.
+__device__ __forceinline__ void select_taus(uint32_t n_s, uint32_t r0, uint32_t r1, uint32_t ra, uint32_t r2,
+                                            uint32_t mn, uint32_t mx, uint32_t& t0key, uint32_t& t1key,
+                                            uint32_t& takey, uint32_t& t2key, bool hist_is_zero = false) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   const uint32_t sh = shift_for(mx - mn);
@@ -1365,15 +1382,18 @@ __device__ __forceinline__ void select_taus(uint32_t n_s, uint32_t r0, uint32_t 
       const uint32_t srt = wave_sort_desc(l < m ? s.fl_key[l] : 0u);
       t1key = (uint32_t)__builtin_amdgcn_readlane((int)srt, (int)(r1 - 1));
       t0key = (uint32_t)__builtin_amdgcn_readlane((int)srt, (int)(r0 - 1));
+      takey = (uint32_t)__builtin_amdgcn_readlane((int)srt, (int)(ra - 1));
       t2key = (uint32_t)__builtin_amdgcn_readlane((int)srt, (int)(r2 - 1));
     } else {
       const uint32_t rk = rank_in_list(s.fl_key, m);
       if (rk == r1 - 1) s.sel_above = s.fl_key[t];
       if (rk == r0 - 1) s.sel_bin = s.fl_key[t];
+      if (rk == ra - 1) s.bcast2 = s.fl_key[t];
       if (rk == r2 - 1) s.bcast = s.fl_key[t];
       __syncthreads();
       t1key = s.sel_above;
       t0key = s.sel_bin;
+      takey = s.bcast2;
       t2key = s.bcast;
       __syncthreads();
     }
@@ -1388,6 +1408,12 @@ __device__ __forceinline__ void select_taus(uint32_t n_s, uint32_t r0, uint32_t 
     select_rank([&](auto&& f) {
       for (uint32_t i = threadIdx.x; i < n_s; i += BLOCK) f(g_s.buf[i]);
     }, r0, t1key, mx, t0key, unused);
+    takey = t1key;
+    if (ra != r1) {
+      select_rank([&](auto&& f) {
+        for (uint32_t i = threadIdx.x; i < n_s; i += BLOCK) f(g_s.buf[i]);
+      }, ra, t2key, mx, takey, unused);
+    }
   }
 }
 
@@ -1455,22 +1481,27 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
   const uint32_t r1 = sample_rank(p.T1, n_s, L);
   const uint32_t r0 = sample_rank(p.T0, n_s, L);
   const uint32_t r2 = sample_rank(p.T2, n_s, L);
-  uint32_t t1key, t0key, t2key;
+  // Rows sampled one element per period admit keys down to the deeper sample rank ra
+  // (target T_A): their C(tau1) spreads by about 1/sqrt(r1) around T1 and falls short of
+  // K in a few rows per thousand, each of which would need one more read of the row,
+  // while C(tau_a) almost never falls short of K or exceeds the buffer. C(tau0) and
+  // C(tau1) are then counted among the admitted keys, so each row still reports the
+  // threshold that certifies it. Line-sampled rows (32 keys per period, a far narrower
+  // spread) admit at tau1, on which their line skipping is built.
+  const uint32_t ra = by_lines ? r1 : sample_rank(p.TA, n_s, L);
+  uint32_t t1key, t0key, takey, t2key;
   // The histogram and list counters are still zero from the row's reset (the sample does
   // not touch them).
-  select_taus(n_s, r0, r1, r2, smin, smax, t0key, t1key, t2key, true);
+  select_taus(n_s, r0, r1, ra, r2, smin, smax, t0key, t1key, takey, t2key, true);
   phase_mark(p.phase, row, PH_PROPOSED);
 
-  PassCtx c;
-  c.t1key = t1key;
-  c.t0key = t0key;
-  c.sh = shift_for(smax - t1key);
-  const bool pos = t1key >= 0x80000000u;
-  c.thr = pos ? (t1key ^ 0x80000000u) : ~t1key;
+  const uint32_t akey = takey;  // tau1 when ra = r1
+  const PassCtx c = pass_ctx(akey, smax);
+  const bool pos = akey >= 0x80000000u;
   // Skipping sampled lines needs a value that is never admitted, which exists
-  // unless tau1 is the lowest possible key.
-  const bool skip = by_lines && t1key != 0u;
-  if (skip) write_hot_bitmap(&s.buf[CAP], n_s, t1key);
+  // unless the admission key is the lowest possible key.
+  const bool skip = by_lines && akey != 0u;
+  if (skip) write_hot_bitmap(&s.buf[CAP], n_s, akey);
   reset_row_state();  // its barrier also ends every read of the line maxima in LDS
   if (skip) {
     if (pos) fused_pass<true, true>(x, L, n_s, c);
@@ -1481,45 +1512,54 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
     fused_pass<false, false>(x, L, n_s, c);
   }
   __syncthreads();
-  const uint32_t c1 = s.cnt, c0 = s.cnt0;
+  const uint32_t n = s.cnt;
   phase_mark(p.phase, row, PH_PASSED);
+  uint32_t c0 = 0, c1 = n;
+  if (n <= (uint32_t)CAP) {
+    count_admitted(n, t0key, t1key);
+    c0 = s.cnt0;
+    c1 = s.cnt1;
+  }
   phase_put(p.phase, row, PH_COUNTS, (unsigned long long)c1 | ((unsigned long long)c0 << 32));
-  if (c1 > (uint32_t)CAP) {
-    // Too many admitted to hold: the K-th key is >= tau1, recover exactly. A short row
-    // is recovered in place from the boundary bin of the pass histogram, a long one by
-    // the cooperative recovery kernels.
+  if (n > (uint32_t)CAP) {
+    // Too many admitted to hold: the K-th key is >= the admission key, recover exactly.
+    // A short row is recovered in place from the boundary bin of the pass histogram, a
+    // long one by the cooperative recovery kernels.
     if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_OVER);
     if (L <= p.inplace_max) {
       uint32_t n_ge;
-      const uint32_t thr = overflow_threshold(p.K, t1key, c.sh, n_ge);
+      const uint32_t thr = overflow_threshold(p.K, akey, c.sh, n_ge);
       phase_mark(p.phase, row, PH_END);
-      recover_in_place(x, L, p.K, n_ge <= (uint32_t)CAP ? thr : 0u, smax, t1key, smax, out, p.ctl);
+      recover_in_place(x, L, p.K, n_ge <= (uint32_t)CAP ? thr : 0u, smax, akey, smax, out, p.ctl);
       phase_mark(p.phase, row, PH_RECOVERED);
       phase_path(p.phase, row, PATH_RECOVER_INPLACE);
     } else {
-      queue_overflow(p, row, x, L, t1key, c.sh, smax, out);
+      queue_overflow(p, row, x, L, akey, c.sh, smax, out);
       phase_mark(p.phase, row, PH_END);
       phase_path(p.phase, row, PATH_RECOVER_QUEUED);
     }
-  } else if (c1 < p.K) {
-    // Even the nested threshold underfills: the K-th key is < tau1. A short row is
+  } else if (n < p.K) {
+    // Even the admission threshold underfills: the K-th key is below it. A short row is
     // recovered in place from the deeper sample rank tau2, a long one cooperatively.
     if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_UNDER);
     phase_mark(p.phase, row, PH_END);
     if (L <= p.inplace_max) {
-      recover_in_place(x, L, p.K, t2key, smax, smin, t1key, out, p.ctl);
+      recover_in_place(x, L, p.K, t2key, smax, smin, akey, out, p.ctl);
       phase_mark(p.phase, row, PH_RECOVERED);
       phase_path(p.phase, row, PATH_RECOVER_INPLACE);
     } else {
-      queue_underfill(p, row, x, L, c1, t1key, t2key, smin, (const uint32_t*)&s.buf[0], (const uint32_t*)&s.buf[CAP],
+      queue_underfill(p, row, x, L, n, akey, t2key, smin, (const uint32_t*)&s.buf[0], (const uint32_t*)&s.buf[CAP],
                       out);
       phase_path(p.phase, row, PATH_RECOVER_QUEUED);
     }
   } else {
-    if (t == 0) stat_add(p.ctl, c0 >= p.K ? TOPK_STAT_TAU0 : TOPK_STAT_TAU1);
-    refine_commit(c1, p.K, c, out, p.ctl);
+    const uint32_t path = c0 >= p.K ? PATH_TAU0 : (c1 >= p.K ? PATH_TAU1 : PATH_TAUA);
+    if (t == 0) {
+      stat_add(p.ctl, path == PATH_TAU0 ? TOPK_STAT_TAU0 : (path == PATH_TAU1 ? TOPK_STAT_TAU1 : TOPK_STAT_TAUA));
+    }
+    refine_commit(n, p.K, c, out, p.ctl);
     phase_mark(p.phase, row, PH_END);
-    phase_path(p.phase, row, c0 >= p.K ? PATH_TAU0 : PATH_TAU1);
+    phase_path(p.phase, row, path);
   }
 }
 
@@ -2049,9 +2089,11 @@ void split_select_kernel(Params p) {
     if (i < n_s) s.buf[i] = v[m];
   }
   __syncthreads();
-  uint32_t t0key, t1key, t2key;
-  select_taus(n_s, sample_rank(p.T0, n_s, L), sample_rank(p.T1, n_s, L), sample_rank(p.T2, n_s, L), ~rs->mn_inv,
-              rs->mx, t0key, t1key, t2key);
+  // Line-sampled: the admission rank is tau1's.
+  const uint32_t r1 = sample_rank(p.T1, n_s, L);
+  uint32_t t0key, t1key, takey, t2key;
+  select_taus(n_s, sample_rank(p.T0, n_s, L), r1, r1, sample_rank(p.T2, n_s, L), ~rs->mn_inv, rs->mx, t0key, t1key,
+              takey, t2key);
   if (t == 0) {
     rs->t1key = t1key;
     rs->t0key = t0key;
@@ -2084,9 +2126,10 @@ void split_pass_kernel(Params p) {
       if (i < n_s) s.buf[i] = v[m];
     }
     __syncthreads();
-    uint32_t t2key;
-    select_taus(n_s, sample_rank(p.T0, n_s, L), sample_rank(p.T1, n_s, L), sample_rank(p.T2, n_s, L),
-                ~rs->mn_inv, rs->mx, t0key, t1key, t2key);
+    uint32_t takey, t2key;
+    const uint32_t r1 = sample_rank(p.T1, n_s, L);
+    select_taus(n_s, sample_rank(p.T0, n_s, L), r1, r1, sample_rank(p.T2, n_s, L), ~rs->mn_inv, rs->mx, t0key,
+                t1key, takey, t2key);
     if (part == 0 && t == 0) {
       rs->t1key = t1key;
       rs->t0key = t0key;
@@ -2102,7 +2145,7 @@ void split_pass_kernel(Params p) {
     if (part == 0 && t == 0) atomicAdd(&rs->c1, (uint32_t)CAP + 1u);
     return;
   }
-  const PassCtx c = pass_ctx(t1key, t0key, rs->mx);
+  const PassCtx c = pass_ctx(t1key, rs->mx);
   grow_t x = (grow_t)(p.scores) + (size_t)row * p.N;
   // This part covers the sample periods [q0, q1): row elements [e0, e1), where period
   // P starts at offset 128 P from the 128-byte line below x (the last part runs to the
@@ -2128,15 +2171,18 @@ void split_pass_kernel(Params p) {
     else fused_pass<false, true>(x + e0, e1 - e0, q1 - q0, c, e0);
   }
   __syncthreads();
-  // Merge into the row: one atomic reserves this workgroup's candidate range.
+  // Merge into the row: one atomic reserves this workgroup's candidate range. C(tau0) is
+  // counted among the part's listed keys (short of the truth only past the buffer, where
+  // the row overflows anyway).
   const uint32_t n = s.cnt;
+  const uint32_t keep = n < (uint32_t)CAP ? n : (uint32_t)CAP;
+  count_admitted(keep, t0key, t1key);
   if (t == 0) {
     s.bcast = n ? atomicAdd(&rs->c1, n) : 0u;
     if (s.cnt0) atomicAdd(&rs->c0, s.cnt0);
   }
   __syncthreads();
   const uint32_t base = s.bcast;
-  const uint32_t keep = n < (uint32_t)CAP ? n : (uint32_t)CAP;
   for (uint32_t i = t; i < keep; i += BLOCK) {
     if (base + i < (uint32_t)CAP) {
       rs->cand_idx[base + i] = s.buf[i];
@@ -2217,7 +2263,7 @@ void split_finish_kernel(Params p) {
         }
       }
       __syncthreads();
-      refine_commit(c1, p.K, pass_ctx(t1key, t0key, smax), out, p.ctl);
+      refine_commit(c1, p.K, pass_ctx(t1key, smax), out, p.ctl);
     }
     phase_mark(p.phase, row, PH_END);
     phase_put(p.phase, row, PH_COUNTS, (unsigned long long)c1 | ((unsigned long long)c0 << 32));
@@ -2307,6 +2353,7 @@ std::atomic<int> g_exec{TOPK_EXEC_AUTO};
 std::atomic<int> g_stride{(int)STRIDE};
 std::atomic<int> g_rho0{1500};
 std::atomic<int> g_rho1{1750};
+std::atomic<int> g_rhoa{2250};  // deeper admission target of element-sampled rows; 0: off
 // Per-row phase recording (measurement hook): device buffer and its row capacity.
 std::atomic<unsigned long long*> g_phase_buf{nullptr};
 std::atomic<int64_t> g_phase_rows{0};
@@ -2730,6 +2777,17 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
     const uint32_t t2 = half < lim ? half : lim;
     p.T2 = t2 > p.T1 ? t2 : p.T1;
   }
+  // Admission target of rows sampled one element per period: 2.25 K by default (4608 at
+  // K = 2048), used where it lies strictly between T1 and T2 and within 9/16 of the
+  // candidate buffer, else T1. For a row of exchangeable scores the chance that its
+  // admitted count falls short of K or exceeds the buffer (hypergeometric tails; 1024
+  // samples of 128K) is 3.7e-3 at T1 (rank 28) and 4e-5 at 4608 (rank 36) at K = 2048;
+  // at K >= 3000 no deeper rank lowers it, and 2.25 K passes the buffer bound there.
+  {
+    const int64_t ra = g_rhoa.load();
+    const int64_t ta = (ra * K + 999) / 1000;
+    p.TA = (ta > (int64_t)p.T1 && ta < (int64_t)p.T2 && ta <= 9 * CAP / 16) ? (uint32_t)ta : p.T1;
+  }
   // Rows that need exact recovery and are short are recovered by their own workgroup
   // with one more pass (at most 256 KB; 1 MB in row-split calls, which have few rows);
   // longer ones by the cooperative recovery kernels, which then run after the selector.
@@ -2776,6 +2834,15 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
                 (ex == TOPK_EXEC_AUTO && N_alloc >= ROWSPLIT_MIN_N &&
                  (N_alloc >= 4 * ROWSPLIT_MIN_N ? 4 * M <= resident : 8 * M <= resident)));
   p.inplace_max = g_mode.load() == TOPK_PATH_RECOVERY ? 0u : (split ? INPLACE_MAX_SPLIT : INPLACE_MAX);
+  // With the deeper admission, rows sampled one element per period (at stride 128 those
+  // with fewer than line_min sample periods) need exact recovery about once in 25000 rows
+  // of 128K, so they are recovered in place at any length: a call whose rows are all such
+  // rows launches no recovery kernels (512 x 128K: 86 -> 80 us per call), and the rare row
+  // that does recover streams its row once more on its own.
+  if (!split && p.inplace_max != 0u && p.TA > p.T1 && p.stride == STRIDE && p.line_min > 1u) {
+    const uint32_t elem_max = (p.line_min - 1u) * STRIDE;
+    if (elem_max > p.inplace_max) p.inplace_max = elem_max;
+  }
   hipError_t e;
   hipEvent_t ev_start = nullptr, ev_stop = nullptr;
   if (timing && g_time_start) {
@@ -3027,6 +3094,15 @@ int topk_exact_set_proposal(int32_t stride, int32_t rho0_permille, int32_t rho1_
   g_stride.store(stride);
   g_rho0.store(rho0_permille);
   g_rho1.store(rho1_permille);
+  return TOPK_OK;
+}
+
+int topk_exact_set_admission(int32_t rhoa_permille) {
+  g_err[0] = '\0';
+  if (rhoa_permille == -1) rhoa_permille = 2250;
+  if (rhoa_permille != 0 && (rhoa_permille < 1000 || rhoa_permille > 8000))
+    return fail(TOPK_ERR_BAD_ARG, "admission target %d (thousandths of K) needs -1, 0 or 1000..8000", rhoa_permille);
+  g_rhoa.store(rhoa_permille);
   return TOPK_OK;
 }
 

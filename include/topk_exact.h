@@ -81,7 +81,9 @@ enum {
   TOPK_STAT_SAMPLED = 3,         /* rows that took the sampled proposal */
   TOPK_STAT_TAU0 = 4,            /* sampled rows certified at tau0: C(tau0) >= K */
   TOPK_STAT_TAU1 = 5,            /* sampled rows with C(tau0) < K <= C(tau1) (nested fallback) */
-  TOPK_STAT_RECOVER_UNDER = 6,   /* sampled rows with C(tau1) < K: exact full-row recovery */
+  TOPK_STAT_RECOVER_UNDER = 6,   /* sampled rows whose admitted keys fall short of K (C(tau1) < K,
+                                    or C(tau_a) < K where the deeper admission applies): exact
+                                    recovery */
   TOPK_STAT_RECOVER_OVER = 7,    /* sampled rows whose candidates overflowed: exact recovery */
   TOPK_STAT_ROWSPLIT = 8,        /* rows scanned by several workgroups (row-split) */
   TOPK_STAT_FORCED_RECOVERY = 9, /* rows sent to exact recovery by TOPK_PATH_RECOVERY */
@@ -95,6 +97,9 @@ enum {
                                      262144 long, or past the cooperative queue's capacity) */
   TOPK_STAT_INPLACE_CERTIFIED = 16, /* of those: one more pass at a deeper threshold certified */
   TOPK_STAT_INPLACE_FULL = 17,   /* of those: the exact full-row select over the row ran */
+  TOPK_STAT_TAUA = 18,           /* element-sampled rows with C(tau1) < K <= C(tau_a): certified
+                                    at the deeper admission rank (see topk_exact_set_admission),
+                                    without a second read of the row */
   TOPK_STAT_COUNT = 24
 };
 
@@ -204,6 +209,21 @@ int topk_exact_set_execution(int mode);
  * 1 <= stride <= 65536 and 500 <= rho0 <= rho1 <= 4000. Process-wide; a captured graph
  * keeps the setting made before its capture. */
 int topk_exact_set_proposal(int32_t stride, int32_t rho0_permille, int32_t rho1_permille);
+
+/* Admission depth of rows whose sample is read one element per period (no passage
+ * defines it; it is this library's addition to the pages' tau0 / tau1 fallback, [Cx]
+ * section "采样不是处处都该开"). Such a row's single full pass admits every key at or
+ * above tau_a, the sample key of rank ceil(T_A n_s / L) with T_A = rho_a * K (thousandths
+ * of K), instead of stopping at tau1; C(tau0) and C(tau1) are counted among the admitted
+ * keys afterwards, so the statistics still name the threshold that certifies each row, and
+ * a row with C(tau1) < K <= C(tau_a) is finished without reading it again. T_A applies only
+ * where T1 < T_A < T2 and T_A <= 9/16 of the 8192-slot candidate buffer; elsewhere (and
+ * for line-sampled rows, whose sample is 32 keys per period) admission stays at tau1.
+ * rho_a = 0 turns the deeper admission off (every row admits at tau1, as on the pages);
+ * -1 restores the default 2250. Every setting gives an exact result. Returns
+ * TOPK_ERR_BAD_ARG unless rho_a is -1, 0 or in [1000, 8000]. Process-wide; a captured
+ * graph keeps the setting made before its capture. */
+int topk_exact_set_admission(int32_t rhoa_permille);
 
 /* Measurement hook (no passage defines it; it serves the per-kernel timing of the
  * roofline report beside the pages' per-call timing, [Cx] section "什么叫精确，时间怎么量"):

@@ -73,6 +73,13 @@ def test_argument_validation_without_gpu():
     assert L.topk_exact_set_proposal(128, 1500, 4001) == B.TOPK_ERR_BAD_ARG
     assert L.topk_exact_set_proposal(64, 1000, 1250) == B.TOPK_OK
     assert L.topk_exact_set_proposal(0, 0, 0) == B.TOPK_OK
+    # Admission target: -1 (default), 0 (off) or 1000..8000 thousandths of K.
+    assert L.topk_exact_set_admission(999) == B.TOPK_ERR_BAD_ARG
+    assert L.topk_exact_set_admission(8001) == B.TOPK_ERR_BAD_ARG
+    assert L.topk_exact_set_admission(-2) == B.TOPK_ERR_BAD_ARG
+    assert L.topk_exact_set_admission(0) == B.TOPK_OK
+    assert L.topk_exact_set_admission(3000) == B.TOPK_OK
+    assert L.topk_exact_set_admission(-1) == B.TOPK_OK
     # The timing hook takes both events or neither; (NULL, NULL) disarms it.
     assert L.topk_exact_time_next_call(fake, None) == B.TOPK_ERR_NULL_POINTER
     assert L.topk_exact_time_next_call(None, fake) == B.TOPK_ERR_NULL_POINTER

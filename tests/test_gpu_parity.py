@@ -80,7 +80,7 @@ def test_c1_rows():
         out, st = _run(s, l)
     _check(s, l, out, label="c1")
     assert st["sampled"] == 64 and st["row_per_wg"] == 64 and st["rowsplit"] == 0
-    assert st["tau0"] + st["tau1"] + st["recover_under"] + st["recover_over"] == 64
+    assert st["tau0"] + st["tau1"] + st["tau_a"] + st["recover_under"] + st["recover_over"] == 64
 
 
 def test_c2_rows():
@@ -115,10 +115,12 @@ def _sample_positions(L, stride=128):
     return np.arange(0, L, stride)
 
 
-def _adversarial_row(L, n_mid, seed):
-    """Row of length L whose stride-128 sample ranks put tau0 at 100 and tau1 at 50
-    (ranks 24 and 28 of 1024 samples at L = 131072), with n_mid non-sample entries
-    at 75 between them and everything else below 50."""
+def _adversarial_row(L, n_mid, seed, n_a=0):
+    """Row of length L whose stride-128 sample ranks put tau0 at 100, tau1 at 50 and the
+    deeper admission rank tau_a at 45 (ranks 24, 28 and 36 of 1024 samples at L = 131072;
+    samples of ranks 29-40 hold 45, the rest 0), with n_mid non-sample entries at 75,
+    n_a at 47 (between tau_a and tau1) and everything else below 40:
+    C(tau0) = 24, C(tau1) = 28 + n_mid, C(tau_a) = 40 + n_mid + n_a."""
     rng = np.random.default_rng(seed)
     x = rng.uniform(0.0, 40.0, size=L).astype(np.float32)
     sp = _sample_positions(L)
@@ -126,8 +128,11 @@ def _adversarial_row(L, n_mid, seed):
     pick = rng.permutation(len(sp))
     x[sp[pick[:24]]] = 100.0
     x[sp[pick[24:28]]] = 50.0
+    x[sp[pick[28:40]]] = 45.0
     non_sample = np.setdiff1d(np.arange(L), sp)
-    x[rng.choice(non_sample, size=n_mid, replace=False)] = 75.0
+    chosen = rng.choice(non_sample, size=n_mid + n_a, replace=False)
+    x[chosen[:n_mid]] = 75.0
+    x[chosen[n_mid:]] = 47.0
     return x
 
 
@@ -141,14 +146,40 @@ def test_forced_tau1_fallback():
     assert st["tau1"] == 4 and st["tau0"] == 0 and st["recover_under"] == 0
 
 
-def test_forced_exact_recovery_underfill():
+@pytest.mark.parametrize("execution", [tk.EXEC_AUTO, tk.EXEC_ROW_PER_WG])
+def test_forced_exact_recovery_underfill(execution):
+    # Auto dispatch row-splits 4 rows (admission at tau1); one workgroup per row admits
+    # down to tau_a, which underfills too, and recovers the rows in place (rows sampled
+    # element by element are recovered by their own workgroup at any length).
     L = 131072
     rows = np.stack([_adversarial_row(L, 1000, 10 + seed) for seed in range(4)])
     s = torch.from_numpy(rows).to(DEV)
     l = torch.full((4,), L, dtype=torch.int32, device=DEV)
-    out, st = _run(s, l)
+    with tk.execution(execution):
+        out, st = _run(s, l)
     _check(s, l, out, label="underfill recovery")
     assert st["recover_under"] == 4
+    if execution == tk.EXEC_ROW_PER_WG:
+        assert st["recover_inplace"] == 4 and st["queued"] == 0
+
+
+@pytest.mark.parametrize("execution", [tk.EXEC_ROW_PER_WG, tk.EXEC_PERSISTENT])
+def test_deeper_admission_rescues_tau1_underfill(execution):
+    # C(tau1) = 1028 < K <= C(tau_a) = 2540: certified at the deeper admission rank in the
+    # one pass; with the deeper admission off (every row admits at tau1, the pages' design)
+    # the same rows underfill and take exact recovery. Both results are exact.
+    L = 131072
+    rows = np.stack([_adversarial_row(L, 1000, 20 + seed, n_a=1500) for seed in range(4)])
+    s = torch.from_numpy(rows).to(DEV)
+    l = torch.full((4,), L, dtype=torch.int32, device=DEV)
+    with tk.execution(execution):
+        out, st = _run(s, l)
+        _check(s, l, out, label="tau_a rescue")
+        assert st["tau_a"] == 4 and st["tau1"] == 0 and st["recover_under"] == 0
+        with tk.admission(0):
+            out, st = _run(s, l)
+        _check(s, l, out, label="tau_a off")
+        assert st["recover_under"] == 4 and st["tau_a"] == 0
 
 
 def test_forced_overflow_recovery_negative_threshold():
@@ -212,13 +243,13 @@ def test_recovery_rows_mixed_with_normal_rows():
 
 
 def _controlled_row(L, kind, seed):
-    """Rows of L = 65536 (512 samples; sample ranks r0 = 24, r1 = 28, r2 = 46 at the
-    method's targets, as for any L that is a multiple of 128) that take each branch of
-    in-place exact recovery:
-      under_certified  tau1 underfills (1028 keys >= 50) but the deeper tau2 = 40 holds
-                       4046 keys: one more pass certifies;
-      under_full       tau1 underfills and every key below it is >= tau2 = 0: the second
-                       pass overflows, the exact full-row select runs;
+    """Rows of L = 65536 (512 samples; sample ranks r0 = 24, r1 = 28, r_a = 36 and
+    r2 = 46 at the method's targets, as for any L that is a multiple of 128) that take
+    each branch of in-place exact recovery:
+      under_certified  tau1 = 50 and tau_a = 45 underfill (1028 and 1040 keys) but the
+                       deeper tau2 = 40 holds 4046 keys: one more pass certifies;
+      under_full       tau1 and tau_a underfill and every key below them is >= tau2 = 0:
+                       the second pass overflows, the exact full-row select runs;
       over_certified   9028 keys >= tau1 = 50 (overflow), spread over distinct values: the
                        boundary bin of the pass histogram bounds a second pass;
       over_full        9000 copies of one value above tau1: the boundary bin alone exceeds
@@ -232,15 +263,17 @@ def _controlled_row(L, kind, seed):
     x[sp[pick[:24]]] = 100.0
     x[sp[pick[24:28]]] = 50.0
     if kind == "under_certified":
-        x[sp[pick[28:46]]] = 40.0
+        x[sp[pick[28:40]]] = 45.0
+        x[sp[pick[40:46]]] = 40.0
         chosen = rng.choice(rest, size=4000, replace=False)
         x[chosen[:1000]] = 75.0
-        x[chosen[1000:]] = 45.0
+        x[chosen[1000:]] = 42.0
     elif kind == "under_full":
         x = rng.uniform(0.0, 40.0, size=L).astype(np.float32)
         x[sp] = 0.0
         x[sp[pick[:24]]] = 100.0
         x[sp[pick[24:28]]] = 50.0
+        x[sp[pick[28:40]]] = 45.0
         x[rng.choice(rest, size=1000, replace=False)] = 75.0
     elif kind == "over_certified":
         x[rng.choice(rest, size=9000, replace=False)] = rng.uniform(55.0, 95.0, size=9000).astype(np.float32)
@@ -482,7 +515,8 @@ def test_selector_timing_hook():
 
 def test_phase_recording_hook():
     # Per-row phase stamps: ordered in time, path codes matching the row counters, tau1
-    # counts certified; disarmed calls write nothing.
+    # counts certified; disarmed calls write nothing. Admission at tau1 (the deeper
+    # admission off), so that the underfilling rows take the cooperative recovery kernels.
     s, l = _window_rows("c1", [(0, 20)])
     L = 131072
     adv = torch.from_numpy(np.stack([_adversarial_row(L, 1000, 700 + i) for i in range(2)])).to(DEV)
@@ -491,7 +525,7 @@ def test_phase_recording_hook():
     buf = torch.zeros((s.shape[0], 8), dtype=torch.int64, device=DEV)
     khz = tk.record_phases(buf)
     try:
-        with tk.execution(tk.EXEC_ROW_PER_WG):
+        with tk.execution(tk.EXEC_ROW_PER_WG), tk.admission(0):
             out, st = _run(s, l)
     finally:
         tk.record_phases(None)
@@ -501,6 +535,7 @@ def test_phase_recording_hook():
     codes = rec[:, 6] & 0xFF
     names = [tk.PATH_CODES.get(int(c)) for c in codes]
     assert names.count("tau0") == st["tau0"] and names.count("tau1") == st["tau1"]
+    assert names.count("tau_a") == st["tau_a"]
     assert names.count("recover_queued") == st["queued"] >= 2
     for r, n in zip(rec, names):
         start, sampled, proposed, passed, end = (int(v) for v in r[:5])
@@ -508,6 +543,8 @@ def test_phase_recording_hook():
         c1 = int(r[7]) & 0xFFFFFFFF
         if n in ("tau0", "tau1"):
             assert c1 >= K and r[5] == 0
+        elif n == "tau_a":
+            assert c1 < K and r[5] == 0
         else:
             assert c1 < K and int(r[5]) >= end  # recovered by the cooperative kernels after
     buf.zero_()
