@@ -379,7 +379,7 @@ enum : int {
   PH_END = 4,        // committed, or handed to the recovery kernels
   PH_RECOVERED = 5,  // exact recovery done (in place, or by the recovery finish kernel)
   PH_WHERE = 6,      // path code | XCC id << 8 | hardware wave id << 32
-  PH_COUNTS = 7,     // C(tau1) | C(tau0) << 32 (the admitted count alone past the buffer)
+  PH_COUNTS = 7,     // C(tau1) | C(tau0) << 32 (certified rows), else the admitted count
 };
 enum : uint32_t {
   PATH_SENTINEL = 1, PATH_DIRECT = 2, PATH_TAU0 = 3, PATH_TAU1 = 4, PATH_RECOVER_INPLACE = 5,
@@ -675,9 +675,9 @@ __device__ __attribute__((noinline)) void exact_full_row(grow_t x, uint32_t L, u
 // Direct exact selection of a short row: the row is staged in LDS as keys (one HBM
 // read), its first histogram over [min, max] is built there, and the LDS list is
 // refined like a certified candidate list (refine_list, below).
-template <bool KEYS_ONLY>
+template <bool KEYS_ONLY, bool COUNT = false>
 __device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t base, uint32_t sh, RowOut out,
-                                            Control* ctl);
+                                            Control* ctl, uint32_t k0 = 0u, uint32_t k1 = 0u);
 
 __device__ __forceinline__ void direct_exact(grow_t x, uint32_t L, uint32_t K, RowOut out, Control* ctl) {
   Smem& s = g_s;
@@ -1049,9 +1049,12 @@ __device__ __forceinline__ void sample_lines(grow_t x, uint32_t L, uint32_t n_s,
 // zeroed: the bins above the bin holding rank K are committed in one pass, that
 // bin's keys move to the frontier buffer (or, when too many, only their extremes are
 // noted), and the frontier is resolved exactly.
-template <bool KEYS_ONLY>
+//
+// With COUNT, the first sweep also counts the listed keys >= k0 and >= k1 into s.cnt0
+// and s.cnt1 (zeroed by reset_row_state), which hold the totals once this returns.
+template <bool KEYS_ONLY, bool COUNT>
 __device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t base, uint32_t sh, RowOut out,
-                                            Control* ctl) {
+                                            Control* ctl, uint32_t k0, uint32_t k1) {
   Smem& s = g_s;
   // The list: (index, key) pairs at s.buf[i], s.buf[CAP + i], or keys only at s.buf[i]
   // with the position as the index.
@@ -1074,12 +1077,13 @@ __device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t bas
   // is too wide for it, note the extremes of its keys.
   // Two sweeps over the list: count this thread's keys above the bin and in it (and
   // note the bin's extremes), reserve their slots once per wave, then write them.
-  uint32_t bmn = KEY_MAX, bmx = 0, ng = 0, nin = 0;
+  uint32_t bmn = KEY_MAX, bmx = 0, ng = 0, nin = 0, cnt01 = 0;
   for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
     const uint32_t k = key_at(i);
     const bool in = k >= blo && k <= bhi;
     ng += k > bhi ? 1u : 0u;
     nin += in ? 1u : 0u;
+    if (COUNT) cnt01 += (k >= k0 ? 1u : 0u) + (k >= k1 ? 0x10000u : 0u);
     if (in) {
       bmn = min(bmn, k);
       bmx = max(bmx, k);
@@ -1106,9 +1110,14 @@ __device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t bas
   }
   bmn = wave_min_u32(bmn);
   bmx = wave_max_u32(bmx);
+  if (COUNT) cnt01 = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(cnt01), WAVE - 1);
   if (lane_id() == 0) {
     atomicMin(&s.mn, bmn);
     atomicMax(&s.mx, bmx);
+    if (COUNT && cnt01 != 0u) {
+      atomicAdd(&s.cnt0, cnt01 & 0xFFFFu);
+      atomicAdd(&s.cnt1, cnt01 >> 16);
+    }
   }
   __syncthreads();
   uint32_t T, gt2;
@@ -1514,17 +1523,11 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
   __syncthreads();
   const uint32_t n = s.cnt;
   phase_mark(p.phase, row, PH_PASSED);
-  uint32_t c0 = 0, c1 = n;
-  if (n <= (uint32_t)CAP) {
-    count_admitted(n, t0key, t1key);
-    c0 = s.cnt0;
-    c1 = s.cnt1;
-  }
-  phase_put(p.phase, row, PH_COUNTS, (unsigned long long)c1 | ((unsigned long long)c0 << 32));
   if (n > (uint32_t)CAP) {
     // Too many admitted to hold: the K-th key is >= the admission key, recover exactly.
     // A short row is recovered in place from the boundary bin of the pass histogram, a
     // long one by the cooperative recovery kernels.
+    phase_put(p.phase, row, PH_COUNTS, (unsigned long long)n);
     if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_OVER);
     if (L <= p.inplace_max) {
       uint32_t n_ge;
@@ -1541,6 +1544,7 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
   } else if (n < p.K) {
     // Even the admission threshold underfills: the K-th key is below it. A short row is
     // recovered in place from the deeper sample rank tau2, a long one cooperatively.
+    phase_put(p.phase, row, PH_COUNTS, (unsigned long long)n);
     if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_UNDER);
     phase_mark(p.phase, row, PH_END);
     if (L <= p.inplace_max) {
@@ -1553,12 +1557,16 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
       phase_path(p.phase, row, PATH_RECOVER_QUEUED);
     }
   } else {
+    // Certified (K <= C(tau_a) <= CAP): refine, counting C(tau0) and C(tau1) among the
+    // admitted keys on the way, which name the threshold that certifies the row.
+    refine_list<false, true>(n, p.K, c.akey, c.sh, out, p.ctl, t0key, t1key);
+    const uint32_t c0 = s.cnt0, c1 = s.cnt1;
     const uint32_t path = c0 >= p.K ? PATH_TAU0 : (c1 >= p.K ? PATH_TAU1 : PATH_TAUA);
     if (t == 0) {
       stat_add(p.ctl, path == PATH_TAU0 ? TOPK_STAT_TAU0 : (path == PATH_TAU1 ? TOPK_STAT_TAU1 : TOPK_STAT_TAUA));
     }
-    refine_commit(n, p.K, c, out, p.ctl);
     phase_mark(p.phase, row, PH_END);
+    phase_put(p.phase, row, PH_COUNTS, (unsigned long long)c1 | ((unsigned long long)c0 << 32));
     phase_path(p.phase, row, path);
   }
 }
