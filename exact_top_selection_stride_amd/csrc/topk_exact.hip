@@ -2217,7 +2217,7 @@ void split_finish_kernel(Params p) {
     grow_t x = (grow_t)(p.scores) + (size_t)row * p.N;
     const RowOut out = row_out(p, row);
     const uint32_t c1 = rs->c1, c0 = rs->c0;
-    const uint32_t t1key = rs->t1key, t0key = rs->t0key, t2key = rs->t2key;
+    const uint32_t t1key = rs->t1key, t2key = rs->t2key;
     const uint32_t smin = ~rs->mn_inv, smax = rs->mx;
     if (c1 > (uint32_t)CAP) {
       if (t == 0) stat_add(p.ctl, TOPK_STAT_RECOVER_OVER);
