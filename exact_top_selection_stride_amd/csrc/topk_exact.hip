@@ -2828,6 +2828,13 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
   // per-row loop overhead is not amortised).
   const int64_t resident = (int64_t)st->occ * st->n_cu;
   const int ex = g_exec.load();
+  // The deeper admission pays where a row's exact recovery would lengthen the call: at
+  // most one row per resident workgroup (512 x 128K: 95.5 -> 79.9 us per call with it and
+  // in-place recovery). With more rows per workgroup a rare recovery is absorbed by the
+  // workgroup's other rows, and the extra candidates cost more than it saves: 4096 rows
+  // of 32K and 64K bf16 take 0.197 and 0.265 ms admitting at tau1, 0.203 and 0.271 ms
+  // admitting down to tau_a.
+  if (M > resident) p.TA = p.T1;
   // Line sampling reads the sampled lines whole and skips them in the full pass; a
   // sampled line is read again when its maximum reaches tau1 ("hot"). With about T1
   // admitted elements in a row of L, a 32-element line is hot with probability of

@@ -217,8 +217,10 @@ int topk_exact_set_proposal(int32_t stride, int32_t rho0_permille, int32_t rho1_
  * of K), instead of stopping at tau1; C(tau0) and C(tau1) are counted among the admitted
  * keys afterwards, so the statistics still name the threshold that certifies each row, and
  * a row with C(tau1) < K <= C(tau_a) is finished without reading it again. T_A applies only
- * where T1 < T_A < T2 and T_A <= 9/16 of the 8192-slot candidate buffer; elsewhere (and
- * for line-sampled rows, whose sample is 32 keys per period) admission stays at tau1.
+ * where T1 < T_A < T2 and T_A <= 9/16 of the 8192-slot candidate buffer, and in calls of at
+ * most one row per resident workgroup (where a row's recovery would lengthen the call);
+ * elsewhere (and for line-sampled rows, whose sample is 32 keys per period) admission stays
+ * at tau1.
  * rho_a = 0 turns the deeper admission off (every row admits at tau1, as on the pages);
  * -1 restores the default 2250. Every setting gives an exact result. Returns
  * TOPK_ERR_BAD_ARG unless rho_a is -1, 0 or in [1000, 8000]. Process-wide; a captured
