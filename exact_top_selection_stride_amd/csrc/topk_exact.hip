@@ -759,16 +759,21 @@ __device__ __forceinline__ void admit_batch(const u32x4 (&v)[NQ], const uint32_t
   }
   uint32_t pos = wave_reserve_n<NBITS>(n, &s.cnt);
   if (n == 0) return;
+  // Slots are addressed in bytes, and those past the buffer are clamped onto its last
+  // slot: a row that overflows is recovered from the histogram alone, so what that slot
+  // then holds is never read. With POS every admitted value is >= +0, whose order key is
+  // its bits with the top bit set, and key - akey = bits - (akey without its top bit).
+  uint32_t pb = 4u * pos;
+  const uint32_t ubase = c.akey & 0x7FFFFFFFu;
   auto one = [&](uint32_t u, uint32_t idx) {
     if (admits<POS>(u, c.thr)) {
-      const uint32_t k = key_of_bits(u);
-      if (pos < (uint32_t)CAP) {
-        s.buf[pos] = idx;
-        s.buf[CAP + pos] = k;
-      }
-      const uint32_t d = (k - c.akey) >> c.sh;
+      const uint32_t at = pb < 4u * (CAP - 1) ? pb : 4u * (CAP - 1);
+      const uint32_t k = POS ? (u | 0x80000000u) : key_of_bits(u);
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(s.buf) + at) = idx;
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(s.buf + CAP) + at) = k;
+      const uint32_t d = (POS ? (u - ubase) : (k - c.akey)) >> c.sh;
       atomicAdd(&s.hist[d < (uint32_t)(NB - 1) ? d : (uint32_t)(NB - 1)], 1u);
-      ++pos;
+      pb += 4u;
     }
   };
 #pragma unroll
@@ -874,13 +879,22 @@ __device__ __forceinline__ void fused_pass(grow_t x, uint32_t L, uint32_t n_s, c
     if (l == 0) v = atomicAdd(&s.pass_next, 1u);
     return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
   };
+  // Masking is needed only where a chunk that must not be admitted can read as an
+  // admitted value: without SKIP, in the last batch (its chunks past the end re-read the
+  // body's last chunk); with SKIP, where zeros (what a skipped chunk reads) are admitted,
+  // i.e. unless the admission threshold is above +0.
+  const bool skip_masked = !(POS && c.thr != 0u);
   auto examine = [&](const u32x4 (&raw)[PASS_UNROLL], const uint32_t (&inert)[PASS_UNROLL], uint32_t b) {
     u32x4 v[PASS_UNROLL];
     uint32_t e[PASS_UNROLL];
 #pragma unroll
     for (int u = 0; u < PASS_UNROLL; ++u) {
-      v[u] = raw[u] | splat4(inert[u]);
+      v[u] = raw[u];
       e[u] = ebase + head + 4u * (b * PERW + (uint32_t)u * WAVE + l);
+    }
+    if (SKIP ? skip_masked : (b + 1u == nb)) {
+#pragma unroll
+      for (int u = 0; u < PASS_UNROLL; ++u) v[u] = v[u] | splat4(inert[u]);
     }
     admit_batch<POS, PASS_UNROLL>(v, e, c);
   };
