@@ -176,6 +176,8 @@ struct Params {
   uint32_t pass_taus;   // row-split: each passing workgroup selects the row's taus itself
   unsigned long long* phase;  // per-row phase record (PHASE_WORDS per row), or null
   uint32_t* okey;       // [M][K] selected keys beside out (sorted output), or null
+  uint32_t sort_rows;   // sorted output: each row is sorted by its workgroup once complete
+  float* oval;          // sorted output values (with sort_rows), or null
 };
 
 __device__ __forceinline__ RowOut row_out(const Params& p, uint32_t row) {
@@ -1585,11 +1587,207 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
   }
 }
 
+__device__ __forceinline__ uint32_t row_length(const Params& p, uint32_t row) {
+  const int32_t len = p.row_len[row];
+  uint32_t L = len < 0 ? 0u : (uint32_t)len;
+  return L > p.N ? p.N : L;
+}
+
+// ------------------------------------------------------------ sorted output
+//
+// The sorted, value-returning output (an option beyond the pages' unordered contract):
+// one workgroup per row orders the row's selected entries by (key descending, index
+// ascending), then writes the indices and their scores; slots past the row's valid
+// entries keep the sentinel and get -inf. Entries are 64-bit composites
+// (key << 32 | ~index), never 0 for a valid entry (indices are below 2^31), so the zero
+// padding sorts last. The order comes from a bitonic network over P = EPT * BLOCK
+// entries, thread t holding entries t*EPT .. t*EPT+EPT-1. Every stage is a separate
+// instantiation with its run length and exchange distance known at compile time:
+// distances below EPT stay in registers, those up to 32 EPT go across the lanes of a wave
+// (see lane_xor64), and the larger ones (across waves) through LDS, double-buffered so
+// that each such stage needs one barrier.
+
+// Exchange of a 64-bit value with lane ^ M. The network is bound by vector ALU issue, so
+// only the one-instruction quad permutes (M = 1, 2) use DPP; M = 4, 8, 16 go through the
+// LDS crossbar's swizzle (bit mode: lane ^ M within groups of 32) and M = 32 through a
+// permute, both issued to the LDS pipe instead of the vector ALU.
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor_lds(uint32_t v) {
+  if constexpr (M <= 2) return lane_xor<M>(v);
+  else if constexpr (M <= 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (M << 10) | 0x1F);
+  else return (uint32_t)__shfl_xor((int)v, M);
+}
+template <int M>
+__device__ __forceinline__ uint64_t lane_xor64(uint64_t v) {
+  const uint32_t lo = lane_xor_lds<M>((uint32_t)v), hi = lane_xor_lds<M>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Stage (KB, J): runs of 2^KB entries, exchange distance J. An entry e meets e ^ J; the
+// lower entry of the pair keeps the larger value where bit KB of e is clear.
+template <int EPT, int KB, uint32_t J>
+__device__ __forceinline__ void sort_stage(uint64_t (&v)[EPT], uint32_t t, uint64_t (*c)[EPT * BLOCK],
+                                           int& buf) {
+  constexpr uint32_t K = 1u << KB;
+  if constexpr (J < (uint32_t)EPT) {
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      if (((uint32_t)q & J) == 0u) {
+        const int r = q | (int)J;
+        const bool desc = ((t * EPT + (uint32_t)q) & K) == 0u;
+        const uint64_t x = v[q], y = v[r];
+        // One compare: with x == y swapping changes nothing, so "y > x" may stand for
+        // "x < y" and its negation for "x > y".
+        const bool swap = (y > x) == desc;
+        v[q] = swap ? y : x;
+        v[r] = swap ? x : y;
+      }
+    }
+  } else {
+    constexpr uint32_t M = J / EPT;  // partner thread t ^ M, same register slot
+    const bool lo = (t & M) == 0u;
+    const bool desc = ((t * EPT) & K) == 0u;  // K >= J >= EPT: the same for every slot
+    const bool keep_max = desc == lo;
+    if constexpr (M < (uint32_t)WAVE) {
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) {
+        const uint64_t p = lane_xor64<(int)M>(v[q]);
+        v[q] = ((p > v[q]) == keep_max) ? p : v[q];  // equal values: either is the result
+      }
+    } else {
+      uint64_t* cb = c[buf];
+      buf ^= 1;
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) cb[t * EPT + (uint32_t)q] = v[q];
+      __syncthreads();
+      const uint32_t pt = t ^ M;
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) {
+        const uint64_t p = cb[pt * EPT + (uint32_t)q];
+        v[q] = ((p > v[q]) == keep_max) ? p : v[q];
+      }
+    }
+  }
+}
+
+// Every stage of runs of 2^KB, distances J, J / 2, ..., 1.
+template <int EPT, int KB, uint32_t J>
+__device__ __forceinline__ void sort_merge(uint64_t (&v)[EPT], uint32_t t, uint64_t (*c)[EPT * BLOCK], int& buf) {
+  sort_stage<EPT, KB, J>(v, t, c, buf);
+  if constexpr (J > 1u) sort_merge<EPT, KB, J / 2>(v, t, c, buf);
+}
+
+// Runs of 2^KB, 2^(KB+1), ..., P.
+template <int EPT, int KB>
+__device__ __forceinline__ void sort_levels(uint64_t (&v)[EPT], uint32_t t, uint64_t (*c)[EPT * BLOCK], int& buf) {
+  constexpr uint32_t P = (uint32_t)EPT * BLOCK;
+  if constexpr ((1u << KB) <= P) {
+    sort_merge<EPT, KB, (1u << KB) / 2>(v, t, c, buf);
+    sort_levels<EPT, KB + 1>(v, t, c, buf);
+  }
+}
+
+// One row of the sorted output by the calling workgroup, through the LDS buffer c
+// (2 EPT BLOCK 64-bit entries). Starts by reading the row's selected entries (written
+// before the caller's last barrier), ends after its own writes.
+template <int EPT>
+__device__ __forceinline__ void sort_row(const float* __restrict__ scores, uint32_t row, uint32_t L, uint32_t N,
+                                         uint32_t K, int32_t* __restrict__ out_idx, float* out_val,
+                                         int32_t sentinel, uint64_t (*c)[EPT * BLOCK]) {
+  const uint32_t t = threadIdx.x;
+  const uint32_t n = L < K ? L : K;  // valid entries of the row
+  int32_t* o = out_idx + (size_t)row * K;
+  const uint32_t* x = reinterpret_cast<const uint32_t*>(scores) + (size_t)row * N;
+  // For rows longer than K the selector left each selected key in out_val, beside its
+  // index (read contiguously here); otherwise the scores are read at the indices (short
+  // rows: the first L scores of the row, in order).
+  const uint32_t* kin = (out_val != nullptr && L > K) ? reinterpret_cast<const uint32_t*>(out_val) + (size_t)row * K
+                                                      : nullptr;
+  float* val = out_val ? out_val + (size_t)row * K : nullptr;
+  // Groups of four entries go through 16-byte loads and stores where the row's index,
+  // key and value slots are 16-byte aligned and the group is entirely valid.
+  const bool vec = (EPT % 4 == 0) && kin != nullptr &&
+                   ((reinterpret_cast<uintptr_t>(o) | reinterpret_cast<uintptr_t>(kin)) & 15u) == 0u;
+  uint64_t v[EPT];
+#pragma unroll
+  for (int g = 0; g < EPT; g += 4) {
+    const uint32_t e0 = t * EPT + (uint32_t)g;
+    if (EPT % 4 == 0 && vec && e0 + 3u < n) {
+      const u32x4 iv = *reinterpret_cast<const u32x4*>(o + e0);
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(kin + e0);
+      v[g] = ((uint64_t)kv.x << 32) | (uint64_t)(0xFFFFFFFFu - iv.x);
+      v[g + 1] = ((uint64_t)kv.y << 32) | (uint64_t)(0xFFFFFFFFu - iv.y);
+      v[g + 2] = ((uint64_t)kv.z << 32) | (uint64_t)(0xFFFFFFFFu - iv.z);
+      v[g + 3] = ((uint64_t)kv.w << 32) | (uint64_t)(0xFFFFFFFFu - iv.w);
+      continue;
+    }
+#pragma unroll
+    for (int q = g; q < g + 4 && q < EPT; ++q) {
+      const uint32_t e = t * EPT + (uint32_t)q;
+      v[q] = 0;
+      if (e < n) {
+        // The selector wrote an index in [0, L) here; the clamp only keeps reads in bounds.
+        const uint32_t i = (uint32_t)o[e] < L ? (uint32_t)o[e] : 0u;
+        const uint32_t k = kin != nullptr ? kin[e] : key_of_bits(x[i]);
+        v[q] = ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - i);
+      }
+    }
+  }
+  __syncthreads();  // every key of the row is read before any thread overwrites out_val
+  int buf = 0;
+  sort_levels<EPT, 1>(v, t, c, buf);
+  const bool vec_out = vec && val != nullptr && (reinterpret_cast<uintptr_t>(val) & 15u) == 0u;
+  auto value_of = [](uint32_t key) { return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key); };
+#pragma unroll
+  for (int g = 0; g < EPT; g += 4) {
+    const uint32_t e0 = t * EPT + (uint32_t)g;
+    if (EPT % 4 == 0 && vec_out && e0 + 3u < n) {
+      u32x4 iv, fv;
+      iv.x = 0xFFFFFFFFu - (uint32_t)v[g];
+      iv.y = 0xFFFFFFFFu - (uint32_t)v[g + 1];
+      iv.z = 0xFFFFFFFFu - (uint32_t)v[g + 2];
+      iv.w = 0xFFFFFFFFu - (uint32_t)v[g + 3];
+      fv.x = __float_as_uint(value_of((uint32_t)(v[g] >> 32)));
+      fv.y = __float_as_uint(value_of((uint32_t)(v[g + 1] >> 32)));
+      fv.z = __float_as_uint(value_of((uint32_t)(v[g + 2] >> 32)));
+      fv.w = __float_as_uint(value_of((uint32_t)(v[g + 3] >> 32)));
+      *reinterpret_cast<u32x4*>(o + e0) = iv;
+      *reinterpret_cast<u32x4*>(val + e0) = fv;
+      continue;
+    }
+#pragma unroll
+    for (int q = g; q < g + 4 && q < EPT; ++q) {
+      const uint32_t e = t * EPT + (uint32_t)q;
+      if (e < n) {
+        o[e] = (int32_t)(0xFFFFFFFFu - (uint32_t)v[q]);
+        if (val) val[e] = value_of((uint32_t)(v[q] >> 32));
+      } else if (e < K) {
+        o[e] = sentinel;
+        if (val) val[e] = -__builtin_inff();
+      }
+    }
+  }
+}
+
+template <int EPT>
+__global__ __launch_bounds__(BLOCK) void sort_rows_kernel(const float* __restrict__ scores,
+                                                          const int32_t* __restrict__ row_len,
+                                                          uint32_t N, uint32_t K,
+                                                          int32_t* __restrict__ out_idx,
+                                                          float* out_val, int32_t sentinel) {
+  __shared__ uint64_t c[2][(uint32_t)EPT * BLOCK];
+  const uint32_t row = blockIdx.x;
+  const int32_t len = row_len[row];
+  uint32_t L = len < 0 ? 0u : (uint32_t)len;
+  if (L > N) L = N;
+  sort_row<EPT>(scores, row, L, N, K, out_idx, out_val, sentinel, c);
+}
+
 // One row, start to commit. Everything on the row's path is inlined: an out-of-line
 // call per row would save and restore its callee-saved registers through scratch
 // memory for every row.
 template <bool STREAM_SAMPLE = false>
-__device__ __forceinline__ void process_row(const Params& p, uint32_t row) {
+__device__ __forceinline__ void process_row_body(const Params& p, uint32_t row) {
   const uint32_t t = threadIdx.x;
   const int32_t len = p.row_len[row];
   uint32_t L = len < 0 ? 0u : (uint32_t)len;
@@ -1621,6 +1819,32 @@ __device__ __forceinline__ void process_row(const Params& p, uint32_t row) {
   } else {
     sampled_row<STREAM_SAMPLE>(p, row, x, L, out);
   }
+}
+
+// The sorted output's order, by the row's own workgroup once its selection is written
+// (calls in which no row is handed to the recovery kernels): the candidate buffer,
+// free by then, holds the sort's exchange buffer.
+// Out of line (one copy for every kernel that holds it), taking scalars only.
+__device__ __noinline__ void sort_row_here(const float* scores, uint32_t row, uint32_t L, uint32_t N, uint32_t K,
+                                           int32_t* out, float* oval, int32_t sentinel) {
+  __syncthreads();  // every output slot of the row is written
+  auto* c = reinterpret_cast<uint64_t*>(g_s.buf);
+  if (K <= (uint32_t)BLOCK) {
+    sort_row<1>(scores, row, L, N, K, out, oval, sentinel, reinterpret_cast<uint64_t(*)[BLOCK]>(c));
+  } else if (K <= 2u * BLOCK) {
+    sort_row<2>(scores, row, L, N, K, out, oval, sentinel, reinterpret_cast<uint64_t(*)[2 * BLOCK]>(c));
+  } else if (K <= 4u * BLOCK) {
+    sort_row<4>(scores, row, L, N, K, out, oval, sentinel, reinterpret_cast<uint64_t(*)[4 * BLOCK]>(c));
+  } else {
+    sort_row<8>(scores, row, L, N, K, out, oval, sentinel, reinterpret_cast<uint64_t(*)[8 * BLOCK]>(c));
+  }
+}
+static_assert(2 * 8 * BLOCK * sizeof(uint64_t) <= sizeof(uint32_t) * 2 * CAP, "the sort's exchange buffer fits the candidate buffer");
+
+template <bool STREAM_SAMPLE = false>
+__device__ __forceinline__ void process_row(const Params& p, uint32_t row) {
+  process_row_body<STREAM_SAMPLE>(p, row);
+  if (p.sort_rows) sort_row_here(p.scores, row, row_length(p, row), p.N, p.K, (int32_t*)p.out, p.oval, p.sentinel);
 }
 
 // The selector kernel. Persistent execution: a grid of resident workgroups pulls
@@ -2034,11 +2258,6 @@ struct RowSplitState {
   uint32_t lmax[LINE_SAMPLE_MAX];
 };
 
-__device__ __forceinline__ uint32_t row_length(const Params& p, uint32_t row) {
-  const int32_t len = p.row_len[row];
-  uint32_t L = len < 0 ? 0u : (uint32_t)len;
-  return L > p.N ? p.N : L;
-}
 
 __device__ __forceinline__ bool split_applies(const Params& p, uint32_t L) {
   if (L <= p.K) return false;
@@ -2466,186 +2685,6 @@ int stream_capturing(hipStream_t stream, bool* capturing) {
   return TOPK_OK;
 }
 
-// ------------------------------------------------------------ sorted output
-//
-// The sorted, value-returning output (an option beyond the pages' unordered contract):
-// one workgroup per row orders the row's selected entries by (key descending, index
-// ascending), then writes the indices and their scores; slots past the row's valid
-// entries keep the sentinel and get -inf. Entries are 64-bit composites
-// (key << 32 | ~index), never 0 for a valid entry (indices are below 2^31), so the zero
-// padding sorts last. The order comes from a bitonic network over P = EPT * BLOCK
-// entries, thread t holding entries t*EPT .. t*EPT+EPT-1. Every stage is a separate
-// instantiation with its run length and exchange distance known at compile time:
-// distances below EPT stay in registers, those up to 32 EPT go across the lanes of a wave
-// (see lane_xor64), and the larger ones (across waves) through LDS, double-buffered so
-// that each such stage needs one barrier.
-
-// Exchange of a 64-bit value with lane ^ M. The network is bound by vector ALU issue, so
-// only the one-instruction quad permutes (M = 1, 2) use DPP; M = 4, 8, 16 go through the
-// LDS crossbar's swizzle (bit mode: lane ^ M within groups of 32) and M = 32 through a
-// permute, both issued to the LDS pipe instead of the vector ALU.
-template <int M>
-__device__ __forceinline__ uint32_t lane_xor_lds(uint32_t v) {
-  if constexpr (M <= 2) return lane_xor<M>(v);
-  else if constexpr (M <= 16) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (M << 10) | 0x1F);
-  else return (uint32_t)__shfl_xor((int)v, M);
-}
-template <int M>
-__device__ __forceinline__ uint64_t lane_xor64(uint64_t v) {
-  const uint32_t lo = lane_xor_lds<M>((uint32_t)v), hi = lane_xor_lds<M>((uint32_t)(v >> 32));
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Stage (KB, J): runs of 2^KB entries, exchange distance J. An entry e meets e ^ J; the
-// lower entry of the pair keeps the larger value where bit KB of e is clear.
-template <int EPT, int KB, uint32_t J>
-__device__ __forceinline__ void sort_stage(uint64_t (&v)[EPT], uint32_t t, uint64_t (*c)[EPT * BLOCK],
-                                           int& buf) {
-  constexpr uint32_t K = 1u << KB;
-  if constexpr (J < (uint32_t)EPT) {
-#pragma unroll
-    for (int q = 0; q < EPT; ++q) {
-      if (((uint32_t)q & J) == 0u) {
-        const int r = q | (int)J;
-        const bool desc = ((t * EPT + (uint32_t)q) & K) == 0u;
-        const uint64_t x = v[q], y = v[r];
-        // One compare: with x == y swapping changes nothing, so "y > x" may stand for
-        // "x < y" and its negation for "x > y".
-        const bool swap = (y > x) == desc;
-        v[q] = swap ? y : x;
-        v[r] = swap ? x : y;
-      }
-    }
-  } else {
-    constexpr uint32_t M = J / EPT;  // partner thread t ^ M, same register slot
-    const bool lo = (t & M) == 0u;
-    const bool desc = ((t * EPT) & K) == 0u;  // K >= J >= EPT: the same for every slot
-    const bool keep_max = desc == lo;
-    if constexpr (M < (uint32_t)WAVE) {
-#pragma unroll
-      for (int q = 0; q < EPT; ++q) {
-        const uint64_t p = lane_xor64<(int)M>(v[q]);
-        v[q] = ((p > v[q]) == keep_max) ? p : v[q];  // equal values: either is the result
-      }
-    } else {
-      uint64_t* cb = c[buf];
-      buf ^= 1;
-#pragma unroll
-      for (int q = 0; q < EPT; ++q) cb[t * EPT + (uint32_t)q] = v[q];
-      __syncthreads();
-      const uint32_t pt = t ^ M;
-#pragma unroll
-      for (int q = 0; q < EPT; ++q) {
-        const uint64_t p = cb[pt * EPT + (uint32_t)q];
-        v[q] = ((p > v[q]) == keep_max) ? p : v[q];
-      }
-    }
-  }
-}
-
-// Every stage of runs of 2^KB, distances J, J / 2, ..., 1.
-template <int EPT, int KB, uint32_t J>
-__device__ __forceinline__ void sort_merge(uint64_t (&v)[EPT], uint32_t t, uint64_t (*c)[EPT * BLOCK], int& buf) {
-  sort_stage<EPT, KB, J>(v, t, c, buf);
-  if constexpr (J > 1u) sort_merge<EPT, KB, J / 2>(v, t, c, buf);
-}
-
-// Runs of 2^KB, 2^(KB+1), ..., P.
-template <int EPT, int KB>
-__device__ __forceinline__ void sort_levels(uint64_t (&v)[EPT], uint32_t t, uint64_t (*c)[EPT * BLOCK], int& buf) {
-  constexpr uint32_t P = (uint32_t)EPT * BLOCK;
-  if constexpr ((1u << KB) <= P) {
-    sort_merge<EPT, KB, (1u << KB) / 2>(v, t, c, buf);
-    sort_levels<EPT, KB + 1>(v, t, c, buf);
-  }
-}
-
-template <int EPT>
-__global__ __launch_bounds__(BLOCK) void sort_rows_kernel(const float* __restrict__ scores,
-                                                          const int32_t* __restrict__ row_len,
-                                                          uint32_t N, uint32_t K,
-                                                          int32_t* __restrict__ out_idx,
-                                                          float* out_val, int32_t sentinel) {
-  constexpr uint32_t P = (uint32_t)EPT * BLOCK;
-  __shared__ uint64_t c[2][P];
-  const uint32_t row = blockIdx.x, t = threadIdx.x;
-  const int32_t len = row_len[row];
-  uint32_t L = len < 0 ? 0u : (uint32_t)len;
-  if (L > N) L = N;
-  const uint32_t n = L < K ? L : K;  // valid entries of the row
-  int32_t* o = out_idx + (size_t)row * K;
-  const uint32_t* x = reinterpret_cast<const uint32_t*>(scores) + (size_t)row * N;
-  // For rows longer than K the selector left each selected key in out_val, beside its
-  // index (read contiguously here); otherwise the scores are read at the indices (short
-  // rows: the first L scores of the row, in order).
-  const uint32_t* kin = (out_val != nullptr && L > K) ? reinterpret_cast<const uint32_t*>(out_val) + (size_t)row * K
-                                                      : nullptr;
-  float* val = out_val ? out_val + (size_t)row * K : nullptr;
-  // Groups of four entries go through 16-byte loads and stores where the row's index,
-  // key and value slots are 16-byte aligned and the group is entirely valid.
-  const bool vec = (EPT % 4 == 0) && kin != nullptr &&
-                   ((reinterpret_cast<uintptr_t>(o) | reinterpret_cast<uintptr_t>(kin)) & 15u) == 0u;
-  uint64_t v[EPT];
-#pragma unroll
-  for (int g = 0; g < EPT; g += 4) {
-    const uint32_t e0 = t * EPT + (uint32_t)g;
-    if (EPT % 4 == 0 && vec && e0 + 3u < n) {
-      const u32x4 iv = *reinterpret_cast<const u32x4*>(o + e0);
-      const u32x4 kv = *reinterpret_cast<const u32x4*>(kin + e0);
-      v[g] = ((uint64_t)kv.x << 32) | (uint64_t)(0xFFFFFFFFu - iv.x);
-      v[g + 1] = ((uint64_t)kv.y << 32) | (uint64_t)(0xFFFFFFFFu - iv.y);
-      v[g + 2] = ((uint64_t)kv.z << 32) | (uint64_t)(0xFFFFFFFFu - iv.z);
-      v[g + 3] = ((uint64_t)kv.w << 32) | (uint64_t)(0xFFFFFFFFu - iv.w);
-      continue;
-    }
-#pragma unroll
-    for (int q = g; q < g + 4 && q < EPT; ++q) {
-      const uint32_t e = t * EPT + (uint32_t)q;
-      v[q] = 0;
-      if (e < n) {
-        // The selector wrote an index in [0, L) here; the clamp only keeps reads in bounds.
-        const uint32_t i = (uint32_t)o[e] < L ? (uint32_t)o[e] : 0u;
-        const uint32_t k = kin != nullptr ? kin[e] : key_of_bits(x[i]);
-        v[q] = ((uint64_t)k << 32) | (uint64_t)(0xFFFFFFFFu - i);
-      }
-    }
-  }
-  __syncthreads();  // every key of the row is read before any thread overwrites out_val
-  int buf = 0;
-  sort_levels<EPT, 1>(v, t, c, buf);
-  const bool vec_out = vec && val != nullptr && (reinterpret_cast<uintptr_t>(val) & 15u) == 0u;
-  auto value_of = [](uint32_t key) { return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key); };
-#pragma unroll
-  for (int g = 0; g < EPT; g += 4) {
-    const uint32_t e0 = t * EPT + (uint32_t)g;
-    if (EPT % 4 == 0 && vec_out && e0 + 3u < n) {
-      u32x4 iv, fv;
-      iv.x = 0xFFFFFFFFu - (uint32_t)v[g];
-      iv.y = 0xFFFFFFFFu - (uint32_t)v[g + 1];
-      iv.z = 0xFFFFFFFFu - (uint32_t)v[g + 2];
-      iv.w = 0xFFFFFFFFu - (uint32_t)v[g + 3];
-      fv.x = __float_as_uint(value_of((uint32_t)(v[g] >> 32)));
-      fv.y = __float_as_uint(value_of((uint32_t)(v[g + 1] >> 32)));
-      fv.z = __float_as_uint(value_of((uint32_t)(v[g + 2] >> 32)));
-      fv.w = __float_as_uint(value_of((uint32_t)(v[g + 3] >> 32)));
-      *reinterpret_cast<u32x4*>(o + e0) = iv;
-      *reinterpret_cast<u32x4*>(val + e0) = fv;
-      continue;
-    }
-#pragma unroll
-    for (int q = g; q < g + 4 && q < EPT; ++q) {
-      const uint32_t e = t * EPT + (uint32_t)q;
-      if (e < n) {
-        o[e] = (int32_t)(0xFFFFFFFFu - (uint32_t)v[q]);
-        if (val) val[e] = value_of((uint32_t)(v[q] >> 32));
-      } else if (e < K) {
-        o[e] = sentinel;
-        if (val) val[e] = -__builtin_inff();
-      }
-    }
-  }
-}
-
 // Scratch of the allocation-free entry point (topk_exact_noalloc): a control block, NA_QMAX
 // cooperative-recovery slots and row-split state for NA_RS_ROWS rows, laid out like the
 // workspace. It exists once per GPU from load to process end, zero at load. In host code
@@ -2760,10 +2799,11 @@ int selector_check(const float* scores, const int32_t* row_len, int64_t M, int64
 // workspace, or the allocation-free entry point's scratch). `timing`: the call may take
 // the armed timing events (not under capture).
 // `okey`: device [M][K], receives each selected element's key in its output slot
-// (sorted output), or null.
+// (sorted output), or null. `sort_here` (sorted output): set to whether the selector
+// kernels also sort every row (then no separate sort follows), or null.
 int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc, int32_t K,
                     int32_t* out_idx, int32_t sentinel, hipStream_t stream, bool timing, DevState* st,
-                    uint32_t* okey = nullptr) {
+                    uint32_t* okey = nullptr, bool* sort_here = nullptr) {
   int rc = TOPK_OK;
   Params p;
   p.scores = scores;
@@ -2825,6 +2865,8 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
   p.rs = nullptr;
   p.phase = (timing && M <= g_phase_rows.load()) ? g_phase_buf.load() : nullptr;
   p.okey = okey;
+  p.sort_rows = 0;
+  p.oval = nullptr;
   p.ps = 1;
   p.pp = 1;
   p.pass_taus = 0;
@@ -2871,6 +2913,19 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
   if (!split && p.inplace_max != 0u && p.TA > p.T1 && p.stride == STRIDE && p.line_min > 1u) {
     const uint32_t elem_max = (p.line_min - 1u) * STRIDE;
     if (elem_max > p.inplace_max) p.inplace_max = elem_max;
+  }
+  // Sorted output: in calls of at most one row per resident workgroup where every row is
+  // completed inside the selector kernel (none can be handed to the recovery kernels), each
+  // workgroup sorts its row once complete, overlapping the other rows' passes; otherwise
+  // a sort kernel follows. Measured on MI355X (graph replays, sorted call): 512 x 128K
+  // 94.8 -> 90.5 us and 256 x 8K 26.5 -> 24.7 us sorted here, while 8192 x 64K rows,
+  // sixteen per workgroup, took 622.7 -> 657.4 us.
+  if (sort_here != nullptr) {
+    *sort_here = !split && (int64_t)p.inplace_max >= N_alloc && M <= resident;
+    if (*sort_here) {
+      p.sort_rows = 1;
+      p.oval = reinterpret_cast<float*>(okey);
+    }
   }
   hipError_t e;
   hipEvent_t ev_start = nullptr, ev_stop = nullptr;
@@ -3004,9 +3059,10 @@ int topk_exact_sorted(const float* scores, const int32_t* row_len, int64_t M, in
   if ((reinterpret_cast<uintptr_t>(out_val) & 3u) != 0) return fail(TOPK_ERR_BAD_ARG, "out_val is not 4-byte aligned");
   // With values wanted, the selector also writes each selected key into out_val (same
   // slot as its index); the sort then reads those instead of gathering the scores again.
+  bool sorted_here = false;
   rc = selector_launch(scores, row_len, M, N_alloc, K, out_idx, sentinel, stream, !capturing, st,
-                       reinterpret_cast<uint32_t*>(out_val));
-  if (rc != TOPK_OK) return rc;
+                       reinterpret_cast<uint32_t*>(out_val), &sorted_here);
+  if (rc != TOPK_OK || sorted_here) return rc;
   // Entries per thread: the smallest power of two with EPT * BLOCK >= K (K <= 4096).
   const dim3 grid((unsigned)M), block(BLOCK);
   const uint32_t NN = (uint32_t)N_alloc, KK = (uint32_t)K;

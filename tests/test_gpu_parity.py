@@ -899,3 +899,24 @@ def test_sorted_output_k4096_and_misaligned_values():
     code = tk.lib().topk_exact_sorted(s.data_ptr(), l.data_ptr(), 3, s.shape[1], 4096, idx.data_ptr(),
                                       buf.data_ptr() + 2, -1, torch.cuda.current_stream().cuda_stream)
     assert code == 7  # TOPK_ERR_BAD_ARG, nothing enqueued
+
+
+@pytest.mark.parametrize("Kr", [512, 1000, 2048, 4096])
+def test_sorted_output_in_selector_workgroups(Kr):
+    # Few rows of 64K (bf16 ties; always recovered in place), one workgroup per row: each
+    # workgroup sorts its own row once its selection is written (one to eight entries a
+    # thread by K); values 4-byte but not 16-byte aligned take the scalar stores; the
+    # short row is sorted from its scores.
+    s, l = _window_rows("c4_n65536_m512", [(0, 5)])
+    l[4] = 1500
+    with tk.execution(tk.EXEC_ROW_PER_WG):
+        idx, val = tk.topk_exact_sorted(s, l, K=Kr)
+        torch.cuda.synchronize()
+        _check_sorted(s, l, idx, val, Kr, label=f"sorted in the selector, K {Kr}")
+        buf = torch.empty(5 * Kr + 1, dtype=torch.float32, device=DEV)
+        idx2 = torch.empty((5, Kr), dtype=torch.int32, device=DEV)
+        code = tk.lib().topk_exact_sorted(s.data_ptr(), l.data_ptr(), 5, s.shape[1], Kr, idx2.data_ptr(),
+                                          buf.data_ptr() + 4, -1, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+    assert code == 0, tk.last_error()
+    _check_sorted(s, l, idx2, buf[1:].view(5, Kr), Kr, label=f"sorted in the selector, offset values, K {Kr}")
