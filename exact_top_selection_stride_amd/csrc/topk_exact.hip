@@ -2909,8 +2909,11 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
   // with fewer than line_min sample periods) need exact recovery about once in 25000 rows
   // of 128K, so they are recovered in place at any length: a call whose rows are all such
   // rows launches no recovery kernels (512 x 128K: 86 -> 80 us per call), and the rare row
-  // that does recover streams its row once more on its own.
-  if (!split && p.inplace_max != 0u && p.TA > p.T1 && p.stride == STRIDE && p.line_min > 1u) {
+  // that does recover streams its row once more on its own. The same holds where tau1
+  // itself targets at least 2 K (K <= 1024, whose targets are floored at 16 sample
+  // ranks): 512 x 128K at K = 512 82.0 -> 75.2 us.
+  if (!split && p.inplace_max != 0u && (p.TA > p.T1 || p.T1 >= 2u * (uint32_t)K) && p.stride == STRIDE &&
+      p.line_min > 1u) {
     const uint32_t elem_max = (p.line_min - 1u) * STRIDE;
     if (elem_max > p.inplace_max) p.inplace_max = elem_max;
   }
