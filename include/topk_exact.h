@@ -157,6 +157,18 @@ int topk_exact_noalloc(const float* scores, const int32_t* row_len, int64_t M, i
  * Other arguments, errors and capture behaviour as for topk_exact. The selected set is
  * the same as topk_exact's; which of several boundary-tied scores are kept is free, the
  * order of the output is fully determined by that set. */
+/* Sorted, value-returning output (an option beside the pages' unordered contract of
+ * [Cx] section "什么叫精确，时间怎么量"): the same selection as topk_exact, then each row's
+ * slots ordered by score, descending in IEEE totalOrder with boundary ties by index
+ * ascending; a row with L <= K lists its L indices in that order, then the sentinel.
+ *   out_idx  as for topk_exact, in that order.
+ *   out_val  device, row-major [M][K] float32, 4-byte aligned, or NULL: the selected scores
+ *            (the input's bit patterns) in the order of out_idx, -inf in sentinel slots.
+ *            With NULL only the ordered indices are written. Caller-owned.
+ * Where a call has at most one row per resident workgroup and no row can be handed to the
+ * recovery kernels, each selector workgroup sorts its own row; otherwise a sort kernel
+ * follows on the same stream. Capture, workspace and error behaviour as for topk_exact,
+ * plus TOPK_ERR_BAD_ARG (nothing enqueued) for an out_val that is not 4-byte aligned. */
 int topk_exact_sorted(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc,
                       int32_t K, int32_t* out_idx, float* out_val, int32_t sentinel, hipStream_t stream);
 
