@@ -1465,19 +1465,8 @@ __device__ __forceinline__ void write_hot_bitmap(const uint32_t* lmax, uint32_t 
   }
 }
 
-// The element sample read before the row's length is known: positions j * stride for
-// j < n_s(N_alloc), thread t holding j = n_s(N_alloc) - 1 - (t + m BLOCK) in v[m]; any
-// row sampled element by element at that stride reads its sample from here.
-constexpr int SPEC_KEYS = 2;
-struct EarlySample {
-  bool valid;
-  uint32_t n_s;  // n_s of a full-width row
-  uint32_t v[SPEC_KEYS];
-};
-
 template <bool STREAM_SAMPLE>
-__device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_t x, uint32_t L, RowOut out,
-                                            const EarlySample& es) {
+__device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_t x, uint32_t L, RowOut out) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x;
   // Rows whose stride-s sample would not fit the LDS key list (L > 16384 s, past the
@@ -1498,21 +1487,6 @@ __device__ __forceinline__ void sampled_row(const Params& p, uint32_t row, grow_
   const bool by_lines = stride == STRIDE && n_s <= LINE_SAMPLE_MAX && n_s >= p.line_min;
   if (by_lines) {
     sample_lines<STREAM_SAMPLE>(x, L, n_s, &s.buf[0], &s.buf[CAP]);
-  } else if (es.valid && stride == p.stride) {
-    // Read at the row's start (n_s <= es.n_s: every position below n_s is held).
-    uint32_t mn = KEY_MAX, mx = 0;
-#pragma unroll
-    for (int m = 0; m < SPEC_KEYS; ++m) {
-      const uint32_t jr = t + (uint32_t)m * BLOCK;
-      const uint32_t j = es.n_s - 1u - jr;
-      if (jr < es.n_s && j < n_s) {
-        const uint32_t k = key_of_bits(es.v[m]);
-        s.buf[j] = k;
-        mn = min(mn, k);
-        mx = max(mx, k);
-      }
-    }
-    block_minmax(mn, mx);
   } else {
     uint32_t mn = KEY_MAX, mx = 0;
 #pragma unroll 8
@@ -1815,25 +1789,10 @@ __global__ __launch_bounds__(BLOCK) void sort_rows_kernel(const float* __restric
 template <bool STREAM_SAMPLE = false>
 __device__ __forceinline__ void process_row_body(const Params& p, uint32_t row) {
   const uint32_t t = threadIdx.x;
-  grow_t x = (grow_t)(p.scores) + (size_t)row * p.N;
-  // One workgroup per row: where every sampled row of the call takes the element sample
-  // (at most SPEC_KEYS BLOCK periods, below the line-sampling bound), its loads are issued
-  // together with the length's, at the full width: the positions do not depend on the
-  // length, and the two memory latencies overlap instead of following each other.
-  EarlySample es;
-  es.n_s = (p.N + p.stride - 1u) / p.stride;
-  es.valid = STREAM_SAMPLE && p.mode != TOPK_PATH_DIRECT && p.mode != TOPK_PATH_RECOVERY && p.N > p.direct_max &&
-             es.n_s <= (uint32_t)(SPEC_KEYS * BLOCK) && !(p.stride == STRIDE && es.n_s >= p.line_min);
-  if (es.valid) {
-#pragma unroll
-    for (int m = 0; m < SPEC_KEYS; ++m) {
-      const uint32_t jr = t + (uint32_t)m * BLOCK;
-      es.v[m] = jr < es.n_s ? x[(size_t)(es.n_s - 1u - jr) * p.stride] : 0u;
-    }
-  }
   const int32_t len = p.row_len[row];
   uint32_t L = len < 0 ? 0u : (uint32_t)len;
   if (L > p.N) L = p.N;
+  grow_t x = (grow_t)(p.scores) + (size_t)row * p.N;
   const RowOut out = row_out(p, row);
   if (t == 0) stat_add(p.ctl, TOPK_STAT_ROWS);
   phase_mark(p.phase, row, PH_START);
@@ -1858,7 +1817,7 @@ __device__ __forceinline__ void process_row_body(const Params& p, uint32_t row) 
     phase_mark(p.phase, row, PH_END);
     phase_path(p.phase, row, PATH_FORCED_RECOVERY);
   } else {
-    sampled_row<STREAM_SAMPLE>(p, row, x, L, out, es);
+    sampled_row<STREAM_SAMPLE>(p, row, x, L, out);
   }
 }
 
