@@ -31,6 +31,13 @@ def _ensure_hip_built():
     from exact_top_selection_stride_amd import build as hip_build
     if not os.path.exists(hip_build.LIB):
         hip_build.build()
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "mfma_probe_build", os.path.join(ROOT, "tests", "native", "build.py"))
+    probe_build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(probe_build)
+    if not os.path.exists(probe_build.LIB):
+        probe_build.build()
 
 
 _ensure_hip_built()
