@@ -269,8 +269,8 @@ __device__ __forceinline__ uint32_t wave_reserve_n(uint32_t cnt, uint32_t* count
   return b + before;
 }
 
-// Per-thread item counts of LDS lists walked as i = t, t + BLOCK, ...: at most 32 for
-// lists of up to 16384 entries.
+// Per-thread item counts of LDS lists walked as i = t, t + BLOCK, ... or four entries at
+// a time (i = 4 t, 4 t + 4 BLOCK, ...): at most 32 for lists of up to 16384 entries.
 constexpr int LIST_BITS = 6;
 static_assert((KEYS_CAP + BLOCK - 1) / BLOCK < (1 << LIST_BITS), "per-thread list counts fit LIST_BITS");
 static_assert(CAP < 0x10000, "two per-wave counts of admitted keys share one word");
@@ -693,7 +693,13 @@ __device__ __forceinline__ void direct_exact(grow_t x, uint32_t L, uint32_t K, R
   block_minmax(mn, mx);
   const uint32_t lo = s.mn, hi = s.mx;
   const uint32_t sh = shift_for(hi - lo);
-  for (uint32_t i = threadIdx.x; i < L; i += BLOCK) atomicAdd(&s.hist[(s.buf[i] - lo) >> sh], 1u);
+  for (uint32_t i = 4u * threadIdx.x; i < L; i += 4u * BLOCK) {
+    // four keys per 16-byte LDS read; entries from L on are stale and skipped
+    const u32x4 k4 = *reinterpret_cast<const u32x4*>(&s.buf[i]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i + (uint32_t)u < L) atomicAdd(&s.hist[(k4[u] - lo) >> sh], 1u);
+  }
   __syncthreads();
   refine_list<true>(L, K, lo, sh, out, ctl);
 }
@@ -1075,7 +1081,15 @@ __device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t bas
   // The list: (index, key) pairs at s.buf[i], s.buf[CAP + i], or keys only at s.buf[i]
   // with the position as the index.
   auto key_at = [&](uint32_t i) -> uint32_t { return KEYS_ONLY ? g_s.buf[i] : g_s.buf[CAP + i]; };
-  auto id_at = [&](uint32_t i) -> uint32_t { return KEYS_ONLY ? i : g_s.buf[i]; };
+  // Entries i .. i + 3 (i a multiple of 4 below n; the reads stay inside the list's region,
+  // entries at n and beyond are stale and masked by the callers).
+  auto keys4_at = [&](uint32_t i) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(KEYS_ONLY ? &g_s.buf[i] : &g_s.buf[CAP + i]);
+  };
+  auto ids4_at = [&](uint32_t i) -> u32x4 {
+    if (KEYS_ONLY) return u32x4{i, i + 1u, i + 2u, i + 3u};
+    return *reinterpret_cast<const u32x4*>(&g_s.buf[i]);
+  };
   if (threadIdx.x == 0) {  // extremes of the boundary bin's keys (block_find_bin's barrier orders this)
     s.mn = KEY_MAX;
     s.mx = 0;
@@ -1093,33 +1107,43 @@ __device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t bas
   // is too wide for it, note the extremes of its keys.
   // Two sweeps over the list: count this thread's keys above the bin and in it (and
   // note the bin's extremes), reserve their slots once per wave, then write them.
+  // Each thread takes four consecutive entries per step (16-byte LDS reads, several in
+  // flight), so the sweeps wait on one LDS round trip per four entries.
   uint32_t bmn = KEY_MAX, bmx = 0, ng = 0, nin = 0, cnt01 = 0;
-  for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
-    const uint32_t k = key_at(i);
-    const bool in = k >= blo && k <= bhi;
-    ng += k > bhi ? 1u : 0u;
-    nin += in ? 1u : 0u;
-    if (COUNT) cnt01 += (k >= k0 ? 1u : 0u) + (k >= k1 ? 0x10000u : 0u);
-    if (in) {
-      bmn = min(bmn, k);
-      bmx = max(bmx, k);
+  for (uint32_t i = 4u * threadIdx.x; i < n; i += 4u * BLOCK) {
+    const u32x4 k4 = keys4_at(i);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t k = k4[u];
+      const bool v = i + (uint32_t)u < n;
+      const bool in = v && k >= blo && k <= bhi;
+      ng += (v && k > bhi) ? 1u : 0u;
+      nin += in ? 1u : 0u;
+      if (COUNT) cnt01 += v ? (k >= k0 ? 1u : 0u) + (k >= k1 ? 0x10000u : 0u) : 0u;
+      bmn = in ? min(bmn, k) : bmn;
+      bmx = in ? max(bmx, k) : bmx;
     }
   }
   {
     uint32_t p = wave_reserve_n<LIST_BITS>(ng, &s.out_gt);
     uint32_t f = fits ? wave_reserve_n<LIST_BITS>(nin, &s.fl_cnt) : 0u;
     if (ng + (fits ? nin : 0u) != 0) {
-      for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
-        const uint32_t k = key_at(i);
-        if (k > bhi) {
-          if (p < K) out.put(p, id_at(i), k);
-          ++p;
-        } else if (fits && k >= blo) {
-          if (f < (uint32_t)FL_CAP) {
-            s.fl_idx[f] = id_at(i);
+      for (uint32_t i = 4u * threadIdx.x; i < n; i += 4u * BLOCK) {
+        const u32x4 k4 = keys4_at(i);
+        const u32x4 id4 = ids4_at(i);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t k = k4[u];
+          const bool v = i + (uint32_t)u < n;
+          const bool g = v && k > bhi;
+          const bool in = v && fits && !g && k >= blo;
+          if (g && p < K) out.put(p, id4[u], k);
+          if (in && f < (uint32_t)FL_CAP) {
+            s.fl_idx[f] = id4[u];
             s.fl_key[f] = k;
           }
-          ++f;
+          p += g ? 1u : 0u;
+          f += in ? 1u : 0u;
         }
       }
     }
@@ -1184,22 +1208,32 @@ __device__ __forceinline__ void refine_list(uint32_t n, uint32_t K, uint32_t bas
     const uint32_t gt_total = above + gt2;
     const uint32_t ties = K - gt_total;
     uint32_t ng = 0, ne = 0;
-    for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
-      const uint32_t k = key_at(i);
-      ng += (k > T && k <= bhi) ? 1u : 0u;
-      ne += k == T ? 1u : 0u;
+    for (uint32_t i = 4u * threadIdx.x; i < n; i += 4u * BLOCK) {
+      const u32x4 k4 = keys4_at(i);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t k = k4[u];
+        const bool v = i + (uint32_t)u < n;
+        ng += (v && k > T && k <= bhi) ? 1u : 0u;
+        ne += (v && k == T) ? 1u : 0u;
+      }
     }
     uint32_t p = wave_reserve_n<LIST_BITS>(ng, &s.out_gt);
     uint32_t q = wave_reserve_n<LIST_BITS>(ne, &s.out_tie);
     if (ng + ne != 0) {
-      for (uint32_t i = threadIdx.x; i < n; i += BLOCK) {
-        const uint32_t k = key_at(i);
-        if (k > T && k <= bhi) {
-          if (p < K) out.put(p, id_at(i), k);
-          ++p;
-        } else if (k == T) {
-          if (q < ties && gt_total + q < K) out.put(gt_total + q, id_at(i), k);
-          ++q;
+      for (uint32_t i = 4u * threadIdx.x; i < n; i += 4u * BLOCK) {
+        const u32x4 k4 = keys4_at(i);
+        const u32x4 id4 = ids4_at(i);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t k = k4[u];
+          const bool v = i + (uint32_t)u < n;
+          const bool g = v && k > T && k <= bhi;
+          const bool e = v && k == T;
+          if (g && p < K) out.put(p, id4[u], k);
+          if (e && q < ties && gt_total + q < K) out.put(gt_total + q, id4[u], k);
+          p += g ? 1u : 0u;
+          q += e ? 1u : 0u;
         }
       }
     }
