@@ -1413,7 +1413,13 @@ __device__ __forceinline__ void select_taus(uint32_t n_s, uint32_t r0, uint32_t 
     if (t == 0) s.fl_cnt = 0;
     __syncthreads();
   }
-  for (uint32_t i = t; i < n_s; i += BLOCK) atomicAdd(&s.hist[(s.buf[i] - mn) >> sh], 1u);
+  // Four sample keys per 16-byte LDS read; entries from n_s on are stale and skipped.
+  for (uint32_t i = 4u * t; i < n_s; i += 4u * BLOCK) {
+    const u32x4 k4 = *reinterpret_cast<const u32x4*>(&s.buf[i]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i + (uint32_t)u < n_s) atomicAdd(&s.hist[(k4[u] - mn) >> sh], 1u);
+  }
   __syncthreads();
   block_find_bin(r2);
   const uint32_t b = s.sel_bin;
@@ -1421,14 +1427,20 @@ __device__ __forceinline__ void select_taus(uint32_t n_s, uint32_t r0, uint32_t 
   const uint32_t blo = mn + (b << sh);
   if (m <= (uint32_t)FL_CAP) {
     uint32_t nin = 0;
-    for (uint32_t i = t; i < n_s; i += BLOCK) nin += s.buf[i] >= blo ? 1u : 0u;
+    for (uint32_t i = 4u * t; i < n_s; i += 4u * BLOCK) {
+      const u32x4 k4 = *reinterpret_cast<const u32x4*>(&s.buf[i]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) nin += (i + (uint32_t)u < n_s && k4[u] >= blo) ? 1u : 0u;
+    }
     uint32_t f = wave_reserve_n<LIST_BITS>(nin, &s.fl_cnt);
     if (nin != 0) {
-      for (uint32_t i = t; i < n_s; i += BLOCK) {
-        const uint32_t k = s.buf[i];
-        if (k >= blo) {
-          if (f < (uint32_t)FL_CAP) s.fl_key[f] = k;
-          ++f;
+      for (uint32_t i = 4u * t; i < n_s; i += 4u * BLOCK) {
+        const u32x4 k4 = *reinterpret_cast<const u32x4*>(&s.buf[i]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const bool in = i + (uint32_t)u < n_s && k4[u] >= blo;
+          if (in && f < (uint32_t)FL_CAP) s.fl_key[f] = k4[u];
+          f += in ? 1u : 0u;
         }
       }
     }
