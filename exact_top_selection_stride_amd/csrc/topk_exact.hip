@@ -1646,12 +1646,13 @@ __device__ __forceinline__ uint32_t row_length(const Params& p, uint32_t row) {
 // ascending), then writes the indices and their scores; slots past the row's valid
 // entries keep the sentinel and get -inf. Entries are 64-bit composites
 // (key << 32 | ~index), never 0 for a valid entry (indices are below 2^31), so the zero
-// padding sorts last. The order comes from a bitonic network over P = EPT * BLOCK
-// entries, thread t holding entries t*EPT .. t*EPT+EPT-1. Every stage is a separate
-// instantiation with its run length and exchange distance known at compile time:
-// distances below EPT stay in registers, those up to 32 EPT go across the lanes of a wave
-// (see lane_xor64), and the larger ones (across waves) through LDS, double-buffered so
-// that each such stage needs one barrier.
+// padding sorts last. Thread t holds entries t*EPT .. t*EPT+EPT-1 of the P = EPT * BLOCK.
+// Each wave first sorts its own EPT * WAVE entries with a bitonic network: every stage is
+// a separate instantiation with its run length and exchange distance known at compile
+// time, distances below EPT stay in registers and those up to 32 EPT go across the lanes
+// of the wave (see lane_xor64), so no stage needs a barrier. The waves' runs are then
+// merged pairwise through LDS (merge path, three levels for eight waves), one barrier per
+// level.
 
 // Exchange of a 64-bit value with lane ^ M. The network is bound by vector ALU issue, so
 // only the one-instruction quad permutes (M = 1, 2) use DPP; M = 4, 8, 16 go through the
@@ -1671,7 +1672,7 @@ __device__ __forceinline__ uint64_t lane_xor64(uint64_t v) {
 
 // Stage (KB, J): runs of 2^KB entries, exchange distance J. An entry e meets e ^ J; the
 // lower entry of the pair keeps the larger value where bit KB of e is clear.
-template <int EPT, int KB, uint32_t J>
+template <int EPT, int KB, uint32_t J, bool ALL_DESC = false>
 __device__ __forceinline__ void sort_stage(uint64_t (&v)[EPT], uint32_t t, uint64_t (*c)[EPT * BLOCK],
                                            int& buf) {
   constexpr uint32_t K = 1u << KB;
@@ -1680,7 +1681,7 @@ __device__ __forceinline__ void sort_stage(uint64_t (&v)[EPT], uint32_t t, uint6
     for (int q = 0; q < EPT; ++q) {
       if (((uint32_t)q & J) == 0u) {
         const int r = q | (int)J;
-        const bool desc = ((t * EPT + (uint32_t)q) & K) == 0u;
+        const bool desc = ALL_DESC || ((t * EPT + (uint32_t)q) & K) == 0u;
         const uint64_t x = v[q], y = v[r];
         // One compare: with x == y swapping changes nothing, so "y > x" may stand for
         // "x < y" and its negation for "x > y".
@@ -1692,44 +1693,80 @@ __device__ __forceinline__ void sort_stage(uint64_t (&v)[EPT], uint32_t t, uint6
   } else {
     constexpr uint32_t M = J / EPT;  // partner thread t ^ M, same register slot
     const bool lo = (t & M) == 0u;
-    const bool desc = ((t * EPT) & K) == 0u;  // K >= J >= EPT: the same for every slot
+    const bool desc = ALL_DESC || ((t * EPT) & K) == 0u;  // K >= J >= EPT: the same for every slot
     const bool keep_max = desc == lo;
-    if constexpr (M < (uint32_t)WAVE) {
+    static_assert(M < (uint32_t)WAVE, "stages stay inside a wave");
 #pragma unroll
-      for (int q = 0; q < EPT; ++q) {
-        const uint64_t p = lane_xor64<(int)M>(v[q]);
-        v[q] = ((p > v[q]) == keep_max) ? p : v[q];  // equal values: either is the result
-      }
-    } else {
-      uint64_t* cb = c[buf];
-      buf ^= 1;
-#pragma unroll
-      for (int q = 0; q < EPT; ++q) cb[t * EPT + (uint32_t)q] = v[q];
-      __syncthreads();
-      const uint32_t pt = t ^ M;
-#pragma unroll
-      for (int q = 0; q < EPT; ++q) {
-        const uint64_t p = cb[pt * EPT + (uint32_t)q];
-        v[q] = ((p > v[q]) == keep_max) ? p : v[q];
-      }
+    for (int q = 0; q < EPT; ++q) {
+      const uint64_t p = lane_xor64<(int)M>(v[q]);
+      v[q] = ((p > v[q]) == keep_max) ? p : v[q];  // equal values: either is the result
     }
   }
 }
 
 // Every stage of runs of 2^KB, distances J, J / 2, ..., 1.
-template <int EPT, int KB, uint32_t J>
+template <int EPT, int KB, uint32_t J, bool ALL_DESC = false>
 __device__ __forceinline__ void sort_merge(uint64_t (&v)[EPT], uint32_t t, uint64_t (*c)[EPT * BLOCK], int& buf) {
-  sort_stage<EPT, KB, J>(v, t, c, buf);
-  if constexpr (J > 1u) sort_merge<EPT, KB, J / 2>(v, t, c, buf);
+  sort_stage<EPT, KB, J, ALL_DESC>(v, t, c, buf);
+  if constexpr (J > 1u) sort_merge<EPT, KB, J / 2, ALL_DESC>(v, t, c, buf);
 }
 
-// Runs of 2^KB, 2^(KB+1), ..., P.
-template <int EPT, int KB>
-__device__ __forceinline__ void sort_levels(uint64_t (&v)[EPT], uint32_t t, uint64_t (*c)[EPT * BLOCK], int& buf) {
-  constexpr uint32_t P = (uint32_t)EPT * BLOCK;
-  if constexpr ((1u << KB) <= P) {
+// Runs of 2^KB, 2^(KB+1), ..., 2^KTOP = EPT * WAVE entries, each wave's own entries: every
+// exchange stays inside the wave (no barrier), and the last level leaves every wave's run
+// in descending order.
+template <int EPT, int KB, int KTOP>
+__device__ __forceinline__ void sort_levels_wave(uint64_t (&v)[EPT], uint32_t t, uint64_t (*c)[EPT * BLOCK],
+                                                 int& buf) {
+  static_assert((1u << KTOP) == (uint32_t)EPT * WAVE, "one run per wave");
+  if constexpr (KB < KTOP) {
     sort_merge<EPT, KB, (1u << KB) / 2>(v, t, c, buf);
-    sort_levels<EPT, KB + 1>(v, t, c, buf);
+    sort_levels_wave<EPT, KB + 1, KTOP>(v, t, c, buf);
+  } else {
+    sort_merge<EPT, KTOP, (1u << KTOP) / 2, true>(v, t, c, buf);
+  }
+}
+
+// Merges the waves' descending runs of R = EPT * WAVE entries pairwise through LDS until one
+// run of P = EPT * BLOCK entries remains; thread t ends with entries t*EPT .. t*EPT+EPT-1 of
+// it. At each level a thread finds where its EPT outputs start by a binary search along
+// the merge diagonal of its pair of runs (merge path), then takes them one by one; equal
+// entries (only the zero padding) come from the first run first, both in the search and
+// in the walk, so every output position is produced exactly once.
+template <int EPT>
+__device__ __forceinline__ void merge_wave_runs(uint64_t (&v)[EPT], uint32_t t, uint64_t (*c)[EPT * BLOCK]) {
+  constexpr uint32_t P = (uint32_t)EPT * BLOCK, R = (uint32_t)EPT * WAVE;
+  const uint32_t e0 = t * (uint32_t)EPT;
+  int buf = 0;
+#pragma unroll
+  for (int q = 0; q < EPT; ++q) c[0][e0 + (uint32_t)q] = v[q];
+  __syncthreads();
+#pragma unroll
+  for (uint32_t run = R; run < P; run *= 2u) {
+    const uint64_t* A = c[buf] + (e0 & ~(2u * run - 1u));
+    const uint64_t* B = A + run;
+    const uint32_t d = e0 & (2u * run - 1u);  // outputs of the pair before this thread's
+    uint32_t lo = d > run ? d - run : 0u, hi = d < run ? d : run;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;  // lo <= mid < hi: A[mid] and B[d - mid - 1] lie in their runs
+      if (A[mid] >= B[d - mid - 1u]) lo = mid + 1u;
+      else hi = mid;
+    }
+    uint32_t i = lo, j = d - lo;
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+      const uint64_t a = i < run ? A[i] : 0ull, b = j < run ? B[j] : 0ull;
+      const bool take_a = j >= run || (i < run && a >= b);
+      v[q] = take_a ? a : b;
+      i += take_a ? 1u : 0u;
+      j += take_a ? 0u : 1u;
+    }
+    if (2u * run < P) {
+      uint64_t* dst = c[buf ^ 1];
+#pragma unroll
+      for (int q = 0; q < EPT; ++q) dst[e0 + (uint32_t)q] = v[q];
+      __syncthreads();
+      buf ^= 1;
+    }
   }
 }
 
@@ -1781,7 +1818,9 @@ __device__ __forceinline__ void sort_row(const float* __restrict__ scores, uint3
   }
   __syncthreads();  // every key of the row is read before any thread overwrites out_val
   int buf = 0;
-  sort_levels<EPT, 1>(v, t, c, buf);
+  constexpr int KTOP = EPT == 1 ? 6 : (EPT == 2 ? 7 : (EPT == 4 ? 8 : 9));
+  sort_levels_wave<EPT, 1, KTOP>(v, t, c, buf);
+  merge_wave_runs<EPT>(v, t, c);
   const bool vec_out = vec && val != nullptr && (reinterpret_cast<uintptr_t>(val) & 15u) == 0u;
   auto value_of = [](uint32_t key) { return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key); };
 #pragma unroll
