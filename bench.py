@@ -561,6 +561,21 @@ def _quantile(v, q):
     return v[int(q * (len(v) - 1))]
 
 
+def path_model_line(w, stats, lengths, K):
+    """Rows of the first calls (every row of the window once) that missed K at tau0 and at
+    tau1, beside the beta-binomial model of the stride-128 thresholds for rows of
+    independently drawn scores (exact_top_selection_stride_amd.path_model; the bench runs
+    the method's stride and targets). FP32 windows only: bf16-rounded rows have ties, which
+    the model excludes."""
+    if w.bf16 or stats.get("sampled", 0) == 0:
+        return None
+    from exact_top_selection_stride_amd import path_model as PM
+    e0, e1 = PM.expected_short_rows(lengths.cpu().tolist(), K)
+    n1 = stats["tau_a"] + stats["recover_under"]
+    return {"rows_short_at_tau0": stats["tau1"] + n1, "model_rows_short_at_tau0": round(e0, 1),
+            "rows_short_at_tau1": n1, "model_rows_short_at_tau1": round(e1, 1)}
+
+
 def main(argv=None):
     args = parse(argv)
     if args.summarize_counters:
@@ -778,6 +793,7 @@ def main(argv=None):
         "parity": {"rows_checked": checked, "violations": violations, "post_timing_violations": post_bad,
                    "gate": "torch contract check on device"},
         "path_stats_first_calls": stats,
+        "path_model": path_model_line(w, stats, lengths, K),
         "kernel_source_digest": digest,
         "generation_s": round(t_gen, 2),
         "input_checksums": checksums,

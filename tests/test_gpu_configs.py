@@ -22,6 +22,7 @@ import torch
 
 import oracle
 import exact_top_selection_stride_amd as tk
+from exact_top_selection_stride_amd import path_model as PM
 from exact_top_selection_stride_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -84,6 +85,22 @@ def _check_every_row(window, lengths, outputs, label):
          f"({sum(checked.values())} rows)")
 
 
+def _check_path_rates(st, lengths, label):
+    """The rows that miss K at tau0 and at tau1, counted by the library, against the
+    beta-binomial model of the sampled thresholds (exact_top_selection_stride_amd.path_model;
+    the FP32 windows draw every element independently). The data are fixed, so this is a
+    deterministic check; its band (five standard deviations of a count) is wide enough for
+    the model's sampling noise and narrow enough that tau0 one sample rank too shallow
+    (about 1.6 times as many rows short of K on the 1M window) fails."""
+    e0, e1 = PM.expected_short_rows(lengths.cpu().tolist(), K)
+    n1 = st["tau_a"] + st["recover_under"]          # C(tau1) < K
+    n0 = st["tau1"] + n1                             # C(tau0) < K
+    _say(f"{label} path rates: C(tau0) < K in {n0} rows (model {e0:.1f}), "
+         f"C(tau1) < K in {n1} rows (model {e1:.1f})")
+    assert abs(n0 - e0) <= 5 * e0 ** 0.5 + 3, (label, n0, e0)
+    assert abs(n1 - e1) <= 5 * e1 ** 0.5 + 3, (label, n1, e1)
+
+
 def test_c1_every_group_every_row():
     # 512 x 131072: 16 groups of the causal window, one workgroup per row (element-wise
     # sample, whole-row pass), as the benchmark launches them.
@@ -93,6 +110,7 @@ def test_c1_every_group_every_row():
     _say(f"c1 stats {st}")
     assert st["rows"] == 8192 and st["sampled"] == 8192 and st["row_per_wg"] == 8192
     assert st["rowsplit"] == 0 and st["persistent"] == 0 and st["direct"] == 0
+    _check_path_rates(st, l, "c1")
     _check_every_row(s, l, {"c1 M=512 x 16 groups": (0, out)}, "c1")
 
 
@@ -104,6 +122,7 @@ def test_c2_every_group_every_row():
     _say(f"c2 stats {st}")
     assert st["rows"] == 8192 and st["sampled"] == 8192 and st["persistent"] == 8192
     assert st["rowsplit"] == 0 and st["row_per_wg"] == 0
+    _check_path_rates(st, l, "c2")
     _check_every_row(s, l, {"c2 M=4096 x 2 groups": (0, out)}, "c2")
 
 
@@ -118,6 +137,7 @@ def test_c3a_c3b_every_row():
     _say(f"c3b stats {st_b}")
     assert st_b["rows"] == 8192 and st_b["sampled"] == 8192 and st_b["persistent"] == 8192
     assert st_b["rowsplit"] == 0
+    _check_path_rates(st_b, l, "c3b")
     out_a, st_a = _calls(s, l, wa.M, wa.groups)
     _say(f"c3a stats {st_a}")
     assert st_a["rows"] == 8192 and st_a["sampled"] == 8192 and st_a["row_per_wg"] == 8192
