@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import exact_top_selection_stride_amd as tk
+from exact_top_selection_stride_amd import path_model as PM
 from exact_top_selection_stride_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -550,6 +551,54 @@ def test_phase_recording_hook():
     buf.zero_()
     _run(s, l)
     assert int(buf.abs().sum()) == 0
+
+
+def _host_keys(row):
+    """Order keys of float32 scores (sign flip of the bit pattern, all bits flipped for
+    negatives): key order is score order."""
+    u = row.view(np.uint32)
+    return u ^ np.where(u >> 31 == 1, np.uint32(0xFFFFFFFF), np.uint32(0x80000000))
+
+
+@pytest.mark.parametrize("name,rows,execution", [
+    ("c1", [(0, 24), (4000, 24)], tk.EXEC_ROW_PER_WG),   # element sample, admission to tau_a
+    ("c3a", [(0, 6), (8000, 6)], tk.EXEC_ROW_PER_WG),    # line sample, cold lines skipped
+    ("c2", [(100, 4), (6000, 4)], tk.EXEC_AUTO),         # few 512K rows: row-split
+])
+def test_threshold_counts_equal_sample_rank_counts(name, rows, execution):
+    # Each certified row's recorded C(tau0) and C(tau1) equal, on the host, the number of the
+    # row's keys at or above the r0-th and r1-th largest of its stride-128 sample keys, with
+    # r = ceil(T n_s / L) for the targets T0 = 1.5 K and T1 = 1.75 K: the thresholds are the
+    # sample ranks of the method, in every sampling mode and execution.
+    s, l = _window_rows(name, rows)
+    buf = torch.zeros((s.shape[0], 8), dtype=torch.int64, device=DEV)
+    khz = tk.record_phases(buf)
+    try:
+        with tk.execution(execution):
+            out, st = _run(s, l)
+    finally:
+        tk.record_phases(None)
+    _check(s, l, out, label=f"{name} threshold counts")
+    assert khz > 0
+    rec = buf.cpu().numpy()
+    sh, lh = s.cpu().numpy(), l.cpu().numpy()
+    t0, t1 = PM.targets(K)
+    checked = 0
+    for i in range(s.shape[0]):
+        code = int(rec[i, 6]) & 0x7F
+        if tk.PATH_CODES.get(code) not in ("tau0", "tau1", "tau_a"):
+            continue
+        L = int(lh[i])
+        keys = _host_keys(sh[i, :L])
+        n_s = -(-L // 128)
+        samp = np.sort(keys[::128][:n_s])[::-1]
+        k0 = samp[PM.sample_rank(t0, n_s, L) - 1]
+        k1 = samp[PM.sample_rank(t1, n_s, L) - 1]
+        want = (int((keys >= k0).sum()), int((keys >= k1).sum()))
+        got = (int(rec[i, 7]) >> 32, int(rec[i, 7]) & 0xFFFFFFFF)
+        assert got == want, (name, i, L, got, want)
+        checked += 1
+    assert checked >= s.shape[0] - 2, (checked, st)
 
 
 def test_graph_replay():
