@@ -174,6 +174,7 @@ struct Params {
   uint32_t ps;          // row-split: workgroups per row sampling
   uint32_t pp;          // row-split: workgroups per row passing
   uint32_t pass_taus;   // row-split: each passing workgroup selects the row's taus itself
+  uint32_t split_elem;  // row-split: ... from the row's element sample, read by itself (no sample kernel)
   unsigned long long* phase;  // per-row phase record (PHASE_WORDS per row), or null
   uint32_t* okey;       // [M][K] selected keys beside out (sorted output), or null
   uint32_t sort_rows;   // sorted output: each row is sorted by its workgroup once complete
@@ -2433,11 +2434,56 @@ void split_pass_kernel(Params p) {
   Smem& s = g_s;
   const uint32_t t = threadIdx.x, part = blockIdx.x, row = blockIdx.y;
   RowSplitState* rs = p.rs + row;
-  if (rs->whole) return;
   const uint32_t L = row_length(p, row);
+  if (p.split_elem) {
+    // No sample kernel ran: the rows the split does not apply to are marked here.
+    if (!split_applies(p, L)) {
+      if (part == 0 && t == 0) rs->whole = 1u;
+      return;
+    }
+  } else if (rs->whole) {
+    return;
+  }
   const uint32_t n_s = (L + STRIDE - 1) / STRIDE;
-  uint32_t t0key, t1key;
-  if (p.pass_taus) {
+  grow_t x = (grow_t)(p.scores) + (size_t)row * p.N;
+  uint32_t t0key, t1key, smax;
+  if (p.split_elem) {
+    // Short rows (at most 2048 sample periods): every passing workgroup reads the row's
+    // element sample itself (the parts of a row share it through the cache) and selects
+    // the taus from it, so no sample kernel runs. The pass then reads whole rows, as the
+    // one-workgroup pass does for element-sampled rows; part 0 records the sample's
+    // extremes and the taus for the finish.
+    if (t == 0) {
+      s.mn = KEY_MAX;
+      s.mx = 0;
+    }
+    __syncthreads();
+    uint32_t mn = KEY_MAX, mx = 0;
+#pragma unroll 4
+    for (uint32_t j = t; j < n_s; j += BLOCK) {
+      const uint32_t k = key_of_bits(x[(size_t)j * STRIDE]);
+      s.buf[j] = k;
+      mn = min(mn, k);
+      mx = max(mx, k);
+    }
+    block_minmax(mn, mx);
+    const uint32_t smin = s.mn;
+    smax = s.mx;
+    uint32_t takey, t2key;
+    const uint32_t r1 = sample_rank(p.T1, n_s, L);
+    select_taus(n_s, sample_rank(p.T0, n_s, L), r1, r1, sample_rank(p.T2, n_s, L), smin, smax, t0key, t1key, takey,
+                t2key);
+    if (part == 0 && t == 0) {
+      rs->mn_inv = ~smin;
+      rs->mx = smax;
+      rs->t1key = t1key;
+      rs->t0key = t0key;
+      rs->t2key = t2key;
+      stat_add(p.ctl, TOPK_STAT_ROWS);
+      stat_add(p.ctl, TOPK_STAT_SAMPLED);
+      stat_add(p.ctl, TOPK_STAT_ROWSPLIT);
+    }
+  } else if (p.pass_taus) {
     // The taus from the whole sample, in every part (no separate select launch); part 0
     // records them for the finish.
     uint32_t v[LM_PER_THREAD];
@@ -2461,9 +2507,11 @@ void split_pass_kernel(Params p) {
       rs->t0key = t0key;
       rs->t2key = t2key;
     }
+    smax = rs->mx;
   } else {
     t1key = rs->t1key;
     t0key = rs->t0key;
+    smax = rs->mx;
   }
   if (t1key == 0u) {
     // Every key is admitted at the lowest threshold: count the row as overflowing
@@ -2471,8 +2519,7 @@ void split_pass_kernel(Params p) {
     if (part == 0 && t == 0) atomicAdd(&rs->c1, (uint32_t)CAP + 1u);
     return;
   }
-  const PassCtx c = pass_ctx(t1key, rs->mx);
-  grow_t x = (grow_t)(p.scores) + (size_t)row * p.N;
+  const PassCtx c = pass_ctx(t1key, smax);
   // This part covers the sample periods [q0, q1): row elements [e0, e1), where period
   // P starts at offset 128 P from the 128-byte line below x (the last part runs to the
   // row's end, which may reach one element line past its last sampled period).
@@ -2481,20 +2528,28 @@ void split_pass_kernel(Params p) {
   const uint32_t off4 = (uint32_t)((uintptr_t)x & 127u) >> 2;
   const uint32_t e0 = q0 == 0u ? 0u : 128u * q0 - off4;
   const uint32_t e1 = part == p.pp - 1 ? L : (q1 == 0u ? 0u : 128u * q1 - off4);
-  // Bitmap of this part's hot sampled lines (bit P - q0), as in the one-workgroup pass.
-#pragma unroll
-  for (int m = 0; m < LM_PER_THREAD; ++m) {
-    const uint32_t j = t + (uint32_t)m * BLOCK;
-    const uint64_t hb = __ballot(q0 + j < q1 && rs->lmax[q0 + j] >= t1key);
-    if (lane_id() == 0) {
-      s.fl_idx[j >> 5] = (uint32_t)hb;
-      s.fl_idx[(j >> 5) + 1] = (uint32_t)(hb >> 32);
+  if (p.split_elem) {
+    reset_row_state();
+    if (e1 > e0) {
+      if (t1key >= 0x80000000u) fused_pass<true, false>(x + e0, e1 - e0, q1 - q0, c, e0);
+      else fused_pass<false, false>(x + e0, e1 - e0, q1 - q0, c, e0);
     }
-  }
-  reset_row_state();
-  if (e1 > e0) {
-    if (t1key >= 0x80000000u) fused_pass<true, true>(x + e0, e1 - e0, q1 - q0, c, e0);
-    else fused_pass<false, true>(x + e0, e1 - e0, q1 - q0, c, e0);
+  } else {
+    // Bitmap of this part's hot sampled lines (bit P - q0), as in the one-workgroup pass.
+#pragma unroll
+    for (int m = 0; m < LM_PER_THREAD; ++m) {
+      const uint32_t j = t + (uint32_t)m * BLOCK;
+      const uint64_t hb = __ballot(q0 + j < q1 && rs->lmax[q0 + j] >= t1key);
+      if (lane_id() == 0) {
+        s.fl_idx[j >> 5] = (uint32_t)hb;
+        s.fl_idx[(j >> 5) + 1] = (uint32_t)(hb >> 32);
+      }
+    }
+    reset_row_state();
+    if (e1 > e0) {
+      if (t1key >= 0x80000000u) fused_pass<true, true>(x + e0, e1 - e0, q1 - q0, c, e0);
+      else fused_pass<false, true>(x + e0, e1 - e0, q1 - q0, c, e0);
+    }
   }
   __syncthreads();
   // Merge into the row: one atomic reserves this workgroup's candidate range. C(tau0) is
@@ -2955,6 +3010,7 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
   p.ps = 1;
   p.pp = 1;
   p.pass_taus = 0;
+  p.split_elem = 0;
   // Execution by shape. Row-split when rows are few and long: their scan and
   // sampling are divided among several workgroups. Measured on MI355X (512 resident
   // slots, graph replays): for rows of 1M, row-split takes 44-62 us for 1-32 rows
@@ -3055,7 +3111,15 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
     // 128K and 16 rows of 1M 0.6-0.9 us. A larger grid repeats that work in later rounds,
     // and 64 rows of 1M lose 6 us with it.
     p.pass_taus = (int64_t)p.pp * M <= resident ? 1u : 0u;
-    hipLaunchKernelGGL(split_sample_kernel, dim3(p.ps, (unsigned)M), dim3(BLOCK), 0, stream, p);
+    // With the taus selected in the passing workgroups, each of them can read the row's
+    // element sample itself, so that no sample kernel is launched; the pass then reads the
+    // whole row (no line skipping). Measured on MI355X (graph replays, median call): rows
+    // of 128K, 1 / 4 / 16 / 64 of them, 30.4 / 31.0 / 31.8 / 39.1 -> 25.1 / 25.6 / 26.8 /
+    // 37.4 us (most of their sampled lines are hot anyway); one 1M row 37.9 -> 35.0 us,
+    // but 4 and 16 rows of 1M lose 2 and 9 us (every part re-reads 8192 samples, and the
+    // skipped cold lines are read). So: rows of at most 2048 sample periods, or one row.
+    p.split_elem = (p.pass_taus && (n_s_max <= 2048 || M == 1)) ? 1u : 0u;
+    if (!p.split_elem) hipLaunchKernelGGL(split_sample_kernel, dim3(p.ps, (unsigned)M), dim3(BLOCK), 0, stream, p);
     if (!p.pass_taus) hipLaunchKernelGGL(split_select_kernel, dim3((unsigned)M), dim3(BLOCK), 0, stream, p);
     hipLaunchKernelGGL(split_pass_kernel, dim3(p.pp, (unsigned)M), dim3(BLOCK), 0, stream, p);
     hipLaunchKernelGGL(split_finish_kernel, dim3((unsigned)M), dim3(BLOCK), 0, stream, p);

@@ -563,7 +563,8 @@ def _host_keys(row):
 @pytest.mark.parametrize("name,rows,execution", [
     ("c1", [(0, 24), (4000, 24)], tk.EXEC_ROW_PER_WG),   # element sample, admission to tau_a
     ("c3a", [(0, 6), (8000, 6)], tk.EXEC_ROW_PER_WG),    # line sample, cold lines skipped
-    ("c2", [(100, 4), (6000, 4)], tk.EXEC_AUTO),         # few 512K rows: row-split
+    ("c2", [(100, 4), (6000, 4)], tk.EXEC_AUTO),         # few 512K rows: row-split, line sample
+    ("c1", [(10, 3), (7000, 3)], tk.EXEC_AUTO),          # few 128K rows: row-split, element sample
 ])
 def test_threshold_counts_equal_sample_rank_counts(name, rows, execution):
     # Each certified row's recorded C(tau0) and C(tau1) equal, on the host, the number of the
