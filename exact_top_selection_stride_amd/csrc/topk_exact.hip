@@ -2323,9 +2323,13 @@ void recovery_finish_kernel(Params p) {
 //                           merged into the row's state (one atomic per workgroup,
 //                           one per non-empty bin);
 //   split_finish (M)        certify, then refine and commit or queue for recovery.
-// Rows the split does not apply to (L <= K, direct-exact, forced recovery, rows past
-// the line-sample limit) are processed whole by split_finish. split_finish also
-// rewinds the row state for the next call.
+// split_select runs only when the passing grid exceeds one round of resident
+// workgroups (otherwise every passing workgroup selects the taus itself), and
+// split_sample not at all for rows of at most 2048 sample periods or a single row
+// (every passing workgroup then reads the row's element sample itself and passes the
+// whole row). Rows the split does not apply to (L <= K, direct-exact, forced recovery,
+// rows past the line-sample limit) are processed whole by split_finish. split_finish
+// also rewinds the row state for the next call.
 
 constexpr uint32_t RS_MAX_ROWS = 1024;  // rows per call the row-split state holds
 
