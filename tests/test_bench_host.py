@@ -143,3 +143,25 @@ def test_order_keys_follow_total_order():
     x = torch.tensor([-np.inf, -1.0, -0.0, 0.0, 1e-45, 1.0, np.inf], dtype=torch.float32)
     k = bench.order_keys(x)
     assert bool((k[1:] > k[:-1]).all())
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    # The selector runs on one GPU: --gpus N > 1 prints one JSON line saying so and exits 2.
+    assert bench.main(["--gpus", "2"]) == 2
+    line = json.loads(capsys.readouterr().out.strip().splitlines()[-1])
+    assert line["n_gpus_requested"] == 2 and "one GPU" in line["error"]
+
+
+def test_path_model_line():
+    # Measured rows short of K at tau0 / tau1 from the counters, beside the model's
+    # expectations; none for bf16-rounded windows (ties) or calls without sampled rows.
+    from exact_top_selection_stride_amd import path_model as PM
+    from exact_top_selection_stride_amd import workloads as W
+    lengths = torch.tensor([131072 - 8192 + r + 1 for r in range(0, 8192, 512)], dtype=torch.int32)
+    st = {"sampled": 16, "tau1": 3, "tau_a": 1, "recover_under": 1}
+    d = bench.path_model_line(W.get("c1"), st, lengths, 2048)
+    e0, e1 = PM.expected_short_rows(lengths.tolist(), 2048)
+    assert d == {"rows_short_at_tau0": 5, "model_rows_short_at_tau0": round(e0, 1),
+                 "rows_short_at_tau1": 2, "model_rows_short_at_tau1": round(e1, 1)}
+    assert bench.path_model_line(W.get("c4_n65536_m8192"), st, lengths, 2048) is None
+    assert bench.path_model_line(W.get("c1"), dict(st, sampled=0), lengths, 2048) is None
