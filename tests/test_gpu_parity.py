@@ -474,6 +474,35 @@ def test_random_shapes_every_mode(seed):
             assert st["rows"] == s.shape[0]
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_random_larger_shapes_and_sorted(seed):
+    # Seeded random larger calls: widths 16K-1M, up to 600 rows (64 at 512K and beyond),
+    # K 512-4096, lengths from K/2 to the width; automatic, row-split and persistent
+    # execution, and the sorted output, each checked against the oracle.
+    rng = np.random.default_rng(5000 + seed)
+    n_alloc = int(rng.choice([16385, 65536, 131072, 262147, 524288, 1048576]))
+    M = int(rng.choice([1, 2, 5, 16, 63, 200, 513, 600]))
+    if n_alloc >= 524288:
+        M = min(M, 64)
+    Kr = int(rng.choice([512, 1000, 2048, 4096]))
+    lens = rng.integers(Kr // 2, n_alloc + 1, size=M)
+    lens[rng.random(M) < 0.3] = n_alloc
+    x = rng.normal(30.0, 2.5, size=(M, n_alloc)).astype(np.float32)
+    tail = rng.random((M, n_alloc)) < 0.01
+    x[tail] = (45.0 + rng.exponential(3.0, size=int(tail.sum()))).astype(np.float32)
+    x[np.arange(n_alloc)[None, :] >= lens[:, None]] = -np.inf
+    s = torch.from_numpy(x).to(DEV)
+    l = torch.from_numpy(lens.astype(np.int32)).to(DEV)
+    label = f"seed {seed} n_alloc {n_alloc} M {M} K {Kr}"
+    for execution in (tk.EXEC_AUTO, tk.EXEC_ROWSPLIT, tk.EXEC_PERSISTENT):
+        with tk.execution(execution):
+            out, st = _run(s, l, K=Kr)
+        _check(s, l, out, K=Kr, label=f"{label} exec {execution}")
+    idx, val = tk.topk_exact_sorted(s, l, K=Kr)
+    torch.cuda.synchronize()
+    _check_sorted(s, l, idx, val, Kr, label=f"{label} sorted")
+
+
 def test_consecutive_calls_reuse_the_ticket():
     # Row tickets rewind after every call: calls of different M back to back.
     s, l = _window_rows("c1", [(0, 40)])
