@@ -205,6 +205,7 @@ struct alignas(16) Smem {
   uint32_t sel_bin, sel_above;
   uint32_t bcast;              // block-wide broadcast of a value read by thread 0
   uint32_t bcast2;
+  uint32_t queued;             // the row was handed to the recovery kernels (sorted output)
   int32_t row;
 };
 
@@ -1314,6 +1315,7 @@ __device__ __forceinline__ void recover_row_window(const Params& p, uint32_t row
   __syncthreads();
   if (q < p.qmax) {
     if (t == 0) {
+      s.queued = 1u;
       RecSlot* r = p.rec + q;
       r->row = row;
       r->L = L;
@@ -1378,6 +1380,7 @@ __device__ __forceinline__ void recover_row(const Params& p, uint32_t row, grow_
   if (q < p.qmax) {
     RecSlot* r = p.rec + q;
     if (t == 0) {
+      s.queued = 1u;
       r->row = row;
       r->L = L;
       r->lo = lo;
@@ -1929,8 +1932,15 @@ static_assert(2 * 8 * BLOCK * sizeof(uint64_t) <= sizeof(uint32_t) * 2 * CAP, "t
 
 template <bool STREAM_SAMPLE = false>
 __device__ __forceinline__ void process_row(const Params& p, uint32_t row) {
+  // Sorted output: a row completed here is sorted here; a row handed to the recovery
+  // kernels is sorted by the recovery finish kernel once complete. (Thread 0 clears the
+  // flag and is the only writer; every thread reads it after the barrier below.)
+  if (p.sort_rows && threadIdx.x == 0) g_s.queued = 0u;
   process_row_body<STREAM_SAMPLE>(p, row);
-  if (p.sort_rows) sort_row_here(p.scores, row, row_length(p, row), p.N, p.K, (int32_t*)p.out, p.oval, p.sentinel);
+  if (p.sort_rows) {
+    __syncthreads();
+    if (!g_s.queued) sort_row_here(p.scores, row, row_length(p, row), p.N, p.K, (int32_t*)p.out, p.oval, p.sentinel);
+  }
 }
 
 // The selector kernel. Persistent execution: a grid of resident workgroups pulls
@@ -2296,6 +2306,11 @@ void recovery_finish_kernel(Params p) {
     }
     __syncthreads();
     phase_mark(p.phase, r->row, PH_RECOVERED);
+    if (p.sort_rows) {
+      // Sorted output: the selector sorted the rows it completed; this row is sorted here.
+      sort_row_here(p.scores, r->row, L, p.N, K, (int32_t*)p.out, p.oval, p.sentinel);
+      __syncthreads();  // the sort's exchange area is free before the next row uses the LDS
+    }
   }
   // The last workgroup to leave rewinds the queue for the next call; every
   // workgroup has read qcount before it increments rec_done.
@@ -3062,14 +3077,19 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
     const uint32_t elem_max = (p.line_min - 1u) * STRIDE;
     if (elem_max > p.inplace_max) p.inplace_max = elem_max;
   }
-  // Sorted output: in calls of at most one row per resident workgroup where every row is
-  // completed inside the selector kernel (none can be handed to the recovery kernels), each
-  // workgroup sorts its row once complete, overlapping the other rows' passes; otherwise
-  // a sort kernel follows. Measured on MI355X (graph replays, sorted call): 512 x 128K
-  // 94.8 -> 90.5 us and 256 x 8K 26.5 -> 24.7 us sorted here, while 8192 x 64K rows,
-  // sixteen per workgroup, took 622.7 -> 657.4 us.
+  const bool persistent = !split && (ex == TOPK_EXEC_PERSISTENT ||
+                                      (ex == TOPK_EXEC_AUTO && M >= 4 * resident && N_alloc >= 262144));
+  // Sorted output: each workgroup sorts a row once it completes it, overlapping the other
+  // rows' passes (the selector's workgroup for the rows it completes, the recovery finish
+  // kernel's for the rows handed to it), in calls of at most one row per resident
+  // workgroup where no row can be handed over, and in persistent calls; otherwise a sort
+  // kernel follows. Measured on MI355X (graph replays, sorted call): 512 x 128K 94.8 ->
+  // 90.5 us and 256 x 8K 26.5 -> 24.7 us sorted here; persistent 8192 x 1M 5.46 -> 5.43 ms
+  // and 4096 x 512K 1.495 -> 1.480 ms. Not kept: 512 x 1M with its queued rows sorted by
+  // the recovery finish kernel (388 -> 391 us), and 8192 x 64K rows, sixteen per
+  // workgroup, one workgroup per row (622.7 -> 657.4 us).
   if (sort_here != nullptr) {
-    *sort_here = !split && (int64_t)p.inplace_max >= N_alloc && M <= resident;
+    *sort_here = !split && (persistent || ((int64_t)p.inplace_max >= N_alloc && M <= resident));
     if (*sort_here) {
       p.sort_rows = 1;
       p.oval = reinterpret_cast<float*>(okey);
@@ -3130,8 +3150,6 @@ int selector_launch(const float* scores, const int32_t* row_len, int64_t M, int6
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "launch row-split kernels");
   } else {
-    const bool persistent = ex == TOPK_EXEC_PERSISTENT ||
-                            (ex == TOPK_EXEC_AUTO && M >= 4 * resident && N_alloc >= 262144);
     if (persistent) {
       const unsigned grid = (unsigned)(M < resident ? M : resident);
       hipLaunchKernelGGL(topk_rows_kernel<true>, dim3(grid), dim3(BLOCK), 0, stream, p);

@@ -969,6 +969,24 @@ def test_sorted_output_every_execution(execution):
     assert st["recover_under"] + st["recover_over"] >= 3
 
 
+@pytest.mark.parametrize("execution", [tk.EXEC_ROW_PER_WG, tk.EXEC_PERSISTENT])
+def test_sorted_output_with_rows_queued_for_recovery(execution):
+    # 1M rows: the selector sorts the rows it completes, and the recovery finish kernel
+    # sorts the rows handed to it (two underfilled rows, C(tau1) = 1028 < K).
+    L = 1048576
+    s1, l1 = _window_rows("c3a", [(0, 4)])
+    adv = torch.from_numpy(np.stack([_adversarial_row(L, 1000, 950 + i) for i in range(2)])).to(DEV)
+    s = torch.cat([s1, adv]).contiguous()
+    l = torch.cat([l1, torch.full((2,), L, dtype=torch.int32, device=DEV)]).contiguous()
+    with tk.execution(execution):
+        tk.reset_stats()
+        idx, val = tk.topk_exact_sorted(s, l, K=K)
+        torch.cuda.synchronize()
+        st = tk.get_stats()
+    _check_sorted(s, l, idx, val, K, label=f"sorted with queued rows, execution {execution}")
+    assert st["queued"] >= 2 and st["recover_under"] >= 2
+
+
 def test_sorted_output_k4096_and_misaligned_values():
     s, l = _window_rows("c3a", [(8000, 3)])
     idx, val = tk.topk_exact_sorted(s, l, K=4096)
