@@ -166,8 +166,9 @@ int topk_exact_noalloc(const float* scores, const int32_t* row_len, int64_t M, i
  *            (the input's bit patterns) in the order of out_idx, -inf in sentinel slots.
  *            With NULL only the ordered indices are written. Caller-owned.
  * Where a call has at most one row per resident workgroup and no row can be handed to the
- * recovery kernels, each selector workgroup sorts its own row; otherwise a sort kernel
- * follows on the same stream. Capture, workspace and error behaviour as for topk_exact,
+ * recovery kernels, and in persistent calls, each row is sorted by the workgroup that
+ * completes it (a selector workgroup, or the recovery finish kernel's for rows handed to
+ * it); otherwise a sort kernel follows on the same stream. Capture, workspace and error behaviour as for topk_exact,
  * plus TOPK_ERR_BAD_ARG (nothing enqueued) for an out_val that is not 4-byte aligned. */
 int topk_exact_sorted(const float* scores, const int32_t* row_len, int64_t M, int64_t N_alloc,
                       int32_t K, int32_t* out_idx, float* out_val, int32_t sentinel, hipStream_t stream);
